@@ -1,0 +1,195 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) hybrid compressed attention forward.
+ *
+ * The method (DeepSeek-V4 hybrid attention) as the pages state it:
+ *  - CSA compresses the KV cache every m = 4 tokens into one entry by a
+ *    weighted average with overlap between adjacent blocks, scores the
+ *    entries with a low-rank FP4 "Lightning Indexer", lets each query token
+ *    attend only to its top-k entries, and uses shared-KV multi-query
+ *    attention (one entry row is both key and value)
+ *        ("DeepSeek-V4: Towards Highly Efficient Million-Token Context
+ *          Intelligence" wiki summary, Proposed method, item 1;
+ *          "deepseek V4 技术论文", part 1.1, CSA bullets);
+ *  - HCA compresses every m' = 128 tokens and attends densely (same places);
+ *  - both add a sliding-window branch of n_win = 128 raw tokens, a learnable
+ *    per-head attention sink, and partial RoPE on the last 64 dims with the
+ *    inverse rotation applied to the attention output (wiki summary, item 1);
+ *  - the inference cache keeps the RoPE dims in BF16 and the other dims in
+ *    FP8 (wiki summary, Training infrastructure item 5); the indexer QK path
+ *    is MXFP4 (wiki summary, Post-training item 3).
+ *
+ * Conventions shared by every call
+ *  - Pointers: every tensor argument is a DEVICE pointer owned by the caller.
+ *    The library never allocates, frees or synchronises; it launches only on
+ *    the given stream (a hipStream_t passed as void*, NULL = default stream),
+ *    so every call is asynchronous and stream-ordered.
+ *  - Layout: row-major, contiguous, batch-major [B, ...]; base pointers
+ *    16-byte aligned.  bf16 = uint16 bit patterns.  MXFP4 = packed e2m1
+ *    nibbles (element 2j in the low nibble of byte j) plus one e8m0 byte
+ *    (2^(byte-127)) per 32 consecutive elements.  FP8 = OCP e4m3fn bytes.
+ *  - Sizes: D (head dim) = 128, rope_dims = 64 or 0, d_idx = 64.
+ *  - Positions are absolute int64.  Query row q of every batch row sits at
+ *    t = q_pos0 + q.  Compressed entry s sits at p_s = (s+1)*m - 1 (its last
+ *    token) and is visible to t iff p_s <= t.
+ *  - RoPE: pairs (D-R+2f, D-R+2f+1) rotated by pos * rope_base^(-2f/R).
+ *    q and raw window rows come in pre-RoPE and are rotated on load at t and
+ *    j; entries are stored post-RoPE (rotated at p_s by csa_compress).
+ *  - Errors: each call returns an int status (CSA_OK = 0 or a negative
+ *    code).  Arguments are validated on the host before anything is
+ *    launched; on error nothing is launched and csa_last_error() returns a
+ *    thread-local message naming the argument.  No exception crosses the ABI.
+ *  - Determinism: every result is bitwise reproducible run to run and does
+ *    not depend on the batch size or on which other rows are in the call.
+ */
+#ifndef CSA_MI355X_H
+#define CSA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define CSA_OK 0
+#define CSA_INVALID_ARG (-1)
+#define CSA_UNSUPPORTED (-2)
+#define CSA_WORKSPACE_TOO_SMALL (-3)
+#define CSA_HIP_ERROR (-4)
+
+/* formats */
+#define CSA_FMT_BF16 0          /* entries [.., 128] bf16 / indexer [.., 64] bf16 */
+#define CSA_FMT_MXFP4 1         /* indexer: codes [.., 32] u8 + scales [.., 2] u8 */
+#define CSA_FMT_FP8_ROPE_BF16 2 /* entries: e4m3 [.., 64] + bf16 [.., 64] + f32 scale [..] */
+
+/*
+ * csa_compress -- token-level compressor (CSA: m = 4 with overlap; HCA:
+ * m = 128 without).  Wiki summary, Proposed method item 1 ("compress every
+ * m tokens into one entry by a weighted average, overlapping adjacent
+ * blocks"); "deepseek V4 技术论文" 1.1 (C^b overlaps C^a).
+ *
+ * Entry i pools the m tokens of block i (role "a") and, when overlap = 1,
+ * also the m tokens of block i-1 (role "b").  Slot r of the L = 2m (or m)
+ * slots has logit beta[r] + z[j][role] (z = NULL means 0; column 0 = role a,
+ * column 1 = role b); slots before token 0 are absent.  The weights are the
+ * softmax of the logits computed in fp64 and rounded to fp32; the pooled
+ * row is an fp32 fma chain over the slots in ascending order; the KV entry
+ * is then rotated at p_i = (i+1)m - 1 (rotation in fp64) and stored.  The
+ * indexer-key stream ik is pooled with the same weights, not rotated, and
+ * stored as bf16 or MXFP4.
+ *
+ *  kv        [B, T, 128] bf16, tokens at positions pos0 .. pos0+T-1
+ *  ik        [B, T, 64] bf16 or NULL (no indexer stream, e.g. HCA)
+ *  z         [B, T, 2] fp32 or NULL
+ *  beta      [L] fp32, L = 2m if overlap else m
+ *  prev_kv   [B, m, 128] bf16: the m tokens just before pos0; required when
+ *            overlap = 1 and pos0 > 0, ignored otherwise (may be NULL)
+ *  prev_ik   [B, m, 64] bf16: same for ik (required iff ik and prev_kv are)
+ *  prev_z    [B, m, 2] fp32 or NULL
+ *  pos0      multiple of m; one entry is written per block of m tokens that
+ *            ends inside [pos0, pos0+T): N_new = T / m entries, the first with
+ *            entry index pos0/m.  Trailing tokens of an incomplete block form
+ *            no entry (the caller passes them again with the next chunk).
+ *  entries_out       entry_fmt BF16: [B, N_new, 128] bf16.
+ *                    entry_fmt FP8_ROPE_BF16: [B, N_new, 64] e4m3 codes of
+ *                    x / scale, scale = amax(dims 0..63) / 448 (fp32).
+ *  entries_rope_out  FP8_ROPE_BF16 only: [B, N_new, 64] bf16 (dims 64..127)
+ *  entry_scale_out   FP8_ROPE_BF16 only: [B, N_new] fp32
+ *  kidx_out          [B, N_new, 64] bf16, or [B, N_new, 32] MXFP4 codes
+ *  kidx_scale_out    MXFP4 only: [B, N_new, 2] e8m0
+ * Returns CSA_INVALID_ARG for a bad shape, format or missing prev rows.
+ */
+int csa_compress(const void* kv, const void* ik, const float* z, const float* beta,
+                 const void* prev_kv, const void* prev_ik, const float* prev_z,
+                 int B, int T, int64_t pos0, int D, int d_idx, int m, int overlap,
+                 int rope_dims, float rope_base,
+                 void* entries_out, void* entries_rope_out, float* entry_scale_out,
+                 int entry_fmt, void* kidx_out, uint8_t* kidx_scale_out, int kidx_fmt,
+                 void* stream);
+
+/*
+ * csa_index_topk -- Lightning Indexer scores and per-query top-k selection.
+ * Wiki summary item 1 (indexer scores in FP4), "deepseek V4 技术论文" 1.1
+ * (low-rank + FP4 indexer selects the top-k entries per query token),
+ * aifrontier EP95 "Lightning Indexer and top-k" segment (top-k must see every
+ * entry).  The pages give no formula; this library computes the DSA form
+ *     I[t,s] = sum_h w[t,h] * relu(<qI[t,h], kI[s]>)
+ * for every visible entry s (p_s <= t, s < N): each dot product in fp32
+ * (exact for MXFP4 operands), the head sum as an fp32 fma chain in
+ * ascending h starting from +0.  It keeps the min(k, n_vis) largest scores,
+ * ties going to the lower entry index, and writes their indices in ascending
+ * order, padded with -1 up to k.
+ *
+ *  qidx        fmt BF16: [B, n, H_I, 64] bf16.  fmt MXFP4 with
+ *              qidx_scale == NULL: [B, n, H_I, 64] bf16, quantised in-kernel
+ *              to MXFP4 (OCP MX rule: E = floor(log2 amax) - 2, RNE,
+ *              saturating).  fmt MXFP4 with qidx_scale: [B, n, H_I, 32] codes.
+ *  qidx_scale  [B, n, H_I, 2] e8m0 or NULL
+ *  widx        [B, n, H_I] fp32 head weights
+ *  kidx        fmt BF16: [B, N, 64] bf16; fmt MXFP4: [B, N, 32] codes
+ *  kidx_scale  fmt MXFP4: [B, N, 2] e8m0
+ *  H_I         1..8; d_idx = 64; 1 <= k <= 2048
+ *  idx_out     [B, n, k] int32
+ *  ws, ws_bytes  device scratch of at least csa_index_topk_workspace_bytes()
+ *              bytes (may be NULL when that is 0)
+ */
+int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* widx,
+                   const void* kidx, const uint8_t* kidx_scale, int fmt,
+                   int B, int n, int64_t q_pos0, int H_I, int d_idx, int N, int m, int k,
+                   int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m, int k);
+
+/*
+ * csa_attend -- CSA core attention: sparse entries + sliding window + sink.
+ * "deepseek V4 技术论文" 1.1 (each query attends to its top-k entries; the
+ * entries are both key and value, shared by all heads: MQA), wiki summary
+ * item 1 (n_win = 128 sliding-window branch, attention sink, partial RoPE
+ * with inverse RoPE on the output).  For each (t, h) one softmax over
+ *     {sink[h]} U {entries idx[t][i] >= 0} U {window rows j, max(0,t-n_win+1) <= j <= t}
+ * with logits <rot(q[t,h], t), key> / sqrt(D) and the sink logit sink[h]
+ * (zero value).  Value = key row (all 128 dims).  Output dims 64..127 get
+ * the inverse rotation by t.  bf16 MFMA products, fp32 softmax and
+ * accumulation, bf16 output.
+ *
+ *  q            [B, n, H, 128] bf16 pre-RoPE; H a multiple of 16, <= 128
+ *  entries      BF16: [B, N, 128] bf16 post-RoPE.  FP8_ROPE_BF16:
+ *               [B, N, 64] e4m3 codes (value = code * entry_scale)
+ *  entries_rope FP8_ROPE_BF16: [B, N, 64] bf16 (dims 64..127); else NULL
+ *  entry_scale  FP8_ROPE_BF16: [B, N] fp32; else NULL
+ *  idx          [B, n, k] int32 entry indices (-1 = unused slot); every
+ *               index must be < N (not checked on the device)
+ *  win_kv       [B, win_len, 128] bf16 pre-RoPE raw rows at positions
+ *               win_pos0 .. win_pos0+win_len-1; must cover
+ *               [max(0, q_pos0-n_win+1), q_pos0+n-1] when n_win > 0
+ *  n_win        0 (no window) .. 128
+ *  sink         [H] fp32 or NULL (no sink)
+ *  out          [B, n, H, 128] bf16
+ */
+int csa_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D,
+               const void* entries, const void* entries_rope, const float* entry_scale,
+               int entry_fmt, int N, int m, const int32_t* idx, int k,
+               const void* win_kv, int64_t win_pos0, int win_len, int n_win,
+               const float* sink, int rope_dims, float rope_base, void* out, void* stream);
+
+/*
+ * hca_attend -- HCA dense attention over every visible entry + window + sink
+ * (wiki summary item 1: HCA keeps dense attention over the m' = 128
+ * compressed entries; "deepseek V4 技术论文" 1.1).  As csa_attend with the
+ * entry set {s < N : (s+1)m - 1 <= t}; entries are BF16 [B, N, 128].
+ */
+int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D,
+               const void* entries, int N, int m,
+               const void* win_kv, int64_t win_pos0, int win_len, int n_win,
+               const float* sink, int rope_dims, float rope_base, void* out, void* stream);
+
+/* Thread-local description of the last error (empty string if none). */
+const char* csa_last_error(void);
+/* Library version: major*10000 + minor*100 + patch. */
+int csa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

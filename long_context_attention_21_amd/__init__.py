@@ -1,0 +1,135 @@
+"""MI355X-native hybrid compressed attention forward (CSA + HCA).
+
+Python binding of the C ABI in include/csa.h.  Every function here only
+marshals arguments: torch tensors supply device memory and the current HIP
+stream; every step of the computation runs in the HIP kernels of
+``libcsa_mi355x.so``.  Output tensors are allocated with torch when the
+caller does not pass them.
+
+Names follow the C ABI: csa_compress, csa_index_topk, csa_attend, hca_attend.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import (FMT_BF16, FMT_FP8_ROPE_BF16, FMT_MXFP4, CsaError, check, lib)
+
+__all__ = ["csa_compress", "csa_index_topk", "csa_attend", "hca_attend", "version", "CsaError",
+           "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16"]
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _fmt(name):
+    return {"bf16": FMT_BF16, "mxfp4": FMT_MXFP4, "fp8": FMT_FP8_ROPE_BF16}[name]
+
+
+def version():
+    return lib().csa_version()
+
+
+def csa_compress(kv, beta, m, overlap, pos0=0, ik=None, z=None, prev_kv=None, prev_ik=None,
+                 prev_z=None, rope_dims=64, rope_base=10000.0, entry_fmt="bf16", kidx_fmt="mxfp4",
+                 out=None, stream=None):
+    """kv [B, T, 128] bf16 -> dict(entries, entries_rope, entry_scale, kidx, kidx_scale).
+    ``out`` may hold preallocated output tensors under the same keys (e.g.
+    views into a larger cache)."""
+    B, T, D = kv.shape
+    n_new = T // m
+    dev = kv.device
+    out = dict(out or {})
+    ef, kf = _fmt(entry_fmt), _fmt(kidx_fmt)
+    if "entries" not in out:
+        if ef == FMT_BF16:
+            out["entries"] = torch.empty((B, n_new, D), dtype=torch.bfloat16, device=dev)
+        else:
+            out["entries"] = torch.empty((B, n_new, 64), dtype=torch.uint8, device=dev)
+    if ef == FMT_FP8_ROPE_BF16:
+        out.setdefault("entries_rope", torch.empty((B, n_new, 64), dtype=torch.bfloat16, device=dev))
+        out.setdefault("entry_scale", torch.empty((B, n_new), dtype=torch.float32, device=dev))
+    if ik is not None:
+        if kf == FMT_BF16:
+            out.setdefault("kidx", torch.empty((B, n_new, 64), dtype=torch.bfloat16, device=dev))
+        else:
+            out.setdefault("kidx", torch.empty((B, n_new, 32), dtype=torch.uint8, device=dev))
+            out.setdefault("kidx_scale", torch.empty((B, n_new, 2), dtype=torch.uint8, device=dev))
+    check(lib().csa_compress(
+        _ptr(kv), _ptr(ik), _ptr(z), _ptr(beta), _ptr(prev_kv), _ptr(prev_ik), _ptr(prev_z),
+        B, T, int(pos0), D, 64 if ik is not None else 0, m, int(overlap), rope_dims,
+        float(rope_base), _ptr(out["entries"]), _ptr(out.get("entries_rope")),
+        _ptr(out.get("entry_scale")), ef, _ptr(out.get("kidx")), _ptr(out.get("kidx_scale")), kf,
+        _stream(stream)))
+    return out
+
+
+def csa_index_topk(qidx, widx, kidx, k, m, q_pos0=0, fmt="mxfp4", qidx_scale=None,
+                   kidx_scale=None, N=None, idx_out=None, ws=None, stream=None):
+    """qidx [B, n, H_I, 64] bf16 (or [B, n, H_I, 32] MXFP4 codes with
+    qidx_scale), widx [B, n, H_I] fp32, kidx [B, N, 64|32] -> idx [B, n, k] int32."""
+    B, n, H_I = qidx.shape[:3]
+    if N is None:
+        N = kidx.shape[1]
+    f = _fmt(fmt)
+    if idx_out is None:
+        idx_out = torch.empty((B, n, k), dtype=torch.int32, device=qidx.device)
+    need = lib().csa_index_topk_workspace_bytes(B, n, int(q_pos0), N, m, k)
+    if ws is None and need > 0:
+        ws = torch.empty((need,), dtype=torch.uint8, device=qidx.device)
+    check(lib().csa_index_topk(
+        _ptr(qidx), _ptr(qidx_scale), _ptr(widx), _ptr(kidx), _ptr(kidx_scale), f, B, n,
+        int(q_pos0), H_I, 64, N, m, k, _ptr(idx_out), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    return idx_out
+
+
+def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=128, sink=None,
+               entries_rope=None, entry_scale=None, rope_dims=64, rope_base=10000.0, N=None,
+               out=None, stream=None):
+    """q [B, n, H, 128] bf16; entries [B, N, 128] bf16 (or e4m3 [B, N, 64] with
+    entries_rope/entry_scale); idx [B, n, k] int32; win_kv [B, W, 128] bf16."""
+    B, n, H, D = q.shape
+    if N is None:
+        N = entries.shape[1]
+    ef = FMT_BF16 if entries_rope is None else FMT_FP8_ROPE_BF16
+    if out is None:
+        out = torch.empty_like(q, dtype=torch.bfloat16)
+    win_len = 0 if win_kv is None else win_kv.shape[1]
+    check(lib().csa_attend(
+        _ptr(q), B, n, int(q_pos0), H, D, _ptr(entries), _ptr(entries_rope), _ptr(entry_scale), ef,
+        N, m, _ptr(idx), idx.shape[2], _ptr(win_kv), int(win_pos0), win_len,
+        int(n_win) if win_kv is not None else 0, _ptr(sink), rope_dims, float(rope_base), _ptr(out),
+        _stream(stream)))
+    return out
+
+
+def hca_attend(q, entries, q_pos0=0, m=128, win_kv=None, win_pos0=0, n_win=128, sink=None,
+               rope_dims=64, rope_base=10000.0, N=None, out=None, stream=None):
+    """q [B, n, H, 128] bf16; entries [B, N, 128] bf16: dense attention over
+    every visible entry + window + sink."""
+    B, n, H, D = q.shape
+    if N is None:
+        N = entries.shape[1]
+    if out is None:
+        out = torch.empty_like(q, dtype=torch.bfloat16)
+    win_len = 0 if win_kv is None else win_kv.shape[1]
+    check(lib().hca_attend(
+        _ptr(q), B, n, int(q_pos0), H, D, _ptr(entries), N, m, _ptr(win_kv), int(win_pos0), win_len,
+        int(n_win) if win_kv is not None else 0, _ptr(sink), rope_dims, float(rope_base), _ptr(out),
+        _stream(stream)))
+    return out

@@ -1,0 +1,250 @@
+// abi.cpp -- the C ABI (include/csa.h): host-side argument validation,
+// launch-parameter setup and error reporting.  Nothing is launched unless
+// every argument checks out; errors are reported as status codes plus a
+// thread-local message.  No allocation, no synchronisation.
+#include "../../include/csa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return CSA_OK;
+}
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CSA_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr double kPi = 3.14159265358979323846;
+
+}  // namespace
+
+#define REQUIRE(cond, ...) \
+  do {                     \
+    if (!(cond)) return fail(CSA_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+extern "C" {
+
+const char* csa_last_error(void) { return g_err.c_str(); }
+
+int csa_version(void) { return 100; }
+
+int csa_compress(const void* kv, const void* ik, const float* z, const float* beta,
+                 const void* prev_kv, const void* prev_ik, const float* prev_z, int B, int T,
+                 int64_t pos0, int D, int d_idx, int m, int overlap, int rope_dims,
+                 float rope_base, void* entries_out, void* entries_rope_out,
+                 float* entry_scale_out, int entry_fmt, void* kidx_out, uint8_t* kidx_scale_out,
+                 int kidx_fmt, void* stream) {
+  REQUIRE(B >= 0 && T >= 0, "csa_compress: B=%d and T=%d must be >= 0", B, T);
+  REQUIRE(D == 128, "csa_compress: D=%d unsupported (head dim must be 128)", D);
+  REQUIRE(m >= 1 && m <= 128, "csa_compress: m=%d must be in [1, 128]", m);
+  REQUIRE(overlap == 0 || overlap == 1, "csa_compress: overlap=%d must be 0 or 1", overlap);
+  REQUIRE(rope_dims == 0 || rope_dims == 64, "csa_compress: rope_dims=%d must be 0 or 64", rope_dims);
+  REQUIRE(rope_dims == 0 || (std::isfinite(rope_base) && rope_base > 1.0f),
+          "csa_compress: rope_base must be finite and > 1");
+  REQUIRE(pos0 >= 0 && pos0 % m == 0, "csa_compress: pos0=%lld must be a non-negative multiple of m",
+          (long long)pos0);
+  REQUIRE(beta != nullptr, "csa_compress: beta is NULL");
+  const int n_new = T / m;
+  if ((int64_t)B * n_new == 0) return ok();
+  REQUIRE(kv != nullptr, "csa_compress: kv is NULL");
+  REQUIRE(entries_out != nullptr, "csa_compress: entries_out is NULL");
+  REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16,
+          "csa_compress: entry_fmt=%d unsupported", entry_fmt);
+  if (entry_fmt == CSA_FMT_FP8_ROPE_BF16)
+    REQUIRE(entries_rope_out && entry_scale_out,
+            "csa_compress: FP8 entries need entries_rope_out and entry_scale_out");
+  if (ik) {
+    REQUIRE(d_idx == 64, "csa_compress: d_idx=%d unsupported (must be 64)", d_idx);
+    if (kidx_out) {
+      REQUIRE(kidx_fmt == CSA_FMT_BF16 || kidx_fmt == CSA_FMT_MXFP4,
+              "csa_compress: kidx_fmt=%d unsupported", kidx_fmt);
+      if (kidx_fmt == CSA_FMT_MXFP4)
+        REQUIRE(kidx_scale_out != nullptr, "csa_compress: MXFP4 kidx needs kidx_scale_out");
+    }
+  }
+  const bool need_prev = overlap && pos0 > 0;
+  if (need_prev) {
+    REQUIRE(prev_kv != nullptr, "csa_compress: prev_kv is required when overlap=1 and pos0>0");
+    if (ik) REQUIRE(prev_ik != nullptr, "csa_compress: prev_ik is required when ik is given and pos0>0");
+  }
+  REQUIRE(((uintptr_t)kv & 3u) == 0 && ((uintptr_t)ik & 3u) == 0 && ((uintptr_t)entries_out & 3u) == 0 &&
+              ((uintptr_t)prev_kv & 3u) == 0 && ((uintptr_t)prev_ik & 3u) == 0 &&
+              ((uintptr_t)kidx_out & 3u) == 0 && ((uintptr_t)entries_rope_out & 3u) == 0,
+          "csa_compress: tensor pointers must be 4-byte aligned");
+
+  csa::CompressParams p{};
+  p.kv = (const uint32_t*)kv;
+  p.ik = (const uint32_t*)ik;
+  p.z = z;
+  p.beta = beta;
+  p.prev_kv = need_prev ? (const uint32_t*)prev_kv : nullptr;
+  p.prev_ik = need_prev ? (const uint32_t*)prev_ik : nullptr;
+  p.prev_z = need_prev ? prev_z : nullptr;
+  p.B = B;
+  p.T = T;
+  p.n_new = n_new;
+  p.m = m;
+  p.L = overlap ? 2 * m : m;
+  p.overlap = overlap;
+  p.rope_dims = rope_dims;
+  p.pos0 = pos0;
+  p.entries_out = entries_out;
+  p.entries_rope_out = entries_rope_out;
+  p.entry_scale_out = entry_scale_out;
+  p.entry_fmt = entry_fmt;
+  p.kidx_out = ik ? kidx_out : nullptr;
+  p.kidx_scale_out = kidx_scale_out;
+  p.kidx_fmt = kidx_fmt;
+  for (int f = 0; f < 32; ++f) p.theta[f] = std::pow((double)rope_base, -2.0 * f / 64.0);
+  return hip_status(csa::launch_compress(p, (hipStream_t)stream), "csa_compress launch");
+}
+
+size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m, int k) {
+  return csa::index_topk_workspace(B, n, q_pos0, N, m, k);
+}
+
+int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* widx,
+                   const void* kidx, const uint8_t* kidx_scale, int fmt, int B, int n,
+                   int64_t q_pos0, int H_I, int d_idx, int N, int m, int k, int32_t* idx_out,
+                   void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(B >= 0 && n >= 0 && N >= 0, "csa_index_topk: B=%d n=%d N=%d must be >= 0", B, n, N);
+  REQUIRE(fmt == CSA_FMT_BF16 || fmt == CSA_FMT_MXFP4, "csa_index_topk: fmt=%d unsupported", fmt);
+  REQUIRE(d_idx == 64, "csa_index_topk: d_idx=%d unsupported (must be 64)", d_idx);
+  REQUIRE(H_I >= 1 && H_I <= 8, "csa_index_topk: H_I=%d must be in [1, 8]", H_I);
+  REQUIRE(k >= 1 && k <= 2048, "csa_index_topk: k=%d must be in [1, 2048]", k);
+  REQUIRE(m >= 1, "csa_index_topk: m=%d must be >= 1", m);
+  REQUIRE(q_pos0 >= 0, "csa_index_topk: q_pos0 must be >= 0");
+  if ((int64_t)B * n == 0) return ok();
+  REQUIRE(qidx && widx && idx_out, "csa_index_topk: qidx, widx and idx_out must be non-NULL");
+  REQUIRE(N == 0 || kidx != nullptr, "csa_index_topk: kidx is NULL");
+  if (fmt == CSA_FMT_MXFP4) REQUIRE(N == 0 || kidx_scale != nullptr, "csa_index_topk: MXFP4 needs kidx_scale");
+  REQUIRE(fmt == CSA_FMT_BF16 || qidx_scale == nullptr || aligned16(qidx),
+          "csa_index_topk: qidx must be 16-byte aligned");
+  REQUIRE(aligned16(qidx) && aligned16(kidx), "csa_index_topk: qidx and kidx must be 16-byte aligned");
+  const size_t need = csa::index_topk_workspace(B, n, q_pos0, N, m, k);
+  if (ws_bytes < need)
+    return fail(CSA_WORKSPACE_TOO_SMALL, "csa_index_topk: workspace of %zu bytes < %zu needed", ws_bytes, need);
+  csa::IndexParams p{};
+  p.q = qidx;
+  p.q_scale = (fmt == CSA_FMT_MXFP4) ? qidx_scale : nullptr;
+  p.w = widx;
+  p.kidx = kidx;
+  p.kidx_scale = kidx_scale;
+  p.fmt = fmt;
+  p.B = B;
+  p.n = n;
+  p.H_I = H_I;
+  p.N = N;
+  p.m = m;
+  p.k = k;
+  p.q_pos0 = q_pos0;
+  p.idx_out = idx_out;
+  p.ws = ws;
+  p.ws_bytes = ws_bytes;
+  return hip_status(csa::launch_index_topk(p, (hipStream_t)stream), "csa_index_topk launch");
+}
+
+static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, int H, int D,
+                         const void* entries, const void* entries_rope, const float* entry_scale,
+                         int N, int m, const int32_t* idx, int k, const void* win_kv,
+                         int64_t win_pos0, int win_len, int n_win, const float* sink,
+                         int rope_dims, float rope_base, void* out, void* stream,
+                         const char* name) {
+  REQUIRE(B >= 0 && n >= 0 && N >= 0 && k >= 0, "%s: B, n, N and k must be >= 0", name);
+  REQUIRE(D == 128, "%s: D=%d unsupported (head dim must be 128)", name, D);
+  REQUIRE(H >= 1 && H <= 64, "%s: H=%d must be in [1, 64]", name, H);
+  REQUIRE(m >= 1, "%s: m=%d must be >= 1", name, m);
+  REQUIRE(q_pos0 >= 0, "%s: q_pos0 must be >= 0", name);
+  REQUIRE(rope_dims == 0 || rope_dims == 64, "%s: rope_dims=%d must be 0 or 64", name, rope_dims);
+  REQUIRE(rope_dims == 0 || (std::isfinite(rope_base) && rope_base > 1.0f),
+          "%s: rope_base must be finite and > 1", name);
+  REQUIRE(n_win >= 0, "%s: n_win=%d must be >= 0", name, n_win);
+  if ((int64_t)B * n == 0) return ok();
+  REQUIRE(q != nullptr && out != nullptr, "%s: q and out must be non-NULL", name);
+  REQUIRE(N == 0 || entries != nullptr, "%s: entries is NULL", name);
+  if (mode == 0 || mode == 1) REQUIRE(k == 0 || idx != nullptr, "%s: idx is NULL", name);
+  if (mode == 1) REQUIRE(N == 0 || (entries_rope && entry_scale), "%s: FP8 entries need entries_rope and entry_scale", name);
+  if (n_win > 0) {
+    REQUIRE(win_kv != nullptr, "%s: win_kv is NULL but n_win > 0", name);
+    int64_t lo = q_pos0 - n_win + 1;
+    if (lo < 0) lo = 0;
+    const int64_t hi = q_pos0 + n - 1;
+    REQUIRE(win_len >= 0 && win_pos0 <= lo && win_pos0 + win_len - 1 >= hi,
+            "%s: window source [%lld, %lld) does not cover positions [%lld, %lld]", name,
+            (long long)win_pos0, (long long)(win_pos0 + win_len), (long long)lo, (long long)hi);
+  }
+  REQUIRE(aligned16(q) && aligned16(entries) && aligned16(entries_rope) && aligned16(win_kv) &&
+              aligned16(out),
+          "%s: q, entries, entries_rope, win_kv and out must be 16-byte aligned", name);
+  csa::AttendParams p{};
+  p.q = (const uint16_t*)q;
+  p.B = B;
+  p.n = n;
+  p.H = H;
+  p.q_pos0 = q_pos0;
+  p.entries = (const uint16_t*)entries;
+  p.entries_rope = (const uint16_t*)entries_rope;
+  p.entry_scale = entry_scale;
+  p.N = N;
+  p.m = m;
+  p.idx = idx;
+  p.k = (mode == 2) ? 0 : k;
+  p.win = (const uint16_t*)win_kv;
+  p.win_pos0 = win_pos0;
+  p.win_len = win_len;
+  p.n_win = n_win;
+  p.sink = sink;
+  p.rope = rope_dims == 64 ? 1 : 0;
+  p.qscale = (float)(1.4426950408889634 / std::sqrt(128.0));
+  p.out = (uint16_t*)out;
+  for (int f = 0; f < 32; ++f) p.rev[f] = std::pow((double)rope_base, -2.0 * f / 64.0) / (2.0 * kPi);
+  return hip_status(csa::launch_attend(p, mode == 2 ? 2 : mode, (hipStream_t)stream), name);
+}
+
+int csa_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const void* entries,
+               const void* entries_rope, const float* entry_scale, int entry_fmt, int N, int m,
+               const int32_t* idx, int k, const void* win_kv, int64_t win_pos0, int win_len,
+               int n_win, const float* sink, int rope_dims, float rope_base, void* out,
+               void* stream) {
+  REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16,
+          "csa_attend: entry_fmt=%d unsupported", entry_fmt);
+  return attend_common(entry_fmt == CSA_FMT_BF16 ? 0 : 1, q, B, n, q_pos0, H, D, entries,
+                       entries_rope, entry_scale, N, m, idx, k, win_kv, win_pos0, win_len, n_win,
+                       sink, rope_dims, rope_base, out, stream, "csa_attend");
+}
+
+int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const void* entries,
+               int N, int m, const void* win_kv, int64_t win_pos0, int win_len, int n_win,
+               const float* sink, int rope_dims, float rope_base, void* out, void* stream) {
+  return attend_common(2, q, B, n, q_pos0, H, D, entries, nullptr, nullptr, N, m, nullptr, 0,
+                       win_kv, win_pos0, win_len, n_win, sink, rope_dims, rope_base, out, stream,
+                       "hca_attend");
+}
+
+}  // extern "C"

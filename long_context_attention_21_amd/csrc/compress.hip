@@ -1,0 +1,178 @@
+// compress.hip -- token-level KV compressor (CSA m = 4 overlapped, HCA m = 128).
+//
+// Method: "DeepSeek-V4: Towards Highly Efficient Million-Token Context
+// Intelligence" wiki summary, Proposed method item 1 (every m tokens become
+// one entry by a weighted average; adjacent blocks overlap for CSA);
+// "deepseek V4 技术论文" 1.1 (C^b overlaps C^a).  Storage formats: wiki
+// summary, Training infrastructure item 5 (RoPE dims BF16, other dims FP8)
+// and Post-training item 3 (MXFP4 indexer QK path).
+//
+// Design: HBM-bound strided pooling.  One wave per output entry; lane l owns
+// KV dims 2l, 2l+1 (one 4-byte load per token row, a 256-byte coalesced row
+// per wave) and, for lanes 0..31, indexer dims 2l, 2l+1.  The L <= 256 slot
+// logits are staged in LDS: the softmax is evaluated in fp64 (exp of
+// max-subtracted logits, summed in ascending slot order) and each weight is
+// rounded to fp32; pooling is an fp32 fma chain in ascending slot order.  The
+// RoPE dims (lanes 32..63) are rotated in fp64 at the entry position.  This
+// fixed order makes the pooled fp32 values -- and so every storage code --
+// reproducible and independent of the launch shape.
+#include "device.h"
+#include "kernels.h"
+
+// The fp64 rotation and the pooling chain must not be contracted further.
+#pragma clang fp contract(off)
+
+namespace csa {
+
+constexpr int kCompressWaves = 4;
+
+__global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
+  __shared__ double s_logit[kCompressWaves][256];
+  __shared__ double s_exp[kCompressWaves][256];
+  __shared__ float s_w[kCompressWaves][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int64_t task = (int64_t)blockIdx.x * kCompressWaves + wv;
+  const int64_t total = (int64_t)p.B * p.n_new;
+  const bool active = task < total;
+  const int b = active ? (int)(task / p.n_new) : 0;
+  const int e = active ? (int)(task % p.n_new) : 0;
+  const int m = p.m, L = p.L;
+  const int64_t i = p.pos0 / m + e;  // absolute entry index
+  const float NEG_INF = -__builtin_inff();
+
+  // ---- slot logits
+  for (int r = lane; r < L; r += 64) {
+    int64_t j;
+    int role;
+    if (p.overlap) {
+      role = (r < m) ? 1 : 0;
+      j = (r < m) ? (i - 1) * m + r : i * m + (r - m);
+    } else {
+      role = 0;
+      j = i * m + r;
+    }
+    double lg = (double)NEG_INF;
+    if (active && j >= 0) {
+      double zz = 0.0;
+      if (j >= p.pos0) {
+        if (p.z) zz = (double)p.z[((int64_t)b * p.T + (j - p.pos0)) * 2 + role];
+      } else if (p.prev_z) {
+        zz = (double)p.prev_z[((int64_t)b * m + (j - (p.pos0 - m))) * 2 + role];
+      }
+      lg = (double)p.beta[r] + zz;
+    }
+    s_logit[wv][r] = lg;
+  }
+  __syncthreads();
+  double mx = (double)NEG_INF;
+  for (int r = 0; r < L; ++r) mx = fmax(mx, s_logit[wv][r]);
+  for (int r = lane; r < L; r += 64) {
+    double lg = s_logit[wv][r];
+    s_exp[wv][r] = (lg == (double)NEG_INF) ? 0.0 : exp(lg - mx);
+  }
+  __syncthreads();
+  double sum = 0.0;
+  for (int r = 0; r < L; ++r) sum += s_exp[wv][r];
+  for (int r = lane; r < L; r += 64) {
+    double lg = s_logit[wv][r];
+    s_w[wv][r] = (lg == (double)NEG_INF) ? NEG_INF : (float)(s_exp[wv][r] / sum);
+  }
+  __syncthreads();
+  if (!active) return;
+
+  // ---- pooling: fp32 fma chain in ascending slot order
+  float a0 = 0.0f, a1 = 0.0f, k0 = 0.0f, k1 = 0.0f;
+  const bool has_ik = p.ik != nullptr;
+  for (int r = 0; r < L; ++r) {
+    float w = s_w[wv][r];
+    if (w == NEG_INF) continue;  // absent slot (before token 0)
+    int64_t j = p.overlap ? ((r < m) ? (i - 1) * m + r : i * m + (r - m)) : i * m + r;
+    const uint32_t* xr;
+    const uint32_t* ur = nullptr;
+    if (j >= p.pos0) {
+      int64_t row = (int64_t)b * p.T + (j - p.pos0);
+      xr = p.kv + row * 64;
+      if (has_ik) ur = p.ik + row * 32;
+    } else {
+      int64_t row = (int64_t)b * m + (j - (p.pos0 - m));
+      xr = p.prev_kv + row * 64;
+      if (has_ik) ur = p.prev_ik + row * 32;
+    }
+    uint32_t x = xr[lane];
+    a0 = __builtin_fmaf(w, bf16lo(x), a0);
+    a1 = __builtin_fmaf(w, bf16hi(x), a1);
+    if (has_ik && lane < 32) {
+      uint32_t u = ur[lane];
+      k0 = __builtin_fmaf(w, bf16lo(u), k0);
+      k1 = __builtin_fmaf(w, bf16hi(u), k1);
+    }
+  }
+
+  // ---- RoPE at p_i = (i+1)m - 1, fp64 rotation (lanes 32..63 own dims 64..127)
+  if (p.rope_dims == 64 && lane >= 32) {
+    const int f = lane - 32;
+    double phi = (double)((i + 1) * m - 1) * p.theta[f];
+    double c = cos(phi), s = sin(phi);
+    double x0 = a0, x1 = a1;
+    double r0 = x0 * c - x1 * s;
+    double r1 = x0 * s + x1 * c;
+    a0 = (float)r0;
+    a1 = (float)r1;
+  }
+
+  // ---- store the KV entry
+  const int64_t orow = (int64_t)b * p.n_new + e;
+  if (p.entry_fmt == 0) {
+    ((uint32_t*)p.entries_out)[orow * 64 + lane] = pack_bf16(a0, a1);
+  } else {
+    // dims 0..63 (lanes 0..31) -> e4m3 with scale amax/448; dims 64..127 -> bf16
+    float amax = (lane < 32) ? fmaxf(fabsf(a0), fabsf(a1)) : 0.0f;
+    for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    float scale = __fdiv_rn(amax, 448.0f);
+    if (lane < 32) {
+      uint32_t c0 = 0, c1 = 0;
+      if (scale != 0.0f) {
+        c0 = f32_to_e4m3(__fdiv_rn(a0, scale));
+        c1 = f32_to_e4m3(__fdiv_rn(a1, scale));
+      }
+      ((uint16_t*)p.entries_out)[orow * 32 + lane] = (uint16_t)(c0 | (c1 << 8));
+      if (lane == 0) p.entry_scale_out[orow] = scale;
+    } else {
+      ((uint32_t*)p.entries_rope_out)[orow * 32 + (lane - 32)] = pack_bf16(a0, a1);
+    }
+  }
+
+  // ---- store the indexer key
+  if (has_ik && p.kidx_out) {
+    if (p.kidx_fmt == 0) {
+      if (lane < 32) ((uint32_t*)p.kidx_out)[orow * 32 + lane] = pack_bf16(k0, k1);
+    } else {
+      // MXFP4: block 0 = dims 0..31 (lanes 0..15), block 1 = dims 32..63 (lanes 16..31)
+      float amax = fmaxf(fabsf(k0), fabsf(k1));
+      for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      if (lane < 32) {
+        uint32_t code = 0, sbyte = 0;
+        if (amax > 0.0f) {
+          int E = mxfp4_exponent(amax);
+          sbyte = (uint32_t)(E + 127);
+          uint32_t c0 = f32_to_e2m1(__builtin_ldexpf(k0, -E));
+          uint32_t c1 = f32_to_e2m1(__builtin_ldexpf(k1, -E));
+          code = c0 | (c1 << 4);
+        }
+        p.kidx_out_u8()[orow * 32 + lane] = (uint8_t)code;
+        if ((lane & 15) == 0) p.kidx_scale_out[orow * 2 + (lane >> 4)] = (uint8_t)sbyte;
+      }
+    }
+  }
+}
+
+hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
+  int64_t total = (int64_t)p.B * p.n_new;
+  if (total == 0) return hipSuccess;
+  dim3 grid((unsigned)((total + kCompressWaves - 1) / kCompressWaves));
+  hipLaunchKernelGGL(compress_kernel, grid, dim3(64 * kCompressWaves), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,72 @@
+// kernels.h -- parameter blocks and launchers shared between the C ABI layer
+// (abi.cpp) and the HIP kernels.  All pointers are device pointers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct CompressParams {
+  const uint32_t* kv;       // [B, T, 128] bf16 (read as bf16 pairs)
+  const uint32_t* ik;       // [B, T, 64] bf16 or null
+  const float* z;           // [B, T, 2] or null
+  const float* beta;        // [L]
+  const uint32_t* prev_kv;  // [B, m, 128] or null
+  const uint32_t* prev_ik;  // [B, m, 64] or null
+  const float* prev_z;      // [B, m, 2] or null
+  int B, T, n_new, m, L, overlap, rope_dims;
+  int64_t pos0;
+  void* entries_out;
+  void* entries_rope_out;
+  float* entry_scale_out;
+  int entry_fmt;  // 0 bf16, 2 fp8 + bf16 rope
+  void* kidx_out;
+  uint8_t* kidx_scale_out;
+  int kidx_fmt;  // 0 bf16, 1 mxfp4
+  double theta[32];  // rope_base^(-2f/64), fp64
+  __device__ uint8_t* kidx_out_u8() const { return (uint8_t*)kidx_out; }
+};
+
+hipError_t launch_compress(const CompressParams& p, hipStream_t stream);
+
+struct AttendParams {
+  const uint16_t* q;  // [B, n, H, 128]
+  int B, n, H;
+  int64_t q_pos0;
+  const uint16_t* entries;       // bf16 [B, N, 128] or e4m3 [B, N, 64]
+  const uint16_t* entries_rope;  // fp8 format: bf16 [B, N, 64]
+  const float* entry_scale;      // fp8 format: [B, N]
+  int N, m;
+  const int32_t* idx;  // CSA: [B, n, k]
+  int k;
+  const uint16_t* win;  // [B, win_len, 128]
+  int64_t win_pos0;
+  int win_len, n_win;
+  const float* sink;  // [H] or null
+  int rope;           // 1: rotate dims 64..127
+  float qscale;       // log2(e) / sqrt(128), folded into q
+  uint16_t* out;      // [B, n, H, 128]
+  double rev[32];     // theta_f / (2 pi): revolutions per position
+};
+
+// mode: 0 = CSA with bf16 entries, 1 = CSA with fp8+bf16 entries, 2 = HCA
+hipError_t launch_attend(const AttendParams& p, int mode, hipStream_t stream);
+
+struct IndexParams {
+  const void* q;             // bf16 [B, n, H_I, 64] or mxfp4 codes [B, n, H_I, 32]
+  const uint8_t* q_scale;    // [B, n, H_I, 2] or null (quantise bf16 q in-kernel)
+  const float* w;            // [B, n, H_I]
+  const void* kidx;          // bf16 [B, N, 64] or mxfp4 codes [B, N, 32]
+  const uint8_t* kidx_scale; // [B, N, 2]
+  int fmt;                   // 0 bf16, 1 mxfp4
+  int B, n, H_I, N, m, k;
+  int64_t q_pos0;
+  int32_t* idx_out;          // [B, n, k]
+  void* ws;
+  size_t ws_bytes;
+};
+
+hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream);
+size_t index_topk_workspace(int B, int n, int64_t q_pos0, int N, int m, int k);
+
+}  // namespace csa
