@@ -247,16 +247,14 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const int col = dt * 16 + 4 * (l16 & 3);
-      v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          LDS_PTR(v4i16, Ks + (4 * g + (l16 >> 2)) * KP + col));
-      v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          LDS_PTR(v4i16, Ks + (16 + 4 * g + (l16 >> 2)) * KP + col));
-      bf16x8 a;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = __builtin_bit_cast(__bf16, lo[e]);
-        a[4 + e] = __builtin_bit_cast(__bf16, hi[e]);
-      }
+      // Whole-vector concatenation: building the operand element by element
+      // from the v4i16 form of this builtin was miscompiled (only the low
+      // dword survived), so the v4bf16 form is used with a shuffle.
+      bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          LDS_PTR(bf16x4, Ks + (4 * g + (l16 >> 2)) * KP + col));
+      bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          LDS_PTR(bf16x4, Ks + (16 + 4 * g + (l16 >> 2)) * KP + col));
+      bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht)
         O[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[ht], O[dt][ht], 0, 0, 0);
