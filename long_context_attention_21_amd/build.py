@@ -24,8 +24,12 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result", "-I", INC
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = {
     "compress.hip": DEVICE + ["-ffp-contract=off"],
-    "attend.hip": DEVICE,
-    "index_topk.hip": DEVICE + ["-ffp-contract=off"],
+    # no NaN ever reaches these kernels: non-IEEE mode drops the NaN
+    # canonicalisation that IEEE-mode max/min would otherwise add
+    "attend.hip": DEVICE + ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    # the score MFMA result feeds VALU code directly: keep it in VGPRs
+    "index_topk.hip": DEVICE + ["-ffp-contract=off", "-fno-honor-nans", "-mno-amdgpu-ieee",
+                                "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "abi.cpp": ["-ffp-contract=off"],
 }
 

@@ -7,33 +7,47 @@
 // item 3 (MXFP4 on the indexer QK path), aifrontier EP95 (top-k has to look
 // at every entry, so the scorer must be light).  Score (DSA form):
 //     I[t,s] = sum_h w[t,h] * relu(<qI[t,h], kI[s]>),   h ascending, fp32 fma chain.
+// Selection: the min(k, n_vis) largest scores, ties to the lower entry index,
+// written in ascending index order and padded with -1.
 //
 // Design for CDNA4
-//  * Scores come from one v_mfma_scale_f32_32x32x64_f8f6f4 (MXFP4) or four
+//  * Scores: one v_mfma_scale_f32_32x32x64_f8f6f4 (MXFP4) or four
 //    v_mfma_f32_32x32x16_bf16 per 32 entries.  The 32 A rows are 4 query
-//    tokens x 8 heads, placed so that each lane's 16 accumulator rows are all
-//    8 heads of two tokens: the head sum is then an in-lane fma chain in
-//    ascending head order (MXFP4 dot products are exact, so MXFP4 scores are
+//    tokens x 8 heads, placed so each lane's 16 accumulator rows are all 8
+//    heads of two tokens: the head sum is an in-lane fma chain in ascending
+//    head order (MXFP4 dot products are exact, so MXFP4 scores are
 //    bit-identical to a sequential evaluation).
-//  * Top-k is exact and streaming: each token keeps a candidate buffer in
-//    LDS.  A 128-entry tile appends the candidates that beat the token's
-//    threshold (wave ballot + one LDS atomic per half-wave).  When a buffer
-//    nears capacity the work-group shrinks it to exactly k by an 8-bit radix
-//    selection on (score desc, index asc) and raises the threshold to
-//    "strictly above the k-th score": later entries have larger indices, so
-//    a tie with the k-th score can never enter.  The final set is selected
-//    the same way and bitonic-sorted by index.
+//  * Selection in one scoring pass, without barriers:
+//      1. a strided sample of the visible entries (at most 4096 per token) is
+//         scored; each token's threshold is the sample quantile that leaves
+//         about k + 850 entries above it;
+//      2. every entry is scored once; scores >= threshold are appended to the
+//         wave's private region of the token's LDS candidate buffer (wave
+//         ballot + register counters: no atomics, no cross-lane round trip);
+//      3. one wave per token selects the exact top-k among the candidates
+//         (radix selection on (score desc, index asc) with adaptive digit
+//         positions and early exit), then emits the indices in ascending
+//         order through an LDS bitmap.
+//    Any threshold with at least k candidates above it keeps every top-k
+//    member, so the result is exact.  If a buffer overflows or ends up with
+//    fewer than k candidates, the work-group reruns its tokens with the exact
+//    streaming method (buffers shrunk to exactly k whenever they fill).
 //  * Tokens whose visible entries all fit in k skip scoring.
 #include "device.h"
 #include "kernels.h"
 
 namespace csa {
 
-constexpr int kTile = 128;  // entries per iteration (4 waves x 32)
+constexpr int kTile = 128;   // entries per iteration (4 waves x 32)
+constexpr int kCap = 4096;   // candidate buffer per token
+constexpr int kSeg = 32768;  // bitmap segment (entries) used to sort the result
+constexpr int kReg = kCap / 4;  // per-wave candidate region of a token's buffer
 
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t f = __float_as_uint(x + 0.0f);  // -0 -> +0
-  return (f & 0x80000000u) ? ~f : (f | 0x80000000u);
+__device__ __forceinline__ uint32_t okey(uint32_t fbits) {
+  return (fbits & 0x80000000u) ? ~fbits : (fbits | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 // Row r of the 32-row A operand -> (token j, head h); see the header comment.
@@ -44,55 +58,177 @@ __device__ __forceinline__ void row_to_token_head(int r, int& j, int& h) {
   h = ic & 7;
 }
 
-template <int QT, int CAP>
+template <int QT>
 struct TopkSmem {
-  uint32_t key[QT][CAP];
-  int32_t idx[QT][CAP];
-  uint32_t hist[256];
+  uint32_t key[QT][kCap];       // fp32 score bits of candidates / samples
+  int32_t idx[QT][kCap];        // entry indices of candidates
+  uint32_t bits[4][kSeg / 32];  // per-wave bitmap for the ascending output
+  uint32_t hist[4][256];        // per-wave radix histograms
   int cnt[QT];
-  uint32_t thr[QT];
+  int wcnt[4][QT];              // candidates per (wave, token) region
+  float thr[QT];
+  int fallback;
   uint32_t sel[4];
-  int32_t regs_dummy;
 };
 
-// Radix selection over one token's buffer.  Finds the r-th largest value of
-// keyfn(i) among the elements passing filt(i); returns it, and sets
-// *above = number of passing elements strictly greater, *equal = number equal.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  for (int off = 32; off >= 1; off >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, off));
+  return x;
+}
+
+// ----------------------------------------------------------------------------
+// Wave-level radix selection of the r-th largest (1-based) keyfn(i) over the
+// i < n passing filt(i).  Digits of up to 8 bits start just below the common
+// prefix of all keys.  Returns the threshold T with *above = count of keys
+// above T's bin.  Stops early when the threshold bin holds exactly the
+// remaining rank (then keep(key) = key >= T selects exactly r); otherwise
+// resolves all 32 bits (*exact = true, T is the r-th key, *inbin its count).
 template <class KeyFn, class FiltFn>
-__device__ uint32_t radix_select(uint32_t* hist, uint32_t* sel, int cnt, uint32_t r, KeyFn keyfn,
-                                 FiltFn filt, uint32_t* above, uint32_t* equal) {
+__device__ uint32_t wave_radix(uint32_t* hist, int n, uint32_t r, KeyFn keyfn, FiltFn filt,
+                               uint32_t* above_out, uint32_t* inbin_out, bool* exact_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+  for (int i = lane; i < n; i += 64)
+    if (filt(i)) { uint32_t k = keyfn(i); kmax = max(kmax, k); kmin = min(kmin, k); }
+  kmax = wave_max_u32(kmax);
+  kmin = wave_min_u32(kmin);
+  if (kmax == kmin) {  // every passing key is equal
+    uint32_t c = 0;
+    for (int i = lane; i < n; i += 64) c += filt(i) ? 1u : 0u;
+    for (int off = 32; off >= 1; off >>= 1) c += (uint32_t)__shfl_xor((int)c, off);
+    *above_out = 0;
+    *inbin_out = c;
+    *exact_out = true;
+    return kmax;
+  }
+  const int hb = 31 - __builtin_clz(kmin ^ kmax);  // highest differing bit
+  uint32_t pmask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = kmax & pmask;
+  uint32_t r_left = r, above = 0;
+  int top = hb;  // current digit covers bits [lo, top]
+  while (true) {
+    const int lo = top >= 7 ? top - 7 : 0;
+    const uint32_t dmask = (1u << (top - lo + 1)) - 1u;
+    for (int bb = lane; bb < 256; bb += 64) hist[bb] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < n; i += 64) {
+      if (!filt(i)) continue;
+      const uint32_t k = keyfn(i);
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane owns bins 4l..4l+3; suffix sums over lanes
+    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
+                   h3 = hist[4 * lane + 3];
+    const uint32_t c = h0 + h1 + h2 + h3;
+    uint32_t suf = c;
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_down((int)suf, off);
+      if (lane + off < 64) suf += o;
+    }
+    const uint64_t bal = __ballot(suf >= r_left);
+    const int L = 63 - __builtin_clzll(bal);
+    uint32_t d = 0, acc = 0, hd = 0;
+    if (lane == L) {
+      acc = suf - c;
+      const uint32_t hh[4] = {h0, h1, h2, h3};
+      d = 4 * lane;
+      for (int i = 3; i >= 0; --i) {
+        if (acc + hh[i] >= r_left) { d = 4 * lane + i; hd = hh[i]; break; }
+        acc += hh[i];
+      }
+    }
+    d = (uint32_t)__shfl((int)d, L);
+    acc = (uint32_t)__shfl((int)acc, L);
+    hd = (uint32_t)__shfl((int)hd, L);
+    __builtin_amdgcn_wave_barrier();
+    above += acc;
+    r_left -= acc;
+    prefix |= d << lo;
+    pmask |= dmask << lo;
+    if (hd == r_left || lo == 0) {
+      *above_out = above;
+      *inbin_out = hd;
+      *exact_out = (lo == 0);
+      return prefix;
+    }
+    top = lo - 1;
+  }
+}
+
+// keep(i) = okey > T || (okey == T && (!ties || id <= id_lim)); with !ties,
+// keep(i) = okey >= T.
+struct Sel {
+  uint32_t T;
+  int ties;
+  int32_t id_lim;
+};
+
+template <int QT>
+__device__ Sel wave_select_topk(TopkSmem<QT>& sm, int j, int n, uint32_t r) {
+  const int w = threadIdx.x >> 6;
+  const uint32_t* keys = sm.key[j];
+  const int32_t* ids = sm.idx[j];
+  uint32_t above, inbin;
+  bool exact;
+  const uint32_t T = wave_radix(sm.hist[w], n, r, [&](int i) { return okey(keys[i]); },
+                                [](int) { return true; }, &above, &inbin, &exact);
+  Sel s{T, 0, 0};
+  if (!exact) return s;
+  const uint32_t need = r - above;
+  if (need >= inbin) return s;  // every tie is kept
+  uint32_t a2, b2;
+  bool e2;
+  const uint32_t tinv = wave_radix(sm.hist[w], n, need, [&](int i) { return ~(uint32_t)ids[i]; },
+                                   [&](int i) { return okey(keys[i]) == T; }, &a2, &b2, &e2);
+  s.ties = 1;
+  s.id_lim = (int32_t)~tinv;
+  return s;
+}
+
+// ----------------------------------------------------------------------------
+// Exact streaming fallback (work-group wide): buffers hold order keys and are
+// shrunk to exactly k whenever they fill.
+
+template <class KeyFn, class FiltFn>
+__device__ uint32_t wg_radix_select(uint32_t* hist, uint32_t* sel, int cnt, uint32_t r, KeyFn keyfn,
+                                    FiltFn filt, uint32_t* above, uint32_t* equal) {
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t prefix = 0, pmask = 0, r_left = r, gt_total = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;  // blockDim == 256 bins
+    hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < cnt; i += 256) {
       if (!filt(i)) continue;
-      uint32_t k = keyfn(i);
+      const uint32_t k = keyfn(i);
       if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < 64) {
-      // lane l owns bins 4l..4l+3; suffix sums over lanes
-      uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-      uint32_t c = h0 + h1 + h2 + h3;
+      const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
+                     h3 = hist[4 * lane + 3];
+      const uint32_t c = h0 + h1 + h2 + h3;
       uint32_t suf = c;
       for (int off = 1; off < 64; off <<= 1) {
-        uint32_t o = __shfl_down(suf, off);
+        const uint32_t o = (uint32_t)__shfl_down((int)suf, off);
         if (lane + off < 64) suf += o;
       }
-      uint64_t bal = __ballot(suf >= r_left);
-      int L = 63 - __builtin_clzll(bal);  // last lane whose suffix reaches r_left
+      const uint64_t bal = __ballot(suf >= r_left);
+      const int L = 63 - __builtin_clzll(bal);
       if (lane == L) {
-        uint32_t acc = suf - c;  // count in bins above this lane's bins
-        uint32_t hh[4] = {h0, h1, h2, h3};
+        uint32_t acc = suf - c;
+        const uint32_t hh[4] = {h0, h1, h2, h3};
         int d = 4 * lane;
         for (int i = 3; i >= 0; --i) {
           if (acc + hh[i] >= r_left) { d = 4 * lane + i; break; }
           acc += hh[i];
         }
         sel[0] = (uint32_t)d;
-        sel[1] = acc;             // passing elements with this prefix and a larger digit
+        sel[1] = acc;
         sel[2] = hist[d];
       }
     }
@@ -109,39 +245,38 @@ __device__ uint32_t radix_select(uint32_t* hist, uint32_t* sel, int cnt, uint32_
   return prefix;
 }
 
-// Keep exactly the kk best (score desc, index asc) elements of token j's buffer.
-template <int QT, int CAP>
-__device__ void shrink_exact(TopkSmem<QT, CAP>& sm, int j, int kk) {
+template <int QT>
+__device__ void wg_shrink_exact(TopkSmem<QT>& sm, int j, int kk) {
   const int tid = threadIdx.x;
   const int cnt = sm.cnt[j];
   if (cnt <= kk) return;
   uint32_t above, equal;
   uint32_t* keys = sm.key[j];
   int32_t* ids = sm.idx[j];
-  const uint32_t tau = radix_select(sm.hist, sm.sel, cnt, (uint32_t)kk,
-                                    [&](int i) { return keys[i]; }, [](int) { return true; },
-                                    &above, &equal);
-  const uint32_t need = (uint32_t)kk - above;  // ties with tau to keep (lowest index)
+  uint32_t* hist = &sm.hist[0][0];
+  const uint32_t tau = wg_radix_select(hist, sm.sel, cnt, (uint32_t)kk, [&](int i) { return keys[i]; },
+                                       [](int) { return true; }, &above, &equal);
+  const uint32_t need = (uint32_t)kk - above;
   uint32_t tau_inv = 0;
   const bool cut_ties = need < equal;
   if (cut_ties) {
     uint32_t a2, e2;
-    tau_inv = radix_select(sm.hist, sm.sel, cnt, need, [&](int i) { return ~(uint32_t)ids[i]; },
-                           [&](int i) { return keys[i] == tau; }, &a2, &e2);
+    tau_inv = wg_radix_select(hist, sm.sel, cnt, need, [&](int i) { return ~(uint32_t)ids[i]; },
+                              [&](int i) { return keys[i] == tau; }, &a2, &e2);
   }
-  // compact: gather kept elements to registers, then rewrite
-  constexpr int PER = (CAP + 255) / 256;
+  constexpr int PER = kCap / 256;
   uint32_t kv[PER];
   int32_t iv[PER];
   int nk = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    int i = tid + q * 256;
-    kv[q] = 0; iv[q] = -1;
+    const int i = tid + q * 256;
+    kv[q] = 0;
+    iv[q] = -1;
     if (i < cnt) {
-      uint32_t k = keys[i];
-      int32_t id = ids[i];
-      bool keep = (k > tau) || (k == tau && (!cut_ties || ~(uint32_t)id >= tau_inv));
+      const uint32_t k = keys[i];
+      const int32_t id = ids[i];
+      const bool keep = (k > tau) || (k == tau && (!cut_ties || ~(uint32_t)id >= tau_inv));
       if (keep) { kv[q] = k; iv[q] = id; ++nk; }
     }
   }
@@ -150,15 +285,14 @@ __device__ void shrink_exact(TopkSmem<QT, CAP>& sm, int j, int kk) {
   __syncthreads();
   int base = atomicAdd(&sm.cnt[j], nk);
 #pragma unroll
-  for (int q = 0; q < PER; ++q) {
+  for (int q = 0; q < PER; ++q)
     if (iv[q] >= 0) { keys[base] = kv[q]; ids[base] = iv[q]; ++base; }
-  }
-  if (tid == 0) sm.thr[j] = tau + 1u;
+  if (tid == 0) sm.thr[j] = __uint_as_float(tau + 1u);  // order key, strictly above the k-th
   __syncthreads();
 }
 
-template <int QT, int CAP>
-__device__ void bitonic_sort_idx(TopkSmem<QT, CAP>& sm, int j, int cnt) {
+template <int QT>
+__device__ void wg_bitonic_sort(TopkSmem<QT>& sm, int j, int cnt) {
   const int tid = threadIdx.x;
   int P = 1;
   while (P < cnt) P <<= 1;
@@ -168,10 +302,10 @@ __device__ void bitonic_sort_idx(TopkSmem<QT, CAP>& sm, int j, int cnt) {
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = tid; i < (P >> 1); i += 256) {
-        int lo = 2 * i - (i & (stride - 1));
-        int hi = lo + stride;
-        bool asc = (lo & size) == 0;
-        int32_t a = s[lo], bb = s[hi];
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool asc = (lo & size) == 0;
+        const int32_t a = s[lo], bb = s[hi];
         if ((a > bb) == asc) { s[lo] = bb; s[hi] = a; }
       }
       __syncthreads();
@@ -179,14 +313,132 @@ __device__ void bitonic_sort_idx(TopkSmem<QT, CAP>& sm, int j, int cnt) {
   }
 }
 
-template <int QT, int CAP, int FMT>
+// ----------------------------------------------------------------------------
+// Scores of one 32-column tile for the work-group's tokens.  Lane column
+// lane % 32 is entry e (any entry index; e >= N gives a zero column).
+
+template <int FMT>
+struct BTile;
+template <>
+struct BTile<1> {  // MXFP4: 16 code bytes + one e8m0 scale per lane
+  u32x4 cw;
+  int sc;
+};
+template <>
+struct BTile<0> {  // bf16: four 8-element pieces per lane
+  bf16x8 v[4];
+};
+
+template <int FMT>
+struct Scorer {
+  i32x8 A_fp4;
+  int a_scale;
+  bf16x8 A_bf[4];
+  float wv[2][8];
+  const uint8_t* kc;
+  const uint16_t* kb;
+  const uint8_t* ksc;
+  int N;
+
+  // B operand of entry column e (lane % 32).  The address is clamped to the
+  // last entry, so the loads are unconditional; columns e >= N hold garbage
+  // that callers never select (every token's n_vis <= N).
+  __device__ __forceinline__ BTile<FMT> load(int e) const {
+    const int lane = threadIdx.x & 63;
+    const int64_t ec = e < N ? e : N - 1;
+    BTile<FMT> t;
+    if constexpr (FMT == 1) {
+      t.cw = *(const u32x4*)(kc + ec * 32 + (lane >> 5) * 16);
+      t.sc = ksc[ec * 2 + (lane >> 5)];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) t.v[ks] = *(const bf16x8*)(kb + ec * 64 + ks * 16 + (lane >> 5) * 8);
+    }
+    return t;
+  }
+
+  __device__ __forceinline__ void compute(const BTile<FMT>& t, float I[2]) const {
+    f32x16 C;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) C[i] = 0.0f;
+    if constexpr (FMT == 1) {
+      i32x8 B;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { B[i] = (int)t.cw[i]; B[4 + i] = 0; }
+      C = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A_fp4, B, C, 4, 4, 0, a_scale, 0, t.sc);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_bf[ks], t.v[ks], C, 0, 0, 0);
+    }
+    // C rows: heads 0..7 of token jl0 (i = 0..7) and of token jl0 + 1 (i = 8..15).
+    // The chain starts from +0 and can never produce -0.
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float s = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) s = __builtin_fmaf(wv[tt][h], fmaxf(C[tt * 8 + h], 0.0f), s);
+      I[tt] = s;
+    }
+  }
+
+  __device__ __forceinline__ void score(int e, float I[2]) const { compute(load(e), I); }
+};
+
+// Appends the passing lanes of each half-wave to their token's buffer.
+template <int QT>
+__device__ __forceinline__ void append(TopkSmem<QT>& sm, const bool pass[2], const uint32_t val[2],
+                                       int e, int jl0, bool clamp) {
+  const int lane = threadIdx.x & 63;
+  const int leader = (lane < 32) ? 0 : 32;
+  const uint64_t halfmask = (lane < 32) ? 0x00000000ffffffffull : 0xffffffff00000000ull;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const uint64_t mine = __ballot(pass[tt]) & halfmask;
+    const int pc = __builtin_popcountll(mine);
+    const int rank = __builtin_popcountll(mine & ((1ull << lane) - 1ull));
+    const int j = jl0 + tt;
+    int basepos = 0;
+    if (lane == leader && pc > 0) basepos = atomicAdd(&sm.cnt[j < QT ? j : 0], pc);
+    basepos = __shfl(basepos, leader);
+    const int pos = basepos + rank;
+    if (pass[tt] && (!clamp || pos < kCap)) {
+      sm.key[j][pos] = val[tt];
+      sm.idx[j][pos] = e;
+    }
+  }
+}
+
+// Appends the passing lanes of each half-wave to this wave's private region
+// of their token's buffer; the running counts live in registers (uniform per
+// half-wave), so there is no LDS atomic or cross-lane round trip.
+template <int QT>
+__device__ __forceinline__ void append_private(TopkSmem<QT>& sm, const bool pass[2], const uint32_t val[2],
+                                               int e, int jl0, int wcnt[2]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const uint64_t bal = __ballot(pass[tt]);
+    const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+    const int rank = lane < 32 ? (int)__builtin_amdgcn_mbcnt_lo(lo, 0u) : (int)__builtin_amdgcn_mbcnt_hi(hi, 0u);
+    const int pos = wcnt[tt] + rank;
+    if (pass[tt] && pos < kReg) {
+      const int j = jl0 + tt;
+      sm.key[j][wave * kReg + pos] = val[tt];
+      sm.idx[j][wave * kReg + pos] = e;
+    }
+    wcnt[tt] += lane < 32 ? __builtin_popcount(lo) : __builtin_popcount(hi);
+  }
+}
+
+template <int QT, int FMT>
 __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
-  __shared__ TopkSmem<QT, CAP> sm;
+  __shared__ TopkSmem<QT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = (p.n + QT - 1) / QT;
   const int b = blockIdx.x / nblk;
-  // heavy (late) query blocks first
-  const int q0 = (nblk - 1 - (int)(blockIdx.x % nblk)) * QT;
+  const int q0 = (nblk - 1 - (int)(blockIdx.x % nblk)) * QT;  // heavy (late) blocks first
 
   int nv[QT];
   int maxnv = 0;
@@ -196,8 +448,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
     const int q = q0 + j;
     int v = 0;
     if (q < p.n) {
-      int64_t t = p.q_pos0 + q;
-      int64_t c = (t + 1) / p.m;
+      const int64_t c = (p.q_pos0 + q + 1) / p.m;
       v = (int)(c < p.N ? c : p.N);
       if (v > p.k) all_small = false;
     }
@@ -216,193 +467,310 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
     return;
   }
 
-  // ---- A operand: rows (token, head), lane row = lane % 32, k-block = lane / 32
-  int arow_j, arow_h;
-  row_to_token_head(lane & 31, arow_j, arow_h);
-  const int aq = q0 + arow_j;
-  const bool arow_ok = (aq < p.n) && (arow_h < p.H_I);
-  const int64_t qrow = ((int64_t)b * p.n + aq) * p.H_I + arow_h;
-  i32x8 A_fp4;
-  int a_scale = 127;
-  bf16x8 A_bf[4];
-  if (FMT == 1) {
+  // ---- A operand: rows (token, head); lane row = lane % 32, k-block = lane / 32
+  Scorer<FMT> sc;
+  {
+    int arow_j, arow_h;
+    row_to_token_head(lane & 31, arow_j, arow_h);
+    const int aq = q0 + arow_j;
+    const bool arow_ok = (arow_j < QT) && (aq < p.n) && (arow_h < p.H_I);
+    const int64_t qrow = ((int64_t)b * p.n + aq) * p.H_I + arow_h;
+    sc.a_scale = 127;
+    if (FMT == 1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) A_fp4[i] = 0;
-    if (arow_ok) {
-      if (p.q_scale) {
-        u32x4 cw = *(const u32x4*)((const uint8_t*)p.q + qrow * 32 + (lane >> 5) * 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) A_fp4[i] = (int)cw[i];
-        a_scale = p.q_scale[qrow * 2 + (lane >> 5)];
-      } else {
-        // quantise 32 bf16 values of this (row, k-block) to MXFP4
-        const u32x4* src = (const u32x4*)((const uint16_t*)p.q + qrow * 64 + (lane >> 5) * 32);
-        float x[32];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x4 v = src[i];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { x[8 * i + 2 * e] = bf16lo(v[e]); x[8 * i + 2 * e + 1] = bf16hi(v[e]); }
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-        if (amax > 0.0f) {
-          const int E = mxfp4_exponent(amax);
-          a_scale = E + 127;
-#pragma unroll
-          for (int i = 0; i < 32; ++i)
-            A_fp4[i >> 3] |= (int)(f32_to_e2m1(__builtin_ldexpf(x[i], -E)) << (4 * (i & 7)));
-        } else {
-          a_scale = 0;
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int i = 0; i < 8; ++i) sc.A_fp4[i] = 0;
       if (arow_ok) {
-        A_bf[ks] = *(const bf16x8*)((const uint16_t*)p.q + qrow * 64 + ks * 16 + (lane >> 5) * 8);
-      } else {
+        if (p.q_scale) {
+          const u32x4 cw = *(const u32x4*)((const uint8_t*)p.q + qrow * 32 + (lane >> 5) * 16);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) A_bf[ks][e] = (__bf16)0.0f;
+          for (int i = 0; i < 4; ++i) sc.A_fp4[i] = (int)cw[i];
+          sc.a_scale = p.q_scale[qrow * 2 + (lane >> 5)];
+        } else {
+          // quantise this (row, 32-element block) of the bf16 query to MXFP4
+          const u32x4* src = (const u32x4*)((const uint16_t*)p.q + qrow * 64 + (lane >> 5) * 32);
+          float x[32];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const u32x4 v = src[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x[8 * i + 2 * e] = bf16lo(v[e]); x[8 * i + 2 * e + 1] = bf16hi(v[e]); }
+          }
+          float amax = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+          if (amax > 0.0f) {
+            const int E = mxfp4_exponent(amax);
+            sc.a_scale = E + 127;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+              sc.A_fp4[i >> 3] |= (int)(f32_to_e2m1(__builtin_ldexpf(x[i], -E)) << (4 * (i & 7)));
+          } else {
+            sc.a_scale = 0;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (arow_ok) {
+          sc.A_bf[ks] = *(const bf16x8*)((const uint16_t*)p.q + qrow * 64 + ks * 16 + (lane >> 5) * 8);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc.A_bf[ks][e] = (__bf16)0.0f;
+        }
       }
     }
   }
-
-  // ---- head weights of this lane's two tokens (heads >= H_I get weight 0)
   const int jl0 = 2 * (lane >> 5);
-  float wv[2][8];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int q = q0 + jl0 + tt;
-#pragma unroll
-    for (int h = 0; h < 8; ++h)
-      wv[tt][h] = (q < p.n && h < p.H_I && jl0 + tt < QT) ? p.w[((int64_t)b * p.n + q) * p.H_I + h] : 0.0f;
-  }
   int nvl[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int q = q0 + jl0 + tt;
     int v = 0;
     if (jl0 + tt < QT && q < p.n) {
-      int64_t c = (p.q_pos0 + q + 1) / p.m;
+      const int64_t c = (p.q_pos0 + q + 1) / p.m;
       v = (int)(c < p.N ? c : p.N);
     }
     nvl[tt] = v;
+#pragma unroll
+    for (int h = 0; h < 8; ++h)
+      sc.wv[tt][h] = (v > 0 && h < p.H_I) ? p.w[((int64_t)b * p.n + q) * p.H_I + h] : 0.0f;
   }
+  sc.kc = (const uint8_t*)p.kidx + (int64_t)b * p.N * 32;
+  sc.kb = (const uint16_t*)p.kidx + (int64_t)b * p.N * 64;
+  sc.ksc = p.kidx_scale ? p.kidx_scale + (int64_t)b * p.N * 2 : nullptr;
+  sc.N = p.N;
 
-  if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = 0u; }
-  __syncthreads();
-
-  const uint8_t* kc = (const uint8_t*)p.kidx + (int64_t)b * p.N * 32;
-  const uint16_t* kb = (const uint16_t*)p.kidx + (int64_t)b * p.N * 64;
-  const uint8_t* ksc = p.kidx_scale ? p.kidx_scale + (int64_t)b * p.N * 2 : nullptr;
-
-  for (int base = 0; base < maxnv; base += kTile) {
-    const int e0 = base + wave * 32;
-    const int e = e0 + (lane & 31);
-    uint32_t u[2] = {0u, 0u};
-    bool pass[2] = {false, false};
-    if (e0 < maxnv) {
-      f32x16 C;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) C[i] = 0.0f;
-      if (FMT == 1) {
-        i32x8 B;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) B[i] = 0;
-        int b_scale = 127;
-        if (e < p.N) {
-          u32x4 cw = *(const u32x4*)(kc + (int64_t)e * 32 + (lane >> 5) * 16);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) B[i] = (int)cw[i];
-          b_scale = ksc[(int64_t)e * 2 + (lane >> 5)];
-        }
-        C = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A_fp4, B, C, 4, 4, 0, a_scale, 0, b_scale);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          bf16x8 Bv;
-          if (e < p.N) {
-            Bv = *(const bf16x8*)(kb + (int64_t)e * 64 + ks * 16 + (lane >> 5) * 8);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) Bv[i] = (__bf16)0.0f;
-          }
-          C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_bf[ks], Bv, C, 0, 0, 0);
-        }
-      }
-      // epilogue: lane holds C rows = heads 0..7 of tokens jl0 (i = 0..7) and jl0+1 (i = 8..15)
+  // ---- phase 1: per-token thresholds from a strided sample (entry S*i)
+  const bool sampling = maxnv > kCap;
+  const int S = (maxnv + kCap - 1) / kCap;
+  if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = -__builtin_inff(); }
+  if (tid == 0) sm.fallback = 0;
+  if (sampling) {
+    const int max_ns = (maxnv + S - 1) / S;
+    for (int tile = wave; tile * 32 < max_ns; tile += 4) {
+      const int i = tile * 32 + (lane & 31);
+      const int e = S * i;
+      float I[2];
+      sc.score(e, I);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        float I = 0.0f;
-#pragma unroll
-        for (int h = 0; h < 8; ++h) I = __builtin_fmaf(wv[tt][h], fmaxf(C[tt * 8 + h], 0.0f), I);
-        u[tt] = order_key(I);
         const int j = jl0 + tt;
-        pass[tt] = (j < QT) && (e < nvl[tt]) && (u[tt] >= sm.thr[j < QT ? j : 0]);
+        if (j < QT && e < nvl[tt]) sm.key[j][i] = __float_as_uint(I[tt]);
       }
     }
-    // append candidates: each half-wave (32 lanes) serves one token per tt
+  }
+  __syncthreads();
+  if (sampling && wave < QT && nv[wave] > kCap) {
+    const int j = wave;
+    const int ns = (nv[j] + S - 1) / S;
+    int target = p.k + 850;
+    if (target > kCap - 1024) target = kCap - 1024;
+    int r = (int)(((int64_t)target * ns + nv[j] - 1) / nv[j]);
+    r = r < 1 ? 1 : (r > ns ? ns : r);
+    uint32_t above, inbin;
+    bool exact;
+    const uint32_t* keys = sm.key[j];
+    const uint32_t T = wave_radix(sm.hist[wave], ns, (uint32_t)r, [&](int i) { return okey(keys[i]); },
+                                  [](int) { return true; }, &above, &inbin, &exact);
+    if (lane == 0) sm.thr[j] = key_to_float(T);
+  }
+  __syncthreads();
+
+  // ---- phase 2: every entry scored once; candidates >= threshold appended
+  float thr2[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const uint64_t bal = __ballot(pass[tt]);
-      const uint64_t halfmask = (lane < 32) ? 0x00000000ffffffffull : 0xffffffff00000000ull;
-      const uint64_t mine = bal & halfmask;
-      const int pc = __builtin_popcountll(mine);
-      const uint64_t below = mine & ((1ull << lane) - 1ull);
-      const int rank = __builtin_popcountll(below);
-      int basepos = 0;
-      const int leader = (lane < 32) ? 0 : 32;
-      const int j = jl0 + tt;
-      if (lane == leader && pc > 0 && j < QT) basepos = atomicAdd(&sm.cnt[j], pc);
-      basepos = __shfl(basepos, leader);
-      if (pass[tt]) {
-        sm.key[j][basepos + rank] = u[tt];
-        sm.idx[j][basepos + rank] = e;
+  for (int tt = 0; tt < 2; ++tt) {
+    const int j = jl0 + tt;
+    thr2[tt] = (j < QT) ? sm.thr[j < QT ? j : 0] : 0.0f;
+  }
+  {
+    // two tiles in flight: each register set is reloaded right after use
+    const int ecol = wave * 32 + (lane & 31);
+    int wcnt[2] = {0, 0};
+    BTile<FMT> ta = sc.load(ecol), tb = sc.load(ecol + kTile);
+    auto step = [&](const BTile<FMT>& t, int base) {
+      const int e = base + ecol;
+      bool pass[2];
+      uint32_t val[2];
+      float I[2];
+      sc.compute(t, I);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        pass[tt] = (e < nvl[tt]) && (I[tt] >= thr2[tt]);
+        val[tt] = __float_as_uint(I[tt]);
       }
+      append_private<QT>(sm, pass, val, e, jl0, wcnt);
+    };
+    for (int base = 0; base < maxnv; base += 2 * kTile) {
+      step(ta, base);
+      ta = sc.load(base + 2 * kTile + ecol);
+      step(tb, base + kTile);
+      tb = sc.load(base + 3 * kTile + ecol);
     }
+    if ((lane & 31) == 0) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        if (jl0 + tt < QT) sm.wcnt[wave][jl0 + tt] = wcnt[tt];
+    }
+  }
+  __syncthreads();
+  if (wave < QT && lane == 0) {
+    int c = 0;
+    bool over = false;
+    for (int w = 0; w < 4; ++w) {
+      c += sm.wcnt[w][wave];
+      over |= sm.wcnt[w][wave] > kReg;
+    }
+    sm.cnt[wave] = c;
+    const int want = nv[wave] < p.k ? nv[wave] : p.k;
+    if (over || c < want) atomicOr(&sm.fallback, 1);
+  }
+  __syncthreads();
+
+  if (sm.fallback) {
+    // ---- exact streaming fallback for every token of this work-group
+    if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = __uint_as_float(0u); }
     __syncthreads();
-    int cnow[QT];
+    for (int base = 0; base < maxnv; base += kTile) {
+      const int e0 = base + wave * 32;
+      const int e = e0 + (lane & 31);
+      bool pass[2] = {false, false};
+      uint32_t val[2] = {0u, 0u};
+      if (e0 < maxnv) {
+        float I[2];
+        sc.score(e, I);
 #pragma unroll
-    for (int j = 0; j < QT; ++j) cnow[j] = sm.cnt[j];
-    __syncthreads();  // every thread has read the counts before any can change
+        for (int tt = 0; tt < 2; ++tt) {
+          const int j = jl0 + tt;
+          const uint32_t u = okey(__float_as_uint(I[tt]));
+          val[tt] = u;
+          pass[tt] = (j < QT) && (e < nvl[tt]) && (u >= __float_as_uint(sm.thr[j < QT ? j : 0]));
+        }
+      }
+      append<QT>(sm, pass, val, e, jl0, false);
+      __syncthreads();
+      int cnow[QT];
 #pragma unroll
-    for (int j = 0; j < QT; ++j)
-      if (cnow[j] > CAP - kTile) shrink_exact(sm, j, p.k);
+      for (int j = 0; j < QT; ++j) cnow[j] = sm.cnt[j];
+      __syncthreads();  // every thread has read the counts before any can change
+#pragma unroll
+      for (int j = 0; j < QT; ++j)
+        if (cnow[j] > kCap - kTile) wg_shrink_exact(sm, j, p.k);
+    }
+    for (int j = 0; j < QT; ++j) {
+      const int q = q0 + j;
+      if (q >= p.n) break;
+      wg_shrink_exact(sm, j, p.k);
+      const int cnt = sm.cnt[j];
+      wg_bitonic_sort(sm, j, cnt);
+      int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
+      for (int i = tid; i < p.k; i += 256) o[i] = i < cnt ? sm.idx[j][i] : -1;
+      __syncthreads();
+    }
+    return;
   }
 
-  // ---- final exact selection, sort by index, write
-  for (int j = 0; j < QT; ++j) {
+  // ---- phase 3: one wave per token: exact top-k among candidates, ascending output
+  if (wave < QT && q0 + wave < p.n) {
+    const int j = wave;
     const int q = q0 + j;
-    if (q >= p.n) break;
-    shrink_exact(sm, j, p.k);
-    const int cnt = sm.cnt[j];
-    bitonic_sort_idx(sm, j, cnt);
+    const int c = sm.cnt[j];
+    const int kk = nv[j] < p.k ? nv[j] : p.k;
+    uint32_t* keys = sm.key[j];
+    int32_t* ids = sm.idx[j];
+    {  // gather the four wave regions into [0, c) (moving data down only)
+      int off = sm.wcnt[0][j];
+      for (int w = 1; w < 4; ++w) {
+        const int cw = sm.wcnt[w][j];
+        for (int i0 = 0; i0 < cw; i0 += 64) {
+          const int i = i0 + lane;
+          uint32_t kv = 0u;
+          int32_t iv = 0;
+          if (i < cw) { kv = keys[w * kReg + i]; iv = ids[w * kReg + i]; }
+          __builtin_amdgcn_wave_barrier();
+          if (i < cw) { keys[off + i] = kv; ids[off + i] = iv; }
+          __builtin_amdgcn_wave_barrier();
+        }
+        off += cw;
+      }
+    }
+    if (c > kk) {  // select, compacting the kept indices to ids[0..kk)
+      const Sel s = wave_select_topk(sm, j, c, (uint32_t)kk);
+      int outp = 0;
+      for (int base = 0; base < c; base += 64) {
+        const int i = base + lane;
+        bool keep = false;
+        int32_t id = 0;
+        if (i < c) {
+          const uint32_t k = okey(keys[i]);
+          id = ids[i];
+          keep = s.ties ? (k > s.T || (k == s.T && id <= s.id_lim)) : (k >= s.T);
+        }
+        const uint64_t bal = __ballot(keep);
+        const int rank = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        __builtin_amdgcn_wave_barrier();
+        if (keep) ids[outp + rank] = id;
+        outp += __builtin_popcountll(bal);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    // ascending order through bitmap segments, staged in keys[]
+    uint32_t* bm = sm.bits[wave];
+    int outc = 0;
+    for (int seg = 0; seg < nv[j]; seg += kSeg) {
+      for (int wd = lane; wd < kSeg / 32; wd += 64) bm[wd] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      for (int i = lane; i < kk; i += 64) {
+        const int s = ids[i] - seg;
+        if (s >= 0 && s < kSeg) atomicOr(&bm[s >> 5], 1u << (s & 31));
+      }
+      __builtin_amdgcn_wave_barrier();
+      uint32_t wds[16];  // lane owns words [16 lane, 16 lane + 16)
+      int cntl = 0;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) { wds[x] = bm[16 * lane + x]; cntl += __builtin_popcount(wds[x]); }
+      int pre = cntl;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(pre, off);
+        if (lane >= off) pre += o;
+      }
+      const int tot = __shfl(pre, 63);
+      int pos = outc + pre - cntl;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        uint32_t wbits = wds[x];
+        while (wbits) {
+          const int bit = __builtin_ctz(wbits);
+          wbits &= wbits - 1u;
+          keys[pos++] = (uint32_t)(seg + 32 * (16 * lane + x) + bit);
+        }
+      }
+      outc += tot;
+      __builtin_amdgcn_wave_barrier();
+    }
     int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
-    for (int i = tid; i < p.k; i += 256) o[i] = i < cnt ? sm.idx[j][i] : -1;
-    __syncthreads();
+    for (int i = lane; i < p.k; i += 64) o[i] = i < kk ? (int32_t)keys[i] : -1;
   }
 }
 
 size_t index_topk_workspace(int, int, int64_t, int, int, int) { return 0; }
 
-template <int QT, int CAP>
+template <int QT>
 static hipError_t launch_q(const IndexParams& p, hipStream_t stream) {
   const int nblk = (p.n + QT - 1) / QT;
   dim3 grid((unsigned)((int64_t)p.B * nblk)), block(256);
   if (p.fmt == 1)
-    hipLaunchKernelGGL((index_topk_kernel<QT, CAP, 1>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((index_topk_kernel<QT, 1>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((index_topk_kernel<QT, CAP, 0>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((index_topk_kernel<QT, 0>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream) {
   if ((int64_t)p.B * p.n == 0) return hipSuccess;
-  if (p.n == 1) return launch_q<1, 8192>(p, stream);
-  return launch_q<4, 3072>(p, stream);
+  if (p.n == 1) return launch_q<1>(p, stream);
+  return launch_q<4>(p, stream);
 }
 
 }  // namespace csa

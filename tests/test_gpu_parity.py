@@ -124,6 +124,8 @@ def _index_case(orc, rng, B, n, N, H_I, k, q_pos0, fmt, m=4, dup_rows=0, prequan
     (2, 301, 75, 8, 16, 0, "mxfp4", {}),             # fast path + selection, ragged tail
     (1, 37, 20000, 8, 2048, 80000 - 37, "mxfp4", {}),  # several exact shrinks per token
     (1, 50, 3000, 8, 64, 12000, "mxfp4", {"dup_rows": 40}),  # massive exact ties
+    (1, 40, 20000, 8, 2048, 80000 - 40, "mxfp4", {"dup_rows": 3}),  # ties overflow -> exact fallback
+    (1, 41, 9000, 8, 2048, 36000 - 41, "mxfp4", {}),  # sampled threshold, stride 3
     (3, 1, 20000, 8, 2048, 80000, "mxfp4", {}),       # decode path, one token per sequence
     (1, 64, 2000, 8, 100, 8000, "mxfp4", {"prequant": True}),
     (1, 301, 75, 4, 16, 0, "bf16", {}),               # bf16 indexer, 4 heads
@@ -138,14 +140,14 @@ def test_index_topk_matches_oracle(orc, B, n, N, H_I, k, q_pos0, fmt, extra):
 # ----------------------------------------------------------------- attention --
 
 def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True, q_scale=1.0,
-                 efmt="bf16", kv_scale=None):
+                 efmt="bf16", kv_scale=None, sink_shift=0.0):
     rng = np.random.default_rng(seed)
     T = q_pos0 + n
     kv_scale = kv_scale or 1 / np.sqrt(128)
     kv = _bf16(rng, (B, T, 128), kv_scale)
     q = _bf16(rng, (B, n, H, 128), q_scale / np.sqrt(128))
     beta = rng.standard_normal(2 * m if mode == "csa" else m).astype(np.float32)
-    sk = rng.standard_normal(H).astype(np.float32) if sink else None
+    sk = (rng.standard_normal(H) + sink_shift).astype(np.float32) if sink else None
     ents = [oracle_compress_store(orc, kv[b], beta, m, 1 if mode == "csa" else 0, entry_fmt=efmt)
             for b in range(B)]
     N = ents[0]["entries_f64"].shape[0]
@@ -190,6 +192,9 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
     dict(B=1, n=300, H=16, q_pos0=0, m=8, mode="hca"),
     dict(B=1, n=129, H=64, q_pos0=2000, m=128, mode="hca", q_scale=24.0),
     dict(B=2, n=40, H=24, q_pos0=700, m=16, mode="hca", n_win=0, sink=False),
+    # sink far below the scores: weights exceed the sink reference by > 2^64,
+    # which forces the restart with a larger reference
+    dict(B=1, n=20, H=32, q_pos0=300, m=4, mode="csa", k=40, sink_shift=-60.0, q_scale=24.0),
 ])
 def test_attend_matches_oracle(orc, case):
     print("attend case %s" % case, flush=True)
