@@ -38,10 +38,12 @@
 
 namespace csa {
 
-constexpr int kTile = 128;   // entries per iteration (4 waves x 32)
-constexpr int kCap = 4096;   // candidate buffer per token
-constexpr int kSeg = 32768;  // bitmap segment (entries) used to sort the result
-constexpr int kReg = kCap / 4;  // per-wave candidate region of a token's buffer
+constexpr int kWaves = 8;              // waves per work-group (2 per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32 * kWaves;     // entries per iteration
+constexpr int kCap = 4096;             // candidate buffer per token
+constexpr int kSeg = 32768;            // bitmap segment (entries) used to sort the result
+constexpr int kReg = kCap / kWaves;    // per-wave candidate region of a token's buffer
 
 __device__ __forceinline__ uint32_t okey(uint32_t fbits) {
   return (fbits & 0x80000000u) ? ~fbits : (fbits | 0x80000000u);
@@ -65,7 +67,7 @@ struct TopkSmem {
   uint32_t bits[4][kSeg / 32];  // per-wave bitmap for the ascending output
   uint32_t hist[4][256];        // per-wave radix histograms
   int cnt[QT];
-  int wcnt[4][QT];              // candidates per (wave, token) region
+  int wcnt[kWaves][QT];         // candidates per (wave, token) region
   float thr[QT];
   int fallback;
   uint32_t sel[4];
@@ -137,6 +139,7 @@ __device__ uint32_t wave_radix(uint32_t* hist, int n, uint32_t r, KeyFn keyfn, F
       acc = suf - c;
       const uint32_t hh[4] = {h0, h1, h2, h3};
       d = 4 * lane;
+#pragma unroll
       for (int i = 3; i >= 0; --i) {
         if (acc + hh[i] >= r_left) { d = 4 * lane + i; hd = hh[i]; break; }
         acc += hh[i];
@@ -145,6 +148,130 @@ __device__ uint32_t wave_radix(uint32_t* hist, int n, uint32_t r, KeyFn keyfn, F
     d = (uint32_t)__shfl((int)d, L);
     acc = (uint32_t)__shfl((int)acc, L);
     hd = (uint32_t)__shfl((int)hd, L);
+    __builtin_amdgcn_wave_barrier();
+    above += acc;
+    r_left -= acc;
+    prefix |= d << lo;
+    pmask |= dmask << lo;
+    if (hd == r_left || lo == 0) {
+      *above_out = above;
+      *inbin_out = hd;
+      *exact_out = (lo == 0);
+      return prefix;
+    }
+    top = lo - 1;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Register-resident selection: each lane holds up to 64 keys (kr[slot], valid
+// where bit slot of vm is set).  Reductions and scans use DPP row operations,
+// readlane and permlane swaps, never an LDS round trip; the per-digit
+// histogram is the only LDS traffic.
+
+constexpr int kSlots = kCap / 64;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, true);
+}
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t x) {
+  x = max(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = max(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = max(x, dpp<0x124>(x));  // row_ror:4
+  x = max(x, dpp<0x128>(x));  // row_ror:8
+  auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max((uint32_t)p[0], (uint32_t)p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((uint32_t)q[0], (uint32_t)q[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t x) {
+  x = min(x, dpp<0xB1>(x));
+  x = min(x, dpp<0x4E>(x));
+  x = min(x, dpp<0x124>(x));
+  x = min(x, dpp<0x128>(x));
+  auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = min((uint32_t)p[0], (uint32_t)p[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return min((uint32_t)q[0], (uint32_t)q[1]);
+}
+// inclusive prefix sum over lanes 0..63
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+  x += dpp<0x111>(x);  // row_shr:1 (zero from outside the row)
+  x += dpp<0x112>(x);  // row_shr:2
+  x += dpp<0x114>(x);  // row_shr:4
+  x += dpp<0x118>(x);  // row_shr:8
+  const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = lane >> 4;
+  x += (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
+  return x;
+}
+
+// r-th largest (1-based) of the valid register keys; semantics as wave_radix.
+__device__ uint32_t reg_radix(const uint32_t (&kr)[kSlots], uint64_t vm, uint32_t r, uint32_t* hist,
+                              uint32_t* above_out, uint32_t* inbin_out, bool* exact_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+  for (int m = 0; m < kSlots; ++m) {
+    const bool v = (vm >> m) & 1ull;
+    kmax = max(kmax, v ? kr[m] : 0u);
+    kmin = min(kmin, v ? kr[m] : 0xffffffffu);
+  }
+  kmax = wave_max_dpp(kmax);
+  kmin = wave_min_dpp(kmin);
+  if (kmax == kmin) {
+    const uint32_t c = (uint32_t)__builtin_popcountll(vm);
+    *above_out = 0;
+    *inbin_out = wave_prefix_sum(c);
+    *inbin_out = (uint32_t)__builtin_amdgcn_readlane((int)*inbin_out, 63);
+    *exact_out = true;
+    return kmax;
+  }
+  const int hb = 31 - __builtin_clz(kmin ^ kmax);
+  uint32_t pmask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = kmax & pmask;
+  uint32_t r_left = r, above = 0;
+  int top = hb;
+  while (true) {
+    const int lo = top >= 7 ? top - 7 : 0;
+    const uint32_t dmask = (1u << (top - lo + 1)) - 1u;
+    *(u32x4*)(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+      const uint32_t k = kr[m];
+      if (((vm >> m) & 1ull) && (k & pmask) == prefix) atomicAdd(&hist[(k >> lo) & dmask], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane l owns bins 255-4l .. 252-4l (descending), so a prefix sum over
+    // lanes counts the elements in bins >= the lane's lowest bin
+    const u32x4 hv = *(const u32x4*)(hist + 252 - 4 * lane);  // bins 252-4l .. 255-4l
+    const uint32_t c = hv[0] + hv[1] + hv[2] + hv[3];
+    const uint32_t incl = wave_prefix_sum(c);
+    const uint64_t bal = __ballot(incl >= r_left);
+    const int L = __builtin_ctzll(bal);  // first lane whose running count reaches r_left
+    uint32_t acc = incl - c;              // elements in bins above lane L's bins
+    uint32_t d = 0, hd = 0;
+    if (lane == L) {
+      d = 252 - 4 * lane;
+      if (acc + hv[3] >= r_left) { d += 3; hd = hv[3]; }
+      else {
+        acc += hv[3];
+        if (acc + hv[2] >= r_left) { d += 2; hd = hv[2]; }
+        else {
+          acc += hv[2];
+          if (acc + hv[1] >= r_left) { d += 1; hd = hv[1]; }
+          else { acc += hv[1]; hd = hv[0]; }
+        }
+      }
+    }
+    d = (uint32_t)__builtin_amdgcn_readlane((int)d, L);
+    acc = (uint32_t)__builtin_amdgcn_readlane((int)acc, L);
+    hd = (uint32_t)__builtin_amdgcn_readlane((int)hd, L);
     __builtin_amdgcn_wave_barrier();
     above += acc;
     r_left -= acc;
@@ -200,9 +327,9 @@ __device__ uint32_t wg_radix_select(uint32_t* hist, uint32_t* sel, int cnt, uint
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t prefix = 0, pmask = 0, r_left = r, gt_total = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < cnt; i += 256) {
+    for (int i = tid; i < cnt; i += kThreads) {
       if (!filt(i)) continue;
       const uint32_t k = keyfn(i);
       if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
@@ -223,7 +350,8 @@ __device__ uint32_t wg_radix_select(uint32_t* hist, uint32_t* sel, int cnt, uint
         uint32_t acc = suf - c;
         const uint32_t hh[4] = {h0, h1, h2, h3};
         int d = 4 * lane;
-        for (int i = 3; i >= 0; --i) {
+  #pragma unroll
+      for (int i = 3; i >= 0; --i) {
           if (acc + hh[i] >= r_left) { d = 4 * lane + i; break; }
           acc += hh[i];
         }
@@ -264,13 +392,13 @@ __device__ void wg_shrink_exact(TopkSmem<QT>& sm, int j, int kk) {
     tau_inv = wg_radix_select(hist, sm.sel, cnt, need, [&](int i) { return ~(uint32_t)ids[i]; },
                               [&](int i) { return keys[i] == tau; }, &a2, &e2);
   }
-  constexpr int PER = kCap / 256;
+  constexpr int PER = kCap / kThreads;
   uint32_t kv[PER];
   int32_t iv[PER];
   int nk = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    const int i = tid + q * 256;
+    const int i = tid + q * kThreads;
     kv[q] = 0;
     iv[q] = -1;
     if (i < cnt) {
@@ -297,11 +425,11 @@ __device__ void wg_bitonic_sort(TopkSmem<QT>& sm, int j, int cnt) {
   int P = 1;
   while (P < cnt) P <<= 1;
   int32_t* s = sm.idx[j];
-  for (int i = cnt + tid; i < P; i += 256) s[i] = 0x7fffffff;
+  for (int i = cnt + tid; i < P; i += kThreads) s[i] = 0x7fffffff;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (P >> 1); i += 256) {
+      for (int i = tid; i < (P >> 1); i += kThreads) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const bool asc = (lo & size) == 0;
@@ -357,7 +485,7 @@ struct Scorer {
     return t;
   }
 
-  __device__ __forceinline__ void compute(const BTile<FMT>& t, float I[2]) const {
+  __device__ __forceinline__ f32x16 mfma(const BTile<FMT>& t) const {
     f32x16 C;
 #pragma unroll
     for (int i = 0; i < 16; ++i) C[i] = 0.0f;
@@ -371,8 +499,12 @@ struct Scorer {
       for (int ks = 0; ks < 4; ++ks)
         C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_bf[ks], t.v[ks], C, 0, 0, 0);
     }
-    // C rows: heads 0..7 of token jl0 (i = 0..7) and of token jl0 + 1 (i = 8..15).
-    // The chain starts from +0 and can never produce -0.
+    return C;
+  }
+
+  // C rows: heads 0..7 of token jl0 (i = 0..7) and of token jl0 + 1 (i = 8..15).
+  // The chain starts from +0 and can never produce -0.
+  __device__ __forceinline__ void epilogue(const f32x16& C, float I[2]) const {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       float s = 0.0f;
@@ -381,6 +513,8 @@ struct Scorer {
       I[tt] = s;
     }
   }
+
+  __device__ __forceinline__ void compute(const BTile<FMT>& t, float I[2]) const { epilogue(mfma(t), I); }
 
   __device__ __forceinline__ void score(int e, float I[2]) const { compute(load(e), I); }
 };
@@ -433,7 +567,7 @@ __device__ __forceinline__ void append_private(TopkSmem<QT>& sm, const bool pass
 }
 
 template <int QT, int FMT>
-__global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
+__global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
   __shared__ TopkSmem<QT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = (p.n + QT - 1) / QT;
@@ -461,7 +595,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
       const int q = q0 + j;
       if (q < p.n) {
         int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
-        for (int i = tid; i < p.k; i += 256) o[i] = i < nv[j] ? i : -1;
+        for (int i = tid; i < p.k; i += kThreads) o[i] = i < nv[j] ? i : -1;
       }
     }
     return;
@@ -548,7 +682,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
   if (tid == 0) sm.fallback = 0;
   if (sampling) {
     const int max_ns = (maxnv + S - 1) / S;
-    for (int tile = wave; tile * 32 < max_ns; tile += 4) {
+    for (int tile = wave; tile * 32 < max_ns; tile += kWaves) {
       const int i = tile * 32 + (lane & 31);
       const int e = S * i;
       float I[2];
@@ -568,11 +702,18 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
     if (target > kCap - 1024) target = kCap - 1024;
     int r = (int)(((int64_t)target * ns + nv[j] - 1) / nv[j]);
     r = r < 1 ? 1 : (r > ns ? ns : r);
+    uint32_t kr[kSlots];
+    uint64_t vm = 0;
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+      const int i = lane + 64 * m;
+      const bool v = i < ns;
+      kr[m] = okey(sm.key[j][v ? i : 0]);
+      vm |= (uint64_t)v << m;
+    }
     uint32_t above, inbin;
     bool exact;
-    const uint32_t* keys = sm.key[j];
-    const uint32_t T = wave_radix(sm.hist[wave], ns, (uint32_t)r, [&](int i) { return okey(keys[i]); },
-                                  [](int) { return true; }, &above, &inbin, &exact);
+    const uint32_t T = reg_radix(kr, vm, (uint32_t)r, sm.hist[wave], &above, &inbin, &exact);
     if (lane == 0) sm.thr[j] = key_to_float(T);
   }
   __syncthreads();
@@ -585,16 +726,17 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
     thr2[tt] = (j < QT) ? sm.thr[j < QT ? j : 0] : 0.0f;
   }
   {
-    // two tiles in flight: each register set is reloaded right after use
+    // two tiles in flight: both MFMAs are issued before either epilogue, and
+    // each register set is reloaded right after its MFMA
     const int ecol = wave * 32 + (lane & 31);
     int wcnt[2] = {0, 0};
     BTile<FMT> ta = sc.load(ecol), tb = sc.load(ecol + kTile);
-    auto step = [&](const BTile<FMT>& t, int base) {
+    auto finish_tile = [&](const f32x16& C, int base) {
       const int e = base + ecol;
+      float I[2];
+      sc.epilogue(C, I);
       bool pass[2];
       uint32_t val[2];
-      float I[2];
-      sc.compute(t, I);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         pass[tt] = (e < nvl[tt]) && (I[tt] >= thr2[tt]);
@@ -603,10 +745,12 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
       append_private<QT>(sm, pass, val, e, jl0, wcnt);
     };
     for (int base = 0; base < maxnv; base += 2 * kTile) {
-      step(ta, base);
+      const f32x16 Ca = sc.mfma(ta);
+      const f32x16 Cb = sc.mfma(tb);
       ta = sc.load(base + 2 * kTile + ecol);
-      step(tb, base + kTile);
       tb = sc.load(base + 3 * kTile + ecol);
+      finish_tile(Ca, base);
+      finish_tile(Cb, base + kTile);
     }
     if ((lane & 31) == 0) {
 #pragma unroll
@@ -618,7 +762,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
   if (wave < QT && lane == 0) {
     int c = 0;
     bool over = false;
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       c += sm.wcnt[w][wave];
       over |= sm.wcnt[w][wave] > kReg;
     }
@@ -665,7 +809,7 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
       const int cnt = sm.cnt[j];
       wg_bitonic_sort(sm, j, cnt);
       int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
-      for (int i = tid; i < p.k; i += 256) o[i] = i < cnt ? sm.idx[j][i] : -1;
+      for (int i = tid; i < p.k; i += kThreads) o[i] = i < cnt ? sm.idx[j][i] : -1;
       __syncthreads();
     }
     return;
@@ -675,82 +819,104 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
   if (wave < QT && q0 + wave < p.n) {
     const int j = wave;
     const int q = q0 + j;
-    const int c = sm.cnt[j];
     const int kk = nv[j] < p.k ? nv[j] : p.k;
-    uint32_t* keys = sm.key[j];
-    int32_t* ids = sm.idx[j];
-    {  // gather the four wave regions into [0, c) (moving data down only)
-      int off = sm.wcnt[0][j];
-      for (int w = 1; w < 4; ++w) {
-        const int cw = sm.wcnt[w][j];
-        for (int i0 = 0; i0 < cw; i0 += 64) {
-          const int i = i0 + lane;
-          uint32_t kv = 0u;
-          int32_t iv = 0;
-          if (i < cw) { kv = keys[w * kReg + i]; iv = ids[w * kReg + i]; }
-          __builtin_amdgcn_wave_barrier();
-          if (i < cw) { keys[off + i] = kv; ids[off + i] = iv; }
-          __builtin_amdgcn_wave_barrier();
-        }
-        off += cw;
+    // candidates in registers, region-major: slot w*8+m <-> region w, position lane + 64m
+    constexpr int kPer = kReg / 64;
+    uint32_t kr[kSlots];
+    uint64_t vm = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int cw = sm.wcnt[w][j];
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const int pos = lane + 64 * m;
+        const bool v = pos < cw;
+        kr[w * kPer + m] = okey(sm.key[j][w * kReg + (v ? pos : 0)]);
+        vm |= (uint64_t)v << (w * kPer + m);
       }
     }
-    if (c > kk) {  // select, compacting the kept indices to ids[0..kk)
-      const Sel s = wave_select_topk(sm, j, c, (uint32_t)kk);
-      int outp = 0;
-      for (int base = 0; base < c; base += 64) {
-        const int i = base + lane;
-        bool keep = false;
-        int32_t id = 0;
-        if (i < c) {
-          const uint32_t k = okey(keys[i]);
-          id = ids[i];
-          keep = s.ties ? (k > s.T || (k == s.T && id <= s.id_lim)) : (k >= s.T);
-        }
-        const uint64_t bal = __ballot(keep);
-        const int rank = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-        __builtin_amdgcn_wave_barrier();
-        if (keep) ids[outp + rank] = id;
-        outp += __builtin_popcountll(bal);
-        __builtin_amdgcn_wave_barrier();
+    const int c = sm.cnt[j];
+    uint32_t T = 0u;
+    int ties = 0;
+    int32_t id_lim = 0;
+    if (c > kk) {
+      uint32_t above, inbin;
+      bool exact;
+      T = reg_radix(kr, vm, (uint32_t)kk, sm.hist[wave], &above, &inbin, &exact);
+      if (exact && (uint32_t)kk - above < inbin) {
+        // ties at T: keep the (kk - above) smallest entry indices among them
+        uint32_t a2, b2;
+        bool e2;
+        const uint32_t* keys = sm.key[j];
+        const int32_t* ids = sm.idx[j];
+        auto slot_i = [&](int i) { return (i / kReg) * kReg + (i % kReg); };
+        const uint32_t tinv = wave_radix(
+            sm.hist[wave], kCap, (uint32_t)kk - above,
+            [&](int i) { return ~(uint32_t)ids[slot_i(i)]; },
+            [&](int i) { return (i % kReg) < sm.wcnt[i / kReg][j] && okey(keys[slot_i(i)]) == T; },
+            &a2, &b2, &e2);
+        ties = 1;
+        id_lim = (int32_t)~tinv;
       }
     }
-    // ascending order through bitmap segments, staged in keys[]
+    // keep mask over the register slots
+    uint64_t keep = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const int sl = w * kPer + m;
+        if (!((vm >> sl) & 1ull)) continue;
+        bool kp = kr[sl] >= T;
+        if (ties && kr[sl] == T) kp = sm.idx[j][w * kReg + lane + 64 * m] <= id_lim;
+        keep |= (uint64_t)kp << sl;
+      }
+    // ascending output through bitmap segments, staged in key[j][0..kk)
     uint32_t* bm = sm.bits[wave];
+    uint32_t* stage = sm.key[j];
     int outc = 0;
     for (int seg = 0; seg < nv[j]; seg += kSeg) {
-      for (int wd = lane; wd < kSeg / 32; wd += 64) bm[wd] = 0u;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) *(u32x4*)(bm + 16 * lane + 4 * x) = u32x4{0u, 0u, 0u, 0u};
       __builtin_amdgcn_wave_barrier();
-      for (int i = lane; i < kk; i += 64) {
-        const int s = ids[i] - seg;
-        if (s >= 0 && s < kSeg) atomicOr(&bm[s >> 5], 1u << (s & 31));
-      }
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+          const int sl = w * kPer + m;
+          if ((keep >> sl) & 1ull) {
+            const int s = sm.idx[j][w * kReg + lane + 64 * m] - seg;
+            if (s >= 0 && s < kSeg) atomicOr(&bm[s >> 5], 1u << (s & 31));
+          }
+        }
       __builtin_amdgcn_wave_barrier();
       uint32_t wds[16];  // lane owns words [16 lane, 16 lane + 16)
-      int cntl = 0;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) { wds[x] = bm[16 * lane + x]; cntl += __builtin_popcount(wds[x]); }
-      int pre = cntl;
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(pre, off);
-        if (lane >= off) pre += o;
+      for (int x = 0; x < 4; ++x) {
+        const u32x4 v = *(const u32x4*)(bm + 16 * lane + 4 * x);
+        wds[4 * x] = v[0]; wds[4 * x + 1] = v[1]; wds[4 * x + 2] = v[2]; wds[4 * x + 3] = v[3];
       }
-      const int tot = __shfl(pre, 63);
-      int pos = outc + pre - cntl;
+      uint32_t cntl = 0;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) cntl += __builtin_popcount(wds[x]);
+      const uint32_t incl = wave_prefix_sum(cntl);
+      const int tot = __builtin_amdgcn_readlane((int)incl, 63);
+      int pos = outc + (int)(incl - cntl);
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         uint32_t wbits = wds[x];
         while (wbits) {
           const int bit = __builtin_ctz(wbits);
           wbits &= wbits - 1u;
-          keys[pos++] = (uint32_t)(seg + 32 * (16 * lane + x) + bit);
+          stage[pos++] = (uint32_t)(seg + 32 * (16 * lane + x) + bit);
         }
       }
       outc += tot;
       __builtin_amdgcn_wave_barrier();
     }
     int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
-    for (int i = lane; i < p.k; i += 64) o[i] = i < kk ? (int32_t)keys[i] : -1;
+    for (int i = lane; i < p.k; i += 64) o[i] = i < kk ? (int32_t)stage[i] : -1;
   }
 }
 
@@ -759,7 +925,7 @@ size_t index_topk_workspace(int, int, int64_t, int, int, int) { return 0; }
 template <int QT>
 static hipError_t launch_q(const IndexParams& p, hipStream_t stream) {
   const int nblk = (p.n + QT - 1) / QT;
-  dim3 grid((unsigned)((int64_t)p.B * nblk)), block(256);
+  dim3 grid((unsigned)((int64_t)p.B * nblk)), block(kThreads);
   if (p.fmt == 1)
     hipLaunchKernelGGL((index_topk_kernel<QT, 1>), grid, block, 0, stream, p);
   else
