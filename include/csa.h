@@ -118,8 +118,9 @@ int csa_compress(const void* kv, const void* ik, const float* z, const float* be
  * for every visible entry s (p_s <= t, s < N): each dot product in fp32
  * (exact for MXFP4 operands), the head sum as an fp32 fma chain in
  * ascending h starting from +0.  It keeps the min(k, n_vis) largest scores,
- * ties going to the lower entry index, and writes their indices in ascending
- * order, padded with -1 up to k.
+ * ties going to the lower entry index, and writes their indices followed by
+ * -1 padding up to k.  The order of the indices within a row is unspecified
+ * (it is deterministic for given inputs); attention does not depend on it.
  *
  *  qidx        fmt BF16: [B, n, H_I, 64] bf16.  fmt MXFP4 with
  *              qidx_scale == NULL: [B, n, H_I, 64] bf16, quantised in-kernel

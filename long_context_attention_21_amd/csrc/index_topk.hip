@@ -8,30 +8,35 @@
 // at every entry, so the scorer must be light).  Score (DSA form):
 //     I[t,s] = sum_h w[t,h] * relu(<qI[t,h], kI[s]>),   h ascending, fp32 fma chain.
 // Selection: the min(k, n_vis) largest scores, ties to the lower entry index,
-// written in ascending index order and padded with -1.
+// written followed by -1 padding (the order within a row is unspecified).
 //
 // Design for CDNA4
-//  * Scores: one v_mfma_scale_f32_32x32x64_f8f6f4 (MXFP4) or four
-//    v_mfma_f32_32x32x16_bf16 per 32 entries.  The 32 A rows are 4 query
-//    tokens x 8 heads, placed so each lane's 16 accumulator rows are all 8
-//    heads of two tokens: the head sum is an in-lane fma chain in ascending
-//    head order (MXFP4 dot products are exact, so MXFP4 scores are
-//    bit-identical to a sequential evaluation).
-//  * Selection in one scoring pass, without barriers:
-//      1. a strided sample of the visible entries (at most 4096 per token) is
-//         scored; each token's threshold is the sample quantile that leaves
-//         about k + 850 entries above it;
+//  * A work-group of 8 waves serves QT = 4 query tokens (1 for single-token
+//    decode).  Scores: one v_mfma_scale_f32_32x32x64_f8f6f4 (MXFP4) or four
+//    v_mfma_f32_32x32x16_bf16 per 32 entries.  The 32 A rows are 4 tokens x 8
+//    heads, placed so each lane's 16 accumulator rows are all 8 heads of two
+//    tokens: the head sum is an in-lane fma chain in ascending head order
+//    (MXFP4 dot products are exact, so MXFP4 scores are bit-identical to a
+//    sequential evaluation).  Entry rows come through range-checked buffer
+//    loads, four tiles in flight per wave.
+//  * Selection in one scoring pass:
+//      1. a strided sample of the visible entries (sized so that about
+//         kMinAbove samples lie above the cut) is scored; each token's
+//         threshold is the sample quantile that leaves about k + 850 entries
+//         above it;
 //      2. every entry is scored once; scores >= threshold are appended to the
-//         wave's private region of the token's LDS candidate buffer (wave
-//         ballot + register counters: no atomics, no cross-lane round trip);
-//      3. one wave per token selects the exact top-k among the candidates
-//         (radix selection on (score desc, index asc) with adaptive digit
-//         positions and early exit), then emits the indices in ascending
-//         order through an LDS bitmap.
+//         wave's private region of the token's LDS candidate buffer (ballot +
+//         mbcnt, counts in registers: no atomics);
+//      3. the waves serving a token (its "group") load the candidates into
+//         registers and find the exact k-th largest (score desc, index asc)
+//         with a radix selection over a histogram they share; after the
+//         first digit the surviving keys move to short LDS lists.  The kept
+//         indices are then written region by region.
 //    Any threshold with at least k candidates above it keeps every top-k
-//    member, so the result is exact.  If a buffer overflows or ends up with
-//    fewer than k candidates, the work-group reruns its tokens with the exact
-//    streaming method (buffers shrunk to exactly k whenever they fill).
+//    member, so the result is exact.  If a region overflows or a token ends
+//    up with fewer than k candidates, the work-group reruns its tokens with
+//    the exact streaming method (buffers shrunk to exactly k whenever they
+//    fill).
 //  * Tokens whose visible entries all fit in k skip scoring.
 #include "device.h"
 #include "kernels.h"
@@ -40,10 +45,12 @@ namespace csa {
 
 constexpr int kWaves = 8;              // waves per work-group (2 per SIMD)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 32 * kWaves;     // entries per iteration
+constexpr int kTile = 32 * kWaves;     // entries per round of the work-group
 constexpr int kCap = 4096;             // candidate buffer per token
-constexpr int kSeg = 32768;            // bitmap segment (entries) used to sort the result
 constexpr int kReg = kCap / kWaves;    // per-wave candidate region of a token's buffer
+constexpr int kDepth = 4;              // score tiles in flight per wave
+constexpr int kMinAbove = 256;         // sampled entries expected above the threshold
+constexpr int kList = 512;             // per-member key list after the first radix digit
 
 __device__ __forceinline__ uint32_t okey(uint32_t fbits) {
   return (fbits & 0x80000000u) ? ~fbits : (fbits | 0x80000000u);
@@ -60,116 +67,22 @@ __device__ __forceinline__ void row_to_token_head(int r, int& j, int& h) {
   h = ic & 7;
 }
 
+// Token j of a work-group is served by the "group" of waves w with
+// w % QT == j (kWaves / QT of them); group member h = w / QT.
 template <int QT>
 struct TopkSmem {
-  uint32_t key[QT][kCap];       // fp32 score bits of candidates / samples
-  int32_t idx[QT][kCap];        // entry indices of candidates
-  uint32_t bits[4][kSeg / 32];  // per-wave bitmap for the ascending output
-  uint32_t hist[4][256];        // per-wave radix histograms
-  int cnt[QT];
-  int wcnt[kWaves][QT];         // candidates per (wave, token) region
+  uint2 cand[QT][kCap];       // {fp32 score bits, entry}; samples in phase 1; output bitmap at the end
+  uint32_t hist[2][QT][256];  // double-buffered radix histograms, one per token group
+  uint32_t xchg[kWaves][2];   // per-wave values read by the other group members
+  int kept[QT][kWaves];       // kept candidates per (token, region)
+  int gdone[2][QT];           // radix selection finished, per token group (double-buffered)
+  int wcnt[kWaves][QT];       // candidates per (wave, token) region
   float thr[QT];
+  int cnt[QT];
   int fallback;
+  int ties;
   uint32_t sel[4];
 };
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-  for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
-  return x;
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-  for (int off = 32; off >= 1; off >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, off));
-  return x;
-}
-
-// ----------------------------------------------------------------------------
-// Wave-level radix selection of the r-th largest (1-based) keyfn(i) over the
-// i < n passing filt(i).  Digits of up to 8 bits start just below the common
-// prefix of all keys.  Returns the threshold T with *above = count of keys
-// above T's bin.  Stops early when the threshold bin holds exactly the
-// remaining rank (then keep(key) = key >= T selects exactly r); otherwise
-// resolves all 32 bits (*exact = true, T is the r-th key, *inbin its count).
-template <class KeyFn, class FiltFn>
-__device__ uint32_t wave_radix(uint32_t* hist, int n, uint32_t r, KeyFn keyfn, FiltFn filt,
-                               uint32_t* above_out, uint32_t* inbin_out, bool* exact_out) {
-  const int lane = threadIdx.x & 63;
-  uint32_t kmax = 0u, kmin = 0xffffffffu;
-  for (int i = lane; i < n; i += 64)
-    if (filt(i)) { uint32_t k = keyfn(i); kmax = max(kmax, k); kmin = min(kmin, k); }
-  kmax = wave_max_u32(kmax);
-  kmin = wave_min_u32(kmin);
-  if (kmax == kmin) {  // every passing key is equal
-    uint32_t c = 0;
-    for (int i = lane; i < n; i += 64) c += filt(i) ? 1u : 0u;
-    for (int off = 32; off >= 1; off >>= 1) c += (uint32_t)__shfl_xor((int)c, off);
-    *above_out = 0;
-    *inbin_out = c;
-    *exact_out = true;
-    return kmax;
-  }
-  const int hb = 31 - __builtin_clz(kmin ^ kmax);  // highest differing bit
-  uint32_t pmask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
-  uint32_t prefix = kmax & pmask;
-  uint32_t r_left = r, above = 0;
-  int top = hb;  // current digit covers bits [lo, top]
-  while (true) {
-    const int lo = top >= 7 ? top - 7 : 0;
-    const uint32_t dmask = (1u << (top - lo + 1)) - 1u;
-    for (int bb = lane; bb < 256; bb += 64) hist[bb] = 0u;
-    __builtin_amdgcn_wave_barrier();
-    for (int i = lane; i < n; i += 64) {
-      if (!filt(i)) continue;
-      const uint32_t k = keyfn(i);
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> lo) & dmask], 1u);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // lane owns bins 4l..4l+3; suffix sums over lanes
-    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
-                   h3 = hist[4 * lane + 3];
-    const uint32_t c = h0 + h1 + h2 + h3;
-    uint32_t suf = c;
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = (uint32_t)__shfl_down((int)suf, off);
-      if (lane + off < 64) suf += o;
-    }
-    const uint64_t bal = __ballot(suf >= r_left);
-    const int L = 63 - __builtin_clzll(bal);
-    uint32_t d = 0, acc = 0, hd = 0;
-    if (lane == L) {
-      acc = suf - c;
-      const uint32_t hh[4] = {h0, h1, h2, h3};
-      d = 4 * lane;
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        if (acc + hh[i] >= r_left) { d = 4 * lane + i; hd = hh[i]; break; }
-        acc += hh[i];
-      }
-    }
-    d = (uint32_t)__shfl((int)d, L);
-    acc = (uint32_t)__shfl((int)acc, L);
-    hd = (uint32_t)__shfl((int)hd, L);
-    __builtin_amdgcn_wave_barrier();
-    above += acc;
-    r_left -= acc;
-    prefix |= d << lo;
-    pmask |= dmask << lo;
-    if (hd == r_left || lo == 0) {
-      *above_out = above;
-      *inbin_out = hd;
-      *exact_out = (lo == 0);
-      return prefix;
-    }
-    top = lo - 1;
-  }
-}
-
-// ----------------------------------------------------------------------------
-// Register-resident selection: each lane holds up to 64 keys (kr[slot], valid
-// where bit slot of vm is set).  Reductions and scans use DPP row operations,
-// readlane and permlane swaps, never an LDS round trip; the per-digit
-// histogram is the only LDS traffic.
-
-constexpr int kSlots = kCap / 64;
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t x) {
@@ -210,111 +123,172 @@ __device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
   return x;
 }
 
-// r-th largest (1-based) of the valid register keys; semantics as wave_radix.
-__device__ uint32_t reg_radix(const uint32_t (&kr)[kSlots], uint64_t vm, uint32_t r, uint32_t* hist,
-                              uint32_t* above_out, uint32_t* inbin_out, bool* exact_out) {
-  const int lane = threadIdx.x & 63;
-  uint32_t kmax = 0u, kmin = 0xffffffffu;
+// ----------------------------------------------------------------------------
+// Radix selection of the r-th largest (1-based) key held in registers by a
+// token's group (kr[m] of every lane of every member; slot m may hold keys
+// only where bit m of smask is set, uniformly).  Zero keys mark empty lanes:
+// they sort below every real key (order keys of finite floats and inverted
+// entry indices are never 0), so they cannot change the result while r does
+// not exceed the number of real keys (n_valid).  Digits of up to 8 bits are
+// taken from key - (kmin - 1) (kmin, kmax: extremes of the real keys),
+// starting at its top bit over the real range; a histogram shared by the group is filled with
+// LDS atomics and scanned by every member alike, so all members reach the
+// same decision.  Stops when the chosen bin holds exactly the remaining rank
+// (then keep(key) = key >= T selects exactly r) or at most slack keys (then
+// it selects r .. r + slack - 1), otherwise resolves all bits (exact: T is
+// the r-th key, inbin the number equal to it, above the number greater).  Every wave of the work-group must call it the
+// same number of times (it synchronises the work-group); groups with nothing
+// to select pass active = false.
+struct RadixOut {
+  uint32_t T, above, inbin;
+  int exact;
+};
+
+template <int QT, int NS>
+__device__ __forceinline__ RadixOut group_radix(TopkSmem<QT>& sm, const uint32_t (&kr)[NS], uint32_t smask, uint32_t r,
+                                                uint32_t n_valid, bool active, uint32_t slack = 0u) {
+  constexpr int G = kWaves / QT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = wave % QT, h = wave / QT;
+  uint32_t kmax = 0u, kmin1 = 0xffffffffu;  // kmin1 = min(key - 1): empty (0) keys wrap to the top
 #pragma unroll
-  for (int m = 0; m < kSlots; ++m) {
-    const bool v = (vm >> m) & 1ull;
-    kmax = max(kmax, v ? kr[m] : 0u);
-    kmin = min(kmin, v ? kr[m] : 0xffffffffu);
+  for (int m = 0; m < NS; ++m) {
+    kmax = max(kmax, kr[m]);
+    kmin1 = min(kmin1, kr[m] - 1u);
   }
   kmax = wave_max_dpp(kmax);
-  kmin = wave_min_dpp(kmin);
-  if (kmax == kmin) {
-    const uint32_t c = (uint32_t)__builtin_popcountll(vm);
-    *above_out = 0;
-    *inbin_out = wave_prefix_sum(c);
-    *inbin_out = (uint32_t)__builtin_amdgcn_readlane((int)*inbin_out, 63);
-    *exact_out = true;
-    return kmax;
+  kmin1 = wave_min_dpp(kmin1);
+  if (lane == 0) { sm.xchg[wave][0] = kmax; sm.xchg[wave][1] = kmin1; }
+  if (lane < 64 / G) *(u32x4*)&sm.hist[0][j][h * (256 / G) + 4 * lane] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    kmax = max(kmax, sm.xchg[j + QT * g][0]);
+    kmin1 = min(kmin1, sm.xchg[j + QT * g][1]);
   }
-  const int hb = 31 - __builtin_clz(kmin ^ kmax);
-  uint32_t pmask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
-  uint32_t prefix = kmax & pmask;
-  uint32_t r_left = r, above = 0;
-  int top = hb;
-  while (true) {
+  const uint32_t kmin = kmin1 + 1u;
+  RadixOut o{0u, 0u, 0u, 0};
+  bool done = !active;
+  if (!done && kmax == kmin) {  // every real key is equal
+    o = RadixOut{kmax, 0u, n_valid, 1};
+    done = true;
+  }
+  // digits of v(key) = max(key, base) - base with base = kmin - 1: real keys
+  // map to 1 .. kmax - base and empty slots to 0, still below every real
+  // key; the first digit splits the real range into up to 256 equal bins
+  const uint32_t base = kmin - 1u;
+  int top = 0;
+  uint32_t prefix = 0u, r_left = r, above = 0u;
+  if (!done) top = 31 - __builtin_clz(kmax - base);
+  // after the first digit the keys of the chosen bin are usually few: each
+  // member then copies its share into a list in the token's (free) buffer,
+  // and the remaining digits scan the lists instead of every register slot
+  uint32_t* list = (uint32_t*)&sm.cand[j][0] + h * kList;
+  int lcnt = 0;
+  bool listmode = false;
+#pragma unroll 1
+  for (int it = 0; it < 4; ++it) {  // at most 4 digits of 8 bits
+    uint32_t* hc = sm.hist[it & 1][j];
     const int lo = top >= 7 ? top - 7 : 0;
     const uint32_t dmask = (1u << (top - lo + 1)) - 1u;
-    *(u32x4*)(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
-    __builtin_amdgcn_wave_barrier();
+    const uint32_t pb = prefix >> lo;
+    if (!done) {
+      if (!listmode) {
 #pragma unroll
-    for (int m = 0; m < kSlots; ++m) {
-      const uint32_t k = kr[m];
-      if (((vm >> m) & 1ull) && (k & pmask) == prefix) atomicAdd(&hist[(k >> lo) & dmask], 1u);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // lane l owns bins 255-4l .. 252-4l (descending), so a prefix sum over
-    // lanes counts the elements in bins >= the lane's lowest bin
-    const u32x4 hv = *(const u32x4*)(hist + 252 - 4 * lane);  // bins 252-4l .. 255-4l
-    const uint32_t c = hv[0] + hv[1] + hv[2] + hv[3];
-    const uint32_t incl = wave_prefix_sum(c);
-    const uint64_t bal = __ballot(incl >= r_left);
-    const int L = __builtin_ctzll(bal);  // first lane whose running count reaches r_left
-    uint32_t acc = incl - c;              // elements in bins above lane L's bins
-    uint32_t d = 0, hd = 0;
-    if (lane == L) {
-      d = 252 - 4 * lane;
-      if (acc + hv[3] >= r_left) { d += 3; hd = hv[3]; }
-      else {
-        acc += hv[3];
-        if (acc + hv[2] >= r_left) { d += 2; hd = hv[2]; }
-        else {
-          acc += hv[2];
-          if (acc + hv[1] >= r_left) { d += 1; hd = hv[1]; }
-          else { acc += hv[1]; hd = hv[0]; }
+        for (int m = 0; m < NS; ++m) {
+          if ((smask >> m) & 1u) {
+            const uint32_t d = ((max(kr[m], base) - base) >> lo) - pb;  // digit, if the key matches the prefix
+            if (d <= dmask) atomicAdd(&hc[d], 1u);
+          }
+        }
+      } else {
+        for (int s0 = 0; s0 < lcnt; s0 += 64) {
+          const int i = s0 + lane;
+          if (i < lcnt) {
+            const uint32_t d = ((max(list[i], base) - base) >> lo) - pb;
+            if (d <= dmask) atomicAdd(&hc[d], 1u);
+          }
         }
       }
     }
-    d = (uint32_t)__builtin_amdgcn_readlane((int)d, L);
-    acc = (uint32_t)__builtin_amdgcn_readlane((int)acc, L);
-    hd = (uint32_t)__builtin_amdgcn_readlane((int)hd, L);
-    __builtin_amdgcn_wave_barrier();
-    above += acc;
-    r_left -= acc;
-    prefix |= d << lo;
-    pmask |= dmask << lo;
-    if (hd == r_left || lo == 0) {
-      *above_out = above;
-      *inbin_out = hd;
-      *exact_out = (lo == 0);
-      return prefix;
+    __syncthreads();
+    if (!done) {
+      // lane l owns bins 252-4l .. 255-4l, so a prefix sum over lanes counts
+      // the keys in bins >= the lane's lowest bin
+      const u32x4 hv = *(const u32x4*)(hc + 252 - 4 * lane);
+      const uint32_t c = hv[0] + hv[1] + hv[2] + hv[3];
+      const uint32_t incl = wave_prefix_sum(c);
+      const int L = __builtin_ctzll(__ballot(incl >= r_left));
+      uint32_t acc = incl - c, d = 0u, hd = 0u;
+      if (lane == L) {
+        d = 252 - 4 * lane;
+        if (acc + hv[3] >= r_left) { d += 3; hd = hv[3]; }
+        else {
+          acc += hv[3];
+          if (acc + hv[2] >= r_left) { d += 2; hd = hv[2]; }
+          else {
+            acc += hv[2];
+            if (acc + hv[1] >= r_left) { d += 1; hd = hv[1]; }
+            else { acc += hv[1]; hd = hv[0]; }
+          }
+        }
+      }
+      d = (uint32_t)__builtin_amdgcn_readlane((int)d, L);
+      acc = (uint32_t)__builtin_amdgcn_readlane((int)acc, L);
+      hd = (uint32_t)__builtin_amdgcn_readlane((int)hd, L);
+      above += acc;
+      r_left -= acc;
+      prefix |= d << lo;
+      if (hd == r_left || lo == 0 || hd <= slack) {
+        // lo == 0: exact; otherwise the bin's lower bound (keep = key >= T
+        // then selects r .. r + hd - 1 keys, exactly r when hd == r_left)
+        o = RadixOut{prefix + base, above, hd, lo == 0 ? 1 : 0};
+        done = true;
+      } else {
+        top = lo - 1;
+        if (!listmode && hd <= (uint32_t)kList) {
+          // keys of the chosen bin -> this member's list (hd bounds every member's share)
+#pragma unroll
+          for (int m = 0; m < NS; ++m) {
+            if ((smask >> m) & 1u) {
+              const bool in = ((max(kr[m], base) - base) >> lo) - pb == d;
+              const uint64_t bal = __ballot(in);
+              const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+              if (in) list[lcnt + rank] = kr[m];
+              lcnt += __builtin_popcountll(bal);
+            }
+          }
+          listmode = true;
+        } else if (listmode) {
+          // keep only the chosen bin, in place (writes never pass the chunk being read)
+          int nc = 0;
+          for (int s0 = 0; s0 < lcnt; s0 += 64) {
+            const int i = s0 + lane;
+            const uint32_t key = i < lcnt ? list[i] : 0u;
+            const bool in = i < lcnt && ((max(key, base) - base) >> lo) - pb == d;
+            const uint64_t bal = __ballot(in);
+            const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (in) list[nc + rank] = key;
+            nc += __builtin_popcountll(bal);
+          }
+          lcnt = nc;
+        }
+      }
     }
-    top = lo - 1;
+    // the other buffer was last read before the previous barrier
+    if (lane < 64 / G) *(u32x4*)&sm.hist[(it + 1) & 1][j][h * (256 / G) + 4 * lane] = u32x4{0u, 0u, 0u, 0u};
+    if (h == 0 && lane == 0) sm.gdone[it & 1][j] = done ? 1 : 0;
+    __syncthreads();
+    // leave together once every group is done (the flags of this iteration
+    // are not rewritten before the next barrier)
+    bool all = true;
+#pragma unroll
+    for (int g = 0; g < QT; ++g) all &= sm.gdone[it & 1][g] != 0;
+    if (all) break;
   }
-}
-
-// keep(i) = okey > T || (okey == T && (!ties || id <= id_lim)); with !ties,
-// keep(i) = okey >= T.
-struct Sel {
-  uint32_t T;
-  int ties;
-  int32_t id_lim;
-};
-
-template <int QT>
-__device__ Sel wave_select_topk(TopkSmem<QT>& sm, int j, int n, uint32_t r) {
-  const int w = threadIdx.x >> 6;
-  const uint32_t* keys = sm.key[j];
-  const int32_t* ids = sm.idx[j];
-  uint32_t above, inbin;
-  bool exact;
-  const uint32_t T = wave_radix(sm.hist[w], n, r, [&](int i) { return okey(keys[i]); },
-                                [](int) { return true; }, &above, &inbin, &exact);
-  Sel s{T, 0, 0};
-  if (!exact) return s;
-  const uint32_t need = r - above;
-  if (need >= inbin) return s;  // every tie is kept
-  uint32_t a2, b2;
-  bool e2;
-  const uint32_t tinv = wave_radix(sm.hist[w], n, need, [&](int i) { return ~(uint32_t)ids[i]; },
-                                   [&](int i) { return okey(keys[i]) == T; }, &a2, &b2, &e2);
-  s.ties = 1;
-  s.id_lim = (int32_t)~tinv;
-  return s;
+  return o;
 }
 
 // ----------------------------------------------------------------------------
@@ -379,18 +353,17 @@ __device__ void wg_shrink_exact(TopkSmem<QT>& sm, int j, int kk) {
   const int cnt = sm.cnt[j];
   if (cnt <= kk) return;
   uint32_t above, equal;
-  uint32_t* keys = sm.key[j];
-  int32_t* ids = sm.idx[j];
-  uint32_t* hist = &sm.hist[0][0];
-  const uint32_t tau = wg_radix_select(hist, sm.sel, cnt, (uint32_t)kk, [&](int i) { return keys[i]; },
+  uint2* cd = sm.cand[j];
+  uint32_t* hist = &sm.hist[0][0][0];
+  const uint32_t tau = wg_radix_select(hist, sm.sel, cnt, (uint32_t)kk, [&](int i) { return cd[i].x; },
                                        [](int) { return true; }, &above, &equal);
   const uint32_t need = (uint32_t)kk - above;
   uint32_t tau_inv = 0;
   const bool cut_ties = need < equal;
   if (cut_ties) {
     uint32_t a2, e2;
-    tau_inv = wg_radix_select(hist, sm.sel, cnt, need, [&](int i) { return ~(uint32_t)ids[i]; },
-                              [&](int i) { return keys[i] == tau; }, &a2, &e2);
+    tau_inv = wg_radix_select(hist, sm.sel, cnt, need, [&](int i) { return ~cd[i].y; },
+                              [&](int i) { return cd[i].x == tau; }, &a2, &e2);
   }
   constexpr int PER = kCap / kThreads;
   uint32_t kv[PER];
@@ -402,8 +375,8 @@ __device__ void wg_shrink_exact(TopkSmem<QT>& sm, int j, int kk) {
     kv[q] = 0;
     iv[q] = -1;
     if (i < cnt) {
-      const uint32_t k = keys[i];
-      const int32_t id = ids[i];
+      const uint32_t k = cd[i].x;
+      const int32_t id = (int32_t)cd[i].y;
       const bool keep = (k > tau) || (k == tau && (!cut_ties || ~(uint32_t)id >= tau_inv));
       if (keep) { kv[q] = k; iv[q] = id; ++nk; }
     }
@@ -414,7 +387,7 @@ __device__ void wg_shrink_exact(TopkSmem<QT>& sm, int j, int kk) {
   int base = atomicAdd(&sm.cnt[j], nk);
 #pragma unroll
   for (int q = 0; q < PER; ++q)
-    if (iv[q] >= 0) { keys[base] = kv[q]; ids[base] = iv[q]; ++base; }
+    if (iv[q] >= 0) { cd[base] = make_uint2(kv[q], (uint32_t)iv[q]); ++base; }
   if (tid == 0) sm.thr[j] = __uint_as_float(tau + 1u);  // order key, strictly above the k-th
   __syncthreads();
 }
@@ -424,8 +397,8 @@ __device__ void wg_bitonic_sort(TopkSmem<QT>& sm, int j, int cnt) {
   const int tid = threadIdx.x;
   int P = 1;
   while (P < cnt) P <<= 1;
-  int32_t* s = sm.idx[j];
-  for (int i = cnt + tid; i < P; i += kThreads) s[i] = 0x7fffffff;
+  uint2* s = sm.cand[j];  // sorts the entry field
+  for (int i = cnt + tid; i < P; i += kThreads) s[i].y = 0x7fffffffu;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -433,8 +406,8 @@ __device__ void wg_bitonic_sort(TopkSmem<QT>& sm, int j, int cnt) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const bool asc = (lo & size) == 0;
-        const int32_t a = s[lo], bb = s[hi];
-        if ((a > bb) == asc) { s[lo] = bb; s[hi] = a; }
+        const int32_t a = (int32_t)s[lo].y, bb = (int32_t)s[hi].y;
+        if ((a > bb) == asc) { s[lo].y = (uint32_t)bb; s[hi].y = (uint32_t)a; }
       }
       __syncthreads();
     }
@@ -463,24 +436,22 @@ struct Scorer {
   int a_scale;
   bf16x8 A_bf[4];
   float wv[2][8];
-  const uint8_t* kc;
-  const uint16_t* kb;
-  const uint8_t* ksc;
-  int N;
+  __amdgpu_buffer_rsrc_t rk;  // this batch's entry keys (MXFP4 codes or bf16 rows)
+  __amdgpu_buffer_rsrc_t rs;  // this batch's MXFP4 block scales
+  int voff_k, voff_s;         // the lane's byte offsets inside an entry's row
 
-  // B operand of entry column e (lane % 32).  The address is clamped to the
-  // last entry, so the loads are unconditional; columns e >= N hold garbage
-  // that callers never select (every token's n_vis <= N).
+  // B operand of entry column e (lane % 32).  Buffer loads are range-checked
+  // by the hardware: entries at or past the end of the array read as zero, so
+  // the loads need no clamp or branch (callers never select e >= n_vis).
   __device__ __forceinline__ BTile<FMT> load(int e) const {
-    const int lane = threadIdx.x & 63;
-    const int64_t ec = e < N ? e : N - 1;
     BTile<FMT> t;
     if constexpr (FMT == 1) {
-      t.cw = *(const u32x4*)(kc + ec * 32 + (lane >> 5) * 16);
-      t.sc = ksc[ec * 2 + (lane >> 5)];
+      t.cw = __builtin_amdgcn_raw_buffer_load_b128(rk, e * 32 + voff_k, 0, 0);
+      t.sc = __builtin_amdgcn_raw_buffer_load_b8(rs, e * 2 + voff_s, 0, 0);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) t.v[ks] = *(const bf16x8*)(kb + ec * 64 + ks * 16 + (lane >> 5) * 8);
+      for (int ks = 0; ks < 4; ++ks)
+        t.v[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, e * 128 + ks * 32 + voff_k, 0, 0));
     }
     return t;
   }
@@ -519,10 +490,10 @@ struct Scorer {
   __device__ __forceinline__ void score(int e, float I[2]) const { compute(load(e), I); }
 };
 
-// Appends the passing lanes of each half-wave to their token's buffer.
+// Appends the passing lanes of each half-wave to their token's buffer
+// (exact fallback: shared count, LDS atomic).
 template <int QT>
-__device__ __forceinline__ void append(TopkSmem<QT>& sm, const bool pass[2], const uint32_t val[2],
-                                       int e, int jl0, bool clamp) {
+__device__ __forceinline__ void append(TopkSmem<QT>& sm, const bool pass[2], const uint32_t val[2], int e, int jl0) {
   const int lane = threadIdx.x & 63;
   const int leader = (lane < 32) ? 0 : 32;
   const uint64_t halfmask = (lane < 32) ? 0x00000000ffffffffull : 0xffffffff00000000ull;
@@ -536,34 +507,25 @@ __device__ __forceinline__ void append(TopkSmem<QT>& sm, const bool pass[2], con
     if (lane == leader && pc > 0) basepos = atomicAdd(&sm.cnt[j < QT ? j : 0], pc);
     basepos = __shfl(basepos, leader);
     const int pos = basepos + rank;
-    if (pass[tt] && (!clamp || pos < kCap)) {
-      sm.key[j][pos] = val[tt];
-      sm.idx[j][pos] = e;
-    }
+    if (pass[tt]) sm.cand[j][pos] = make_uint2(val[tt], (uint32_t)e);
   }
 }
 
-// Appends the passing lanes of each half-wave to this wave's private region
-// of their token's buffer; the running counts live in registers (uniform per
-// half-wave), so there is no LDS atomic or cross-lane round trip.
+// Appends the passing lanes of a half-wave (token j) to this wave's private
+// region of the token's buffer.  The running count wcnt is uniform over the
+// half-wave and lives in a register: no LDS atomic, no cross-lane round trip.
 template <int QT>
-__device__ __forceinline__ void append_private(TopkSmem<QT>& sm, const bool pass[2], const uint32_t val[2],
-                                               int e, int jl0, int wcnt[2]) {
+__device__ __forceinline__ void append_private(TopkSmem<QT>& sm, bool pass, uint32_t val, int e, int j, int& wcnt) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const uint64_t bal = __ballot(pass[tt]);
-    const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
-    const int rank = lane < 32 ? (int)__builtin_amdgcn_mbcnt_lo(lo, 0u) : (int)__builtin_amdgcn_mbcnt_hi(hi, 0u);
-    const int pos = wcnt[tt] + rank;
-    if (pass[tt] && pos < kReg) {
-      const int j = jl0 + tt;
-      sm.key[j][wave * kReg + pos] = val[tt];
-      sm.idx[j][wave * kReg + pos] = e;
-    }
-    wcnt[tt] += lane < 32 ? __builtin_popcount(lo) : __builtin_popcount(hi);
-  }
+  const uint64_t bal = __ballot(pass);
+  const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+  const int plo = __builtin_popcount(lo);
+  // passing lanes below this one in the whole wave, minus the lower half for upper-half lanes
+  const int rank = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u)) - (lane < 32 ? 0 : plo);
+  const int pos = wcnt + rank;
+  if (pass && pos < kReg) sm.cand[j][wave * kReg + pos] = make_uint2(val, (uint32_t)e);
+  wcnt += lane < 32 ? plo : __builtin_popcount(hi);
 }
 
 template <int QT, int FMT>
@@ -670,51 +632,88 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
     for (int h = 0; h < 8; ++h)
       sc.wv[tt][h] = (v > 0 && h < p.H_I) ? p.w[((int64_t)b * p.n + q) * p.H_I + h] : 0.0f;
   }
-  sc.kc = (const uint8_t*)p.kidx + (int64_t)b * p.N * 32;
-  sc.kb = (const uint16_t*)p.kidx + (int64_t)b * p.N * 64;
-  sc.ksc = p.kidx_scale ? p.kidx_scale + (int64_t)b * p.N * 2 : nullptr;
-  sc.N = p.N;
+  {
+    // the descriptors are uniform: build them from scalar values so that the
+    // loads take them from SGPRs
+    auto uniform_ptr = [](const void* ptr) {
+      const uint64_t v = (uint64_t)ptr;
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+      return (void*)(((uint64_t)hi << 32) | lo);
+    };
+    const int nrec = __builtin_amdgcn_readfirstlane(p.N * (FMT == 1 ? 32 : 128));
+    sc.rk = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t*)p.kidx + (int64_t)b * nrec), (short)0, nrec,
+                                              0x00020000);
+    sc.rs = sc.rk;
+    if (FMT == 1)
+      sc.rs = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.kidx_scale + (int64_t)b * p.N * 2), (short)0,
+                                                __builtin_amdgcn_readfirstlane(p.N * 2), 0x00020000);
+    sc.voff_k = (lane >> 5) * 16;
+    sc.voff_s = lane >> 5;
+  }
+  const int l32 = lane & 31;
+  const int grp_j = wave % QT, grp_h = wave / QT;  // this wave's token group and member index
+  constexpr int G = kWaves / QT;                    // waves per token group
+  constexpr int NS = kCap / G / 64;                 // register slots per lane in a group selection
 
   // ---- phase 1: per-token thresholds from a strided sample (entry S*i)
   const bool sampling = maxnv > kCap;
-  const int S = (maxnv + kCap - 1) / kCap;
-  if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = -__builtin_inff(); }
-  if (tid == 0) sm.fallback = 0;
+  int target = p.k + 850;
+  if (target > kCap - 1024) target = kCap - 1024;
+  int S = 1;
   if (sampling) {
-    const int max_ns = (maxnv + S - 1) / S;
-    for (int tile = wave; tile * 32 < max_ns; tile += kWaves) {
-      const int i = tile * 32 + (lane & 31);
-      const int e = S * i;
-      float I[2];
-      sc.score(e, I);
+    // about kMinAbove sampled entries above the threshold, at most kCap samples
+    int64_t want = ((int64_t)kMinAbove * maxnv + target - 1) / target;
+    if (want > kCap) want = kCap;
+    S = (int)((maxnv + want - 1) / want);
+  }
+  if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = -__builtin_inff(); }
+  if (tid == 0) { sm.fallback = 0; sm.ties = 0; }
+  if (sampling) {
+    // sample tiles wave, wave + kWaves, ...; kDepth tiles in flight per wave
+    const int ntile = ((maxnv + S - 1) / S + 31) / 32;
+    BTile<FMT> t[kDepth];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int j = jl0 + tt;
-        if (j < QT && e < nvl[tt]) sm.key[j][i] = __float_as_uint(I[tt]);
+    for (int u = 0; u < kDepth; ++u) {
+      t[u] = sc.load(S * ((wave + u * kWaves) * 32 + l32));
+      __builtin_amdgcn_sched_barrier(0);  // issue order = consumption order (tight waits)
+    }
+    for (int tile0 = wave; tile0 < ntile; tile0 += kDepth * kWaves) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        // unconditional: tiles past the end store nothing (e >= nvl)
+        const int tile = tile0 + u * kWaves;
+        const f32x16 C = sc.mfma(t[u]);
+        t[u] = sc.load(S * ((tile + kDepth * kWaves) * 32 + l32));
+        float I[2];
+        sc.epilogue(C, I);
+        const int i = tile * 32 + l32;
+        const int e = S * i;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int j = jl0 + tt;
+          if (j < QT && e < nvl[tt]) sm.cand[j][i].x = __float_as_uint(I[tt]);
+        }
       }
     }
-  }
-  __syncthreads();
-  if (sampling && wave < QT && nv[wave] > kCap) {
-    const int j = wave;
-    const int ns = (nv[j] + S - 1) / S;
-    int target = p.k + 850;
-    if (target > kCap - 1024) target = kCap - 1024;
-    int r = (int)(((int64_t)target * ns + nv[j] - 1) / nv[j]);
-    r = r < 1 ? 1 : (r > ns ? ns : r);
-    uint32_t kr[kSlots];
-    uint64_t vm = 0;
+    __syncthreads();
+    // sample quantile: member h of token j's group holds samples h*kCap/G + lane + 64m
+    const int nsj = (q0 + grp_j < p.n && nv[grp_j] > kCap) ? (nv[grp_j] + S - 1) / S : 0;
+    uint32_t kr[NS];
+    uint32_t smask = 0u;
 #pragma unroll
-    for (int m = 0; m < kSlots; ++m) {
-      const int i = lane + 64 * m;
-      const bool v = i < ns;
-      kr[m] = okey(sm.key[j][v ? i : 0]);
-      vm |= (uint64_t)v << m;
+    for (int m = 0; m < NS; ++m) {
+      const int i0 = grp_h * (kCap / G) + 64 * m;
+      const int i = i0 + lane;
+      smask |= (i0 < nsj ? 1u : 0u) << m;
+      kr[m] = i < nsj ? okey(sm.cand[grp_j][i].x) : 0u;
     }
-    uint32_t above, inbin;
-    bool exact;
-    const uint32_t T = reg_radix(kr, vm, (uint32_t)r, sm.hist[wave], &above, &inbin, &exact);
-    if (lane == 0) sm.thr[j] = key_to_float(T);
+    int r = nsj > 0 ? (int)(((int64_t)target * nsj + nv[grp_j] - 1) / nv[grp_j]) : 0;
+    r = r < 1 ? 1 : (r > nsj ? nsj : r);
+    // the cut need not be exact: a bin of up to r/16 samples is close enough
+    const RadixOut ro = group_radix<QT, NS>(sm, kr, smask, (uint32_t)r, (uint32_t)nsj, nsj > 0, (uint32_t)(r >> 4));
+    // never above the r-th sample; at least the order key of -inf
+    if (nsj > 0 && grp_h == 0 && lane == 0) sm.thr[grp_j] = key_to_float(max(ro.T, 0x007fffffu));
   }
   __syncthreads();
 
@@ -724,35 +723,35 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
   for (int tt = 0; tt < 2; ++tt) {
     const int j = jl0 + tt;
     thr2[tt] = (j < QT) ? sm.thr[j < QT ? j : 0] : 0.0f;
+    // the LDS read completes here, not inside the scoring loop (whose LDS
+    // stores would otherwise be waited for on every tile)
+    asm volatile("" : "+v"(thr2[tt]));
   }
   {
-    // two tiles in flight: both MFMAs are issued before either epilogue, and
-    // each register set is reloaded right after its MFMA
-    const int ecol = wave * 32 + (lane & 31);
+    // kDepth tiles in flight per wave; each tile's registers are reloaded
+    // right after its MFMA has read them
+    const int ecol = wave * 32 + l32;
     int wcnt[2] = {0, 0};
-    BTile<FMT> ta = sc.load(ecol), tb = sc.load(ecol + kTile);
-    auto finish_tile = [&](const f32x16& C, int base) {
-      const int e = base + ecol;
-      float I[2];
-      sc.epilogue(C, I);
-      bool pass[2];
-      uint32_t val[2];
+    BTile<FMT> t[kDepth];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        pass[tt] = (e < nvl[tt]) && (I[tt] >= thr2[tt]);
-        val[tt] = __float_as_uint(I[tt]);
-      }
-      append_private<QT>(sm, pass, val, e, jl0, wcnt);
-    };
-    for (int base = 0; base < maxnv; base += 2 * kTile) {
-      const f32x16 Ca = sc.mfma(ta);
-      const f32x16 Cb = sc.mfma(tb);
-      ta = sc.load(base + 2 * kTile + ecol);
-      tb = sc.load(base + 3 * kTile + ecol);
-      finish_tile(Ca, base);
-      finish_tile(Cb, base + kTile);
+    for (int u = 0; u < kDepth; ++u) {
+      t[u] = sc.load(u * kTile + ecol);
+      __builtin_amdgcn_sched_barrier(0);  // issue order = consumption order (tight waits)
     }
-    if ((lane & 31) == 0) {
+    for (int base = 0; base < maxnv; base += kDepth * kTile) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {  // unconditional: tiles past the end never pass
+        const f32x16 C = sc.mfma(t[u]);
+        t[u] = sc.load(base + (u + kDepth) * kTile + ecol);
+        const int e = base + u * kTile + ecol;
+        float I[2];
+        sc.epilogue(C, I);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          append_private<QT>(sm, e < nvl[tt] && I[tt] >= thr2[tt], __float_as_uint(I[tt]), e, jl0 + tt, wcnt[tt]);
+      }
+    }
+    if (l32 == 0) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
         if (jl0 + tt < QT) sm.wcnt[wave][jl0 + tt] = wcnt[tt];
@@ -778,7 +777,7 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
     __syncthreads();
     for (int base = 0; base < maxnv; base += kTile) {
       const int e0 = base + wave * 32;
-      const int e = e0 + (lane & 31);
+      const int e = e0 + l32;
       bool pass[2] = {false, false};
       uint32_t val[2] = {0u, 0u};
       if (e0 < maxnv) {
@@ -792,7 +791,7 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
           pass[tt] = (j < QT) && (e < nvl[tt]) && (u >= __float_as_uint(sm.thr[j < QT ? j : 0]));
         }
       }
-      append<QT>(sm, pass, val, e, jl0, false);
+      append<QT>(sm, pass, val, e, jl0);
       __syncthreads();
       int cnow[QT];
 #pragma unroll
@@ -809,114 +808,90 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
       const int cnt = sm.cnt[j];
       wg_bitonic_sort(sm, j, cnt);
       int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
-      for (int i = tid; i < p.k; i += kThreads) o[i] = i < cnt ? sm.idx[j][i] : -1;
+      for (int i = tid; i < p.k; i += kThreads) o[i] = i < cnt ? (int32_t)sm.cand[j][i].y : -1;
       __syncthreads();
     }
     return;
   }
 
-  // ---- phase 3: one wave per token: exact top-k among candidates, ascending output
-  if (wave < QT && q0 + wave < p.n) {
-    const int j = wave;
+  // ---- phase 3: each token's group selects its exact top-k among the
+  // candidates and writes their indices
+  {
+    const int j = grp_j;
     const int q = q0 + j;
+    const bool live = q < p.n;
     const int kk = nv[j] < p.k ? nv[j] : p.k;
-    // candidates in registers, region-major: slot w*8+m <-> region w, position lane + 64m
+    // member h holds regions h*QT .. h*QT + QT - 1; slot s = (region, m) <-> position lane + 64m
     constexpr int kPer = kReg / 64;
-    uint32_t kr[kSlots];
-    uint64_t vm = 0;
+    uint32_t kr[NS];
+    uint32_t ir[NS];
+    uint32_t smask = 0u;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int rr = 0; rr < QT; ++rr) {
+      const int w = grp_h * QT + rr;
       const int cw = sm.wcnt[w][j];
 #pragma unroll
       for (int m = 0; m < kPer; ++m) {
+        const int sl = rr * kPer + m;
         const int pos = lane + 64 * m;
-        const bool v = pos < cw;
-        kr[w * kPer + m] = okey(sm.key[j][w * kReg + (v ? pos : 0)]);
-        vm |= (uint64_t)v << (w * kPer + m);
+        smask |= (64 * m < cw ? 1u : 0u) << sl;
+        const uint2 v = sm.cand[j][w * kReg + (pos < cw ? pos : 0)];
+        kr[sl] = pos < cw ? okey(v.x) : 0u;
+        ir[sl] = v.y;
       }
     }
     const int c = sm.cnt[j];
-    uint32_t T = 0u;
-    int ties = 0;
-    int32_t id_lim = 0;
-    if (c > kk) {
-      uint32_t above, inbin;
-      bool exact;
-      T = reg_radix(kr, vm, (uint32_t)kk, sm.hist[wave], &above, &inbin, &exact);
-      if (exact && (uint32_t)kk - above < inbin) {
-        // ties at T: keep the (kk - above) smallest entry indices among them
-        uint32_t a2, b2;
-        bool e2;
-        const uint32_t* keys = sm.key[j];
-        const int32_t* ids = sm.idx[j];
-        auto slot_i = [&](int i) { return (i / kReg) * kReg + (i % kReg); };
-        const uint32_t tinv = wave_radix(
-            sm.hist[wave], kCap, (uint32_t)kk - above,
-            [&](int i) { return ~(uint32_t)ids[slot_i(i)]; },
-            [&](int i) { return (i % kReg) < sm.wcnt[i / kReg][j] && okey(keys[slot_i(i)]) == T; },
-            &a2, &b2, &e2);
-        ties = 1;
-        id_lim = (int32_t)~tinv;
-      }
+    const bool sel = live && c > kk;
+    const RadixOut ro = group_radix<QT, NS>(sm, kr, smask, (uint32_t)kk, (uint32_t)c, sel);
+    const bool need_ties = sel && ro.exact && (uint32_t)kk - ro.above < ro.inbin;
+    if (need_ties && grp_h == 0 && lane == 0) sm.ties = 1;
+    __syncthreads();
+    uint32_t tinv = 0u;
+    if (sm.ties) {
+      // ties at the k-th score: keep the (kk - above) smallest entry indices among them
+      uint32_t k2[NS];
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) k2[sl] = (need_ties && kr[sl] == ro.T) ? ~ir[sl] : 0u;
+      const RadixOut r2 = group_radix<QT, NS>(sm, k2, smask, (uint32_t)kk - ro.above, ro.inbin, need_ties);
+      tinv = r2.T;
     }
-    // keep mask over the register slots
-    uint64_t keep = 0;
+    const uint32_t Tk = sel ? max(ro.T, 1u) : 1u;  // empty slots (key 0) are never kept
+    uint32_t keep = 0u;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
+    for (int sl = 0; sl < NS; ++sl) {
+      bool kp = kr[sl] >= Tk;
+      if (need_ties && kr[sl] == ro.T) kp = ~ir[sl] >= tinv;
+      keep |= (kp ? 1u : 0u) << sl;
+    }
+    // output: the kept entries region by region (regions 0..kWaves-1 of the
+    // token, each in its append order), padded with -1
 #pragma unroll
-      for (int m = 0; m < kPer; ++m) {
-        const int sl = w * kPer + m;
-        if (!((vm >> sl) & 1ull)) continue;
-        bool kp = kr[sl] >= T;
-        if (ties && kr[sl] == T) kp = sm.idx[j][w * kReg + lane + 64 * m] <= id_lim;
-        keep |= (uint64_t)kp << sl;
-      }
-    // ascending output through bitmap segments, staged in key[j][0..kk)
-    uint32_t* bm = sm.bits[wave];
-    uint32_t* stage = sm.key[j];
-    int outc = 0;
-    for (int seg = 0; seg < nv[j]; seg += kSeg) {
+    for (int rr = 0; rr < QT; ++rr) {
+      int cnt = 0;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) *(u32x4*)(bm + 16 * lane + 4 * x) = u32x4{0u, 0u, 0u, 0u};
-      __builtin_amdgcn_wave_barrier();
+      for (int m = 0; m < kPer; ++m) cnt += __builtin_popcountll(__ballot((keep >> (rr * kPer + m)) & 1u));
+      if (lane == 0) sm.kept[j][grp_h * QT + rr] = cnt;
+    }
+    __syncthreads();
+    if (live) {
+      int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
+      int pos = 0;
+      for (int w = 0; w < grp_h * QT; ++w) pos += sm.kept[j][w];
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w)
+      for (int rr = 0; rr < QT; ++rr) {
 #pragma unroll
         for (int m = 0; m < kPer; ++m) {
-          const int sl = w * kPer + m;
-          if ((keep >> sl) & 1ull) {
-            const int s = sm.idx[j][w * kReg + lane + 64 * m] - seg;
-            if (s >= 0 && s < kSeg) atomicOr(&bm[s >> 5], 1u << (s & 31));
-          }
-        }
-      __builtin_amdgcn_wave_barrier();
-      uint32_t wds[16];  // lane owns words [16 lane, 16 lane + 16)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const u32x4 v = *(const u32x4*)(bm + 16 * lane + 4 * x);
-        wds[4 * x] = v[0]; wds[4 * x + 1] = v[1]; wds[4 * x + 2] = v[2]; wds[4 * x + 3] = v[3];
-      }
-      uint32_t cntl = 0;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) cntl += __builtin_popcount(wds[x]);
-      const uint32_t incl = wave_prefix_sum(cntl);
-      const int tot = __builtin_amdgcn_readlane((int)incl, 63);
-      int pos = outc + (int)(incl - cntl);
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        uint32_t wbits = wds[x];
-        while (wbits) {
-          const int bit = __builtin_ctz(wbits);
-          wbits &= wbits - 1u;
-          stage[pos++] = (uint32_t)(seg + 32 * (16 * lane + x) + bit);
+          const int sl = rr * kPer + m;
+          const bool kp = (keep >> sl) & 1u;
+          const uint64_t bal = __ballot(kp);
+          const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          if (kp && pos + rank < p.k) o[pos + rank] = (int32_t)ir[sl];
+          pos += __builtin_popcountll(bal);
         }
       }
-      outc += tot;
-      __builtin_amdgcn_wave_barrier();
+      for (int i = kk + grp_h * 64 + lane; i < p.k; i += G * 64) o[i] = -1;
     }
-    int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
-    for (int i = lane; i < p.k; i += 64) o[i] = i < kk ? (int32_t)stage[i] : -1;
   }
 }
 
