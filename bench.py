@@ -30,6 +30,35 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA/HCA forward query-tokens/s at 128K ctx; % MFMA / HBM roofline"
 PEAK = {"bf16": 2500.0, "fp4": 10100.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s (MI355X)
 
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# (scaled by the plain-copy calibration of --copy-probe), keyed by the
+# sha256 of the kernel source they were taken on: a changed kernel reports
+# null until it is measured again.
+TRAFFIC = {  # profiles/csa_prefill_128k_hbm_counters.txt
+    ("csa_attend", 3): {"sha256": "9eea36c3279a74f73dae90780ffc27f42e859a4a1dc7597a592f457362a2c3c5",
+                        "bytes": 1.852e10},
+    ("csa_index_topk", 3): {"sha256": "ea442c78d7fa3476a387827a409882b532a752cc74ff43be7668878dfc8062eb",
+                            "bytes": 1.219e9},
+    ("csa_compress", 3): {"sha256": "82c3e1fea99ff0128101cd4a89cfefe6bb708f379c3a3e689974d4dc357c12da",
+                          "bytes": 7.279e7},
+}
+KERNEL_SOURCE = {"csa_compress": "compress.hip", "csa_index_topk": "index_topk.hip",
+                 "csa_attend": "attend.hip", "hca_attend": "attend.hip"}
+
+
+def source_sha(kernel):
+    import hashlib
+    path = os.path.join(ROOT, "long_context_attention_21_amd", "csrc", KERNEL_SOURCE[kernel])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_bytes(kernel, config):
+    t = TRAFFIC.get((kernel, config))
+    if t is None or t["sha256"] != source_sha(kernel):
+        return None
+    return t["bytes"]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -44,7 +73,22 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="query rows of the oracle sample (default per config)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 1 GiB device-to-device 3 times (HBM counter calibration)")
+    ap.add_argument("--print-sha", action="store_true", help="print the kernel source hashes and exit")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": src.numel() * 4, "copy_probe_bytes_written": dst.numel() * 4,
+                      "launches": 3}), flush=True)
 
 
 # ---------------------------------------------------------------- workloads --
@@ -203,6 +247,9 @@ WORKLOAD = {
 
 def main():
     args = parse()
+    if args.print_sha:
+        print(json.dumps({k: source_sha(k) for k in KERNEL_SOURCE}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -210,6 +257,9 @@ def main():
     import torch
     assert torch.cuda.is_available(), "no GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe()
+        return
     wl = CsaLayer(args.config) if args.config in (1, 3) else HcaLayer(args.config)
     nk = len(wl.kernels)
     log("warmup %d steps" % args.warmup)
@@ -242,11 +292,12 @@ def main():
             ach, peak, unit = amount / sec / 1e12, PEAK[kind], "TFLOP/s"
         kernels[name] = {"ms": round(per_k[i], 4), "bound": "hbm" if kind == "hbm" else "mfma",
                          "dtype": kind, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                         "frac": round(ach / peak, 4), "work": amount}
+                         "frac": round(ach / peak, 4), "work": amount,
+                         "traffic": traffic_bytes(name, args.config)}
     dom = wl.kernels[int(np.argmax(per_k))]
     dk = kernels[dom]
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
-                "unit": dk["unit"], "frac": dk["frac"], "traffic": None}
+                "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic_bytes(dom, args.config)}
 
     cpu = None
     if not args.no_cpu:
