@@ -159,8 +159,9 @@ size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m
  *               [B, N, 64] e4m3 codes (value = code * entry_scale)
  *  entries_rope FP8_ROPE_BF16: [B, N, 64] bf16 (dims 64..127); else NULL
  *  entry_scale  FP8_ROPE_BF16: [B, N] fp32; else NULL
- *  idx          [B, n, k] int32 entry indices (-1 = unused slot); every
- *               index must be < N (not checked on the device)
+ *  idx          [B, n, k] int32 entry indices (-1 = unused slot), 16-byte
+ *               aligned, k <= 2048; every index must be < N (not checked on
+ *               the device)
  *  win_kv       [B, win_len, 128] bf16 pre-RoPE raw rows at positions
  *               win_pos0 .. win_pos0+win_len-1; must cover
  *               [max(0, q_pos0-n_win+1), q_pos0+n-1] when n_win > 0

@@ -185,10 +185,17 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   REQUIRE(rope_dims == 0 || (std::isfinite(rope_base) && rope_base > 1.0f),
           "%s: rope_base must be finite and > 1", name);
   REQUIRE(n_win >= 0, "%s: n_win=%d must be >= 0", name, n_win);
+  // row sources are addressed with 32-bit byte offsets inside the kernel
+  REQUIRE((int64_t)N * 256 < 0x7fff0000LL && (int64_t)win_len * 256 < 0x7fff0000LL,
+          "%s: N=%d or win_len=%d too large (at most 8388351 rows)", name, N, win_len);
   if ((int64_t)B * n == 0) return ok();
   REQUIRE(q != nullptr && out != nullptr, "%s: q and out must be non-NULL", name);
   REQUIRE(N == 0 || entries != nullptr, "%s: entries is NULL", name);
-  if (mode == 0 || mode == 1) REQUIRE(k == 0 || idx != nullptr, "%s: idx is NULL", name);
+  if (mode == 0 || mode == 1) {
+    REQUIRE(k <= 2048, "%s: k=%d must be <= 2048", name, k);
+    REQUIRE(k == 0 || idx != nullptr, "%s: idx is NULL", name);
+    REQUIRE(aligned16(idx), "%s: idx must be 16-byte aligned", name);
+  }
   if (mode == 1) REQUIRE(N == 0 || (entries_rope && entry_scale), "%s: FP8 entries need entries_rope and entry_scale", name);
   if (n_win > 0) {
     REQUIRE(win_kv != nullptr, "%s: win_kv is NULL but n_win > 0", name);

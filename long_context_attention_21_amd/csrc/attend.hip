@@ -35,6 +35,7 @@ namespace csa {
 
 constexpr int KP = 136;           // LDS row pitch in bf16 (272 bytes: 16-byte skew per row)
 constexpr float kSlack = 64.0f;  // allowed excess of a score over the reference (log2 units)
+constexpr int kMaxK = 2048;       // largest top-k whose index row is staged in LDS
 
 struct ChunkRegs {
   u32x4 r[2][4];  // key tile kt (rows kt*16 + l%16), dims ks*32 + 8*(l/16) .. +7
@@ -45,6 +46,7 @@ struct ChunkRegs {
 template <int NHT, int MODE>  // MODE 0: CSA bf16 entries, 1: CSA fp8+bf16 entries, 2: HCA
 __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][32 * KP];
+  __shared__ __attribute__((aligned(16))) int32_t Is[MODE == 2 ? 4 : kMaxK];  // the token's idx row
   const int lane = threadIdx.x;
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t tok = blockIdx.x;  // b * n + q
@@ -128,7 +130,19 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   }
   const int n_chunks = n_ent_chunks + ((n_wk + 31) >> 5);
 
-  // entry index of this lane's key kt in chunk c (-1: none); CSA reads idx
+  // CSA: stage the token's index row in LDS once (coalesced 16-byte loads),
+  // so the loop reads indices from LDS and never waits on them in HBM
+  if (MODE != 2) {
+    const int32_t* irow = p.idx + tok * p.k;
+    if ((p.k & 3) == 0) {
+      for (int i = 4 * lane; i < p.k; i += 256) *(u32x4*)&Is[i] = *(const u32x4*)&irow[i];
+    } else {
+      for (int i = lane; i < p.k; i += 64) Is[i] = irow[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // entry index of this lane's key kt in chunk c (-1: none)
   auto fetch_idx = [&](int c, int out[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -136,49 +150,72 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
       int s = -1;
       if (c < n_ent_chunks) {
         if (MODE == 2) s = kk < n_ent ? kk : -1;
-        else if (kk < p.k) s = p.idx[tok * p.k + kk];
+        else if (kk < p.k) s = Is[kk];
       }
       out[kt] = s;
     }
   };
+  // Row sources as buffer descriptors of this batch row.  The hardware
+  // range check returns zeros for offsets past the end, so a missing key
+  // (index -1, past the window, past the last chunk) is an unconditional load
+  // at an out-of-range offset: no branch, and the compiler can track exactly
+  // which loads each use waits for.
+  auto uniform_ptr = [](const void* ptr) {
+    const uint64_t v = (uint64_t)ptr;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (void*)(((uint64_t)hi << 32) | lo);
+  };
+  constexpr int kOOB = 0x7fff0000;  // past every row source (the host bounds them below this)
+  const int bu = __builtin_amdgcn_readfirstlane(b);
+  __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(p.win ? p.win + (int64_t)bu * p.win_len * 128 : p.q), (short)0,
+      p.win ? __builtin_amdgcn_readfirstlane(p.win_len * 256) : 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t rE, rR = rW, rS = rW;
+  if (MODE == 1) {
+    rE = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t*)p.entries + (int64_t)bu * p.N * 64),
+                                           (short)0, __builtin_amdgcn_readfirstlane(p.N * 64), 0x00020000);
+    rR = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.entries_rope + (int64_t)bu * p.N * 64), (short)0,
+                                           __builtin_amdgcn_readfirstlane(p.N * 128), 0x00020000);
+    rS = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.entry_scale + (int64_t)bu * p.N), (short)0,
+                                           __builtin_amdgcn_readfirstlane(p.N * 4), 0x00020000);
+  } else {
+    rE = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.entries + (int64_t)bu * p.N * 128), (short)0,
+                                           __builtin_amdgcn_readfirstlane(p.N * 256), 0x00020000);
+  }
+  const int win_row0 = (int)(j0 - p.win_pos0);  // window source row of key j0
+
   // issue the loads of chunk c (entry indices ids for entry chunks)
   auto issue = [&](int c, const int ids[2], ChunkRegs& R) {
+    const bool ent = c < n_ent_chunks;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      R.v[kt] = false;
-      R.sc[kt] = 1.0f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) R.r[kt][ks] = u32x4{0u, 0u, 0u, 0u};
-      if (c >= n_chunks) continue;
-      if (c < n_ent_chunks) {
-        const int s = ids[kt];
-        if (s < 0) continue;
-        R.v[kt] = true;
-        if (MODE == 1) {
-          const int64_t row = (int64_t)b * p.N + s;
-          const uint8_t* codes = (const uint8_t*)p.entries + row * 64 + 8 * g;
-          const uint16_t* rope = p.entries_rope + row * 64 + 8 * g;
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const uint2 cw = *(const uint2*)(codes + ks * 32);
-            R.r[kt][ks][0] = cw.x;
-            R.r[kt][ks][1] = cw.y;
-          }
-#pragma unroll
-          for (int ks = 2; ks < 4; ++ks) R.r[kt][ks] = *(const u32x4*)(rope + (ks - 2) * 32);
-          R.sc[kt] = p.entry_scale[row];
-        } else {
-          const uint16_t* src = p.entries + ((int64_t)b * p.N + s) * 128 + 8 * g;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) R.r[kt][ks] = *(const u32x4*)(src + ks * 32);
-        }
+      int row;
+      if (ent) {
+        row = ids[kt];
       } else {
         const int wj = (c - n_ent_chunks) * 32 + kt * 16 + l16;
-        if (wj >= n_wk) continue;
-        R.v[kt] = true;
-        const uint16_t* src = p.win + ((int64_t)b * p.win_len + (j0 + wj - p.win_pos0)) * 128 + 8 * g;
+        row = wj < n_wk ? win_row0 + wj : -1;
+      }
+      if (c >= n_chunks) row = -1;
+      R.v[kt] = row >= 0;
+      R.sc[kt] = 1.0f;
+      if (MODE == 1 && ent) {
+        const int oc = row >= 0 ? row * 64 + 8 * g : kOOB;
+        const int orr = row >= 0 ? row * 128 + 16 * g : kOOB;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) R.r[kt][ks] = *(const u32x4*)(src + ks * 32);
+        for (int ks = 0; ks < 2; ++ks) {
+          const auto cw = __builtin_amdgcn_raw_buffer_load_b64(rE, oc + ks * 32, 0, 0);
+          R.r[kt][ks] = u32x4{cw[0], cw[1], 0u, 0u};
+        }
+#pragma unroll
+        for (int ks = 2; ks < 4; ++ks) R.r[kt][ks] = __builtin_amdgcn_raw_buffer_load_b128(rR, orr + (ks - 2) * 64, 0, 0);
+        R.sc[kt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, row >= 0 ? row * 4 : kOOB, 0, 0));
+      } else {
+        const int off = row >= 0 ? row * 256 + 16 * g : kOOB;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          R.r[kt][ks] = __builtin_amdgcn_raw_buffer_load_b128(ent ? rE : rW, off + ks * 64, 0, 0);
       }
     }
   };
@@ -249,24 +286,21 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) O[dt][ht] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    int idx1[2], idx2[2], idx3[2], idx4[2];
     ChunkRegs R;
     {
       int i0[2];
       fetch_idx(0, i0);
-      fetch_idx(1, idx1);
-      fetch_idx(2, idx2);
-      fetch_idx(3, idx3);
       issue(0, i0, R);
     }
     bool again = false;
     for (int c = 0; c < n_chunks; ++c) {
       f32x4 S[2][NHT];
       uint32_t msk[2];
+      int inext[2];
+      fetch_idx(c + 1, inext);
       finish(c, R);
       scores(R, S, msk, c & 1);
-      issue(c + 1, idx1, R);
-      fetch_idx(c + 4, idx4);
+      issue(c + 1, inext, R);
 
       // ---- softmax weights of chunk c (log2 units); masked keys -> -inf
       if ((msk[0] & msk[1]) != 0xffffu) {
@@ -320,9 +354,6 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
       for (int ht = 0; ht < NHT; ++ht)
         Lacc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, P[ht], Lacc[ht], 0, 0, 0);
 
-      idx1[0] = idx2[0]; idx1[1] = idx2[1];
-      idx2[0] = idx3[0]; idx2[1] = idx3[1];
-      idx3[0] = idx4[0]; idx3[1] = idx4[1];
     }
     if (!again) break;
   }
@@ -362,6 +393,424 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 entries (CSA) and HCA.  A work-group of NW waves serves one token; wave
+// w takes head tiles w*NHT .. w*NHT + NHT - 1 (16 heads each), which keeps a
+// wave under 256 registers so that two waves share each SIMD and one wave's
+// MFMAs overlap the other's softmax.  The key rows stream through a ring of
+// LDS chunk buffers filled by direct-to-LDS buffer loads (no registers in
+// flight) kRing - 1 chunks ahead of the one being computed; the waves split
+// each chunk's loads and meet at one barrier per chunk.  K (for S^T) and V^T
+// both come from the ring.  A key row occupies 256 bytes; its 16-byte pieces
+// are XOR-swizzled by the row's low 4 bits so that the K reads (16 rows, one
+// piece each) and the transposing V reads avoid bank conflicts.  One load
+// instruction fills 4 rows: lane l writes row 4q + l/16, piece l%16, and row
+// 4q + h holds key 8h + q of the chunk, so a lane fetches the indices of 8
+// consecutive keys.
+constexpr int kRing = 3;
+template <bool B>
+struct PassTag {
+  static constexpr bool value = B;
+};
+
+__device__ __forceinline__ int ring_key(int r) { return 8 * (r & 3) + (r >> 2); }  // key of ring row r
+
+template <int NHT, int NW, int MODE>  // MODE 0: CSA bf16 entries, 2: HCA
+__global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[kRing][32 * 256];
+  __shared__ __attribute__((aligned(16))) int32_t Is[MODE == 2 ? 4 : kMaxK];  // the token's idx row
+  __shared__ float2 Rt[32];    // (cos, sin) of the token's angle t * theta_f, f = 0..31
+  __shared__ float Rv[32];     // theta_f / 2pi (revolutions per position)
+  __shared__ int flag[2][NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t tok = blockIdx.x;  // b * n + q
+  const int b = (int)(tok / p.n);
+  const int qi = (int)(tok % p.n);
+  const int64_t t = p.q_pos0 + qi;
+  const float LOG2E = 1.4426950408889634f;
+  const int h0 = wave * NHT * 16;  // first head of this wave
+
+  // ---- the token's rotation (angle formed in fp64), the index row (CSA) and
+  // a zeroed ring (rows of missing keys stay finite)
+  if (tid < 32 && p.rope) {
+    float cs, sn;
+    rope_cs((double)t, p.rev[tid], cs, sn);
+    Rt[tid] = make_float2(cs, sn);
+    Rv[tid] = (float)p.rev[tid];
+  }
+  if (MODE == 0) {
+    const int32_t* irow = p.idx + tok * p.k;
+    if ((p.k & 3) == 0) {
+      for (int i = 4 * tid; i < p.k; i += 256 * NW) *(u32x4*)&Is[i] = *(const u32x4*)&irow[i];
+    } else {
+      for (int i = tid; i < p.k; i += 64 * NW) Is[i] = irow[i];
+    }
+  }
+  for (int i = tid; i < kRing * 32 * 16; i += 64 * NW) ((u32x4*)&Ks[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  // ---- Q^T operand: lane l holds head h0 + ht*16 + l16, dims ks*32 + 8g .. +7
+  bf16x8 Q[NHT][4];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int h = h0 + ht * 16 + l16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float x[8];
+      if (h < p.H) {
+        const u32x4 v = *(const u32x4*)(p.q + ((tok * p.H + h) * 128 + ks * 32 + 8 * g));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { x[2 * e] = bf16lo(v[e]); x[2 * e + 1] = bf16hi(v[e]); }
+        if (p.rope && ks >= 2) {
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const float2 r = Rt[(ks - 2) * 16 + 4 * g + pp];
+            const float a0 = x[2 * pp], a1 = x[2 * pp + 1];
+            x[2 * pp] = a0 * r.x - a1 * r.y;
+            x[2 * pp + 1] = a0 * r.y + a1 * r.x;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Q[ht][ks][e] = (__bf16)(x[e] * p.qscale);
+    }
+  }
+
+  // ---- key sequence: entry chunks, then window chunks
+  int n_ent;
+  if (MODE == 2) {
+    const int64_t nv = (t + 1) / p.m;
+    n_ent = (int)(nv < p.N ? nv : p.N);
+  } else {
+    n_ent = p.k;
+  }
+  const int n_ent_chunks = (n_ent + 31) >> 5;
+  int64_t j0 = 0;
+  int n_wk = 0;
+  if (p.n_win > 0) {
+    j0 = t - p.n_win + 1;
+    if (j0 < 0) j0 = 0;
+    n_wk = (int)(t - j0 + 1);
+  }
+  const int n_chunks = n_ent_chunks + ((n_wk + 31) >> 5);
+  const int dt0 = (int)(t - j0);  // t - j of window key 0
+
+  auto uniform_ptr = [](const void* ptr) {
+    const uint64_t v = (uint64_t)ptr;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (void*)(((uint64_t)hi << 32) | lo);
+  };
+  constexpr int kOOB = 0x7fff0000;  // past every row source (the host bounds them below this)
+  const int bu = __builtin_amdgcn_readfirstlane(b);
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(p.win ? p.win + (int64_t)bu * p.win_len * 128 : p.q), (short)0,
+      p.win ? __builtin_amdgcn_readfirstlane(p.win_len * 256) : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rE = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(p.entries + (int64_t)bu * p.N * 128), (short)0, __builtin_amdgcn_readfirstlane(p.N * 256),
+      0x00020000);
+  const int win_row0 = (int)(j0 - p.win_pos0);  // window source row of key j0
+
+  // This wave's share of the loads of chunk c into ring slot `slot`: load
+  // instructions q = wave*QPW .. +QPW-1, each 4 rows.  Always issued: missing
+  // keys and chunks past the end read as zeros.
+  constexpr int QPW = 8 / NW;
+  const int hq = lane >> 4;
+  auto issue = [&](int c, int slot) {
+    int rows[QPW];
+    const int kb0 = c * 32 + 8 * hq + wave * QPW;  // key of this lane's first row
+    if (c < n_ent_chunks) {
+#pragma unroll
+      for (int e = 0; e < QPW; ++e) {
+        const int kk = kb0 + e;
+        if (MODE == 0) rows[e] = kk < p.k ? Is[kk] : -1;
+        else rows[e] = kk < n_ent ? kk : -1;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < QPW; ++e) {
+        const int wj = kb0 - n_ent_chunks * 32 + e;
+        rows[e] = (c < n_chunks && wj < n_wk) ? win_row0 + wj : -1;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rs = c < n_ent_chunks ? rE : rW;
+#pragma unroll
+    for (int e = 0; e < QPW; ++e) {
+      const int q = wave * QPW + e;
+      const int r = 4 * q + hq;
+      const int col = (lane & 15) ^ (r & 15);
+      const int off = rows[e] >= 0 ? rows[e] * 256 + col * 16 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, &Ks[slot][q * 1024]), 16, off, 0, 0, 0);
+    }
+  };
+  // validity of ring rows r = 0..31 of chunk c (bit r)
+  auto chunk_mask = [&](int c) -> uint32_t {
+    const int r = lane & 31;
+    const int kk = ring_key(r);
+    bool v = false;
+    if (c < n_ent_chunks) {
+      const int e = c * 32 + kk;
+      if (MODE == 2) v = e < n_ent;
+      else v = e < p.k && Is[e < p.k ? e : 0] >= 0;
+    } else if (c < n_chunks) {
+      v = (c - n_ent_chunks) * 32 + kk < n_wk;
+    }
+    return (uint32_t)__ballot(v && lane < 32);
+  };
+  // true on every wave if `mine` is true on some wave (flags double-buffered by `par`)
+  int par = 0;
+  auto any_wave = [&](bool mine) -> bool {
+    if (lane == 0) flag[par][wave] = mine ? 1 : 0;
+    __syncthreads();
+    bool a = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) a |= flag[par][w] != 0;
+    par ^= 1;
+    return a;
+  };
+  // wait for chunk c's rows (this wave's loads: only chunk c+1's may still be
+  // outstanding); the barrier makes every wave's loads visible and ends all
+  // reads of chunk c-1, whose slot is refilled right after
+  auto arrive = [&]() {
+    if constexpr (NW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __syncthreads();
+  };
+  // Window chunk c: rotate its rows in place in the ring (dims 64..127 of
+  // each key at its position j = t - d).  R(j) = R(t) R(-d) with d in
+  // [0, 127] taken in fp32 on the hardware sin/cos.  The 32 rows x 8 pieces
+  // of 16 bytes are shared out over the work-group; the caller synchronises.
+  auto rotate_window = [&](int c, int slot) {
+    for (int pi = tid; pi < 256; pi += 64 * NW) {
+      const int r = pi >> 3, rp = pi & 7;
+      uint8_t* ptr = &Ks[slot][0] + r * 256 + (((8 + rp) ^ (r & 15)) << 4);
+      u32x4 w = *(const u32x4*)ptr;
+      const float d = (float)(dt0 - ((c - n_ent_chunks) * 32 + ring_key(r)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int f = rp * 4 + e;
+        float rv = d * Rv[f];
+        rv = rv - __builtin_floorf(rv);
+        const float sd = __builtin_amdgcn_sinf(rv), cd = __builtin_amdgcn_cosf(rv);
+        const float2 rt = Rt[f];
+        const float cs = rt.x * cd + rt.y * sd, sn = rt.y * cd - rt.x * sd;  // angle t - d
+        const float a0 = bf16lo(w[e]), a1 = bf16hi(w[e]);
+        w[e] = pack_bf16(a0 * cs - a1 * sn, a0 * sn + a1 * cs);
+      }
+      *(u32x4*)ptr = w;
+    }
+  };
+  // K operand of a chunk: rows kt*16 + l16, dims ks*32 + 8g .. +7
+  auto load_k = [&](const uint8_t* kb, bf16x8 (&K)[2][4]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        K[kt][ks] = *(const bf16x8*)(kb + (kt * 16 + l16) * 256 + (((ks * 4 + g) ^ l16) << 4));
+  };
+
+  // ---- softmax reference per head (log2 units): the sink logit, or 0
+  // without a sink.  The pass seeds the S accumulators with -mref (MFMA C
+  // operand) and takes weights exp2(S) with no per-chunk test.  If on some
+  // head the row sum left [2^-100, 2^100) (a weight overflowed, or all
+  // underflowed), a max-only pass sets mref to the exact maximum of the sink
+  // and all scores, after which every weight is <= 1 and the pass reruns.
+  float mref[NHT];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int h = h0 + ht * 16 + l16;
+    mref[ht] = p.sink ? (h < p.H ? p.sink[h] : 0.0f) * LOG2E : 0.0f;
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  f32x4 O[8][NHT], Lacc[NHT];
+
+  // one pass over every chunk; returns true (on every wave) if some head's
+  // row sum left [2^-100, 2^100)
+  auto run = [&]() -> bool {
+    f32x4 Cneg[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = h0 + ht * 16 + l16;
+      const float l0 = p.sink ? __builtin_amdgcn_exp2f((h < p.H ? p.sink[h] : 0.0f) * LOG2E - mref[ht]) : 0.0f;
+      Lacc[ht] = f32x4{l0, l0, l0, l0};
+      Cneg[ht] = f32x4{-mref[ht], -mref[ht], -mref[ht], -mref[ht]};
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) O[dt][ht] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    issue(0, 0);
+    issue(1, 1);
+    int slot = 0, slot_next = 2;
+    for (int c = 0; c < n_chunks; ++c) {
+      arrive();
+      issue(c + 2, slot_next);
+      const uint8_t* kb = &Ks[slot][0];
+      const uint32_t msk = chunk_mask(c);
+      if (c >= n_ent_chunks && p.rope) {
+        rotate_window(c, slot);
+        __syncthreads();  // rotated rows visible to every wave
+      }
+      bf16x8 K[2][4];
+      load_k(kb, K);
+
+      // ---- S^T = K Q^T - mref; weights exp2
+      f32x4 S[2][NHT];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+          S[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(K[kt][0], Q[ht][0], Cneg[ht], 0, 0, 0);
+#pragma unroll
+        for (int ks = 1; ks < 4; ++ks)
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht)
+            S[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(K[kt][ks], Q[ht][ks], S[kt][ht], 0, 0, 0);
+      }
+      bf16x8 P[NHT];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) P[ht][kt * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(S[kt][ht][i]);
+      if (msk != 0xffffffffu) {
+        // missing keys get weight 0 (their rows are zero, but the weight
+        // must not reach the row sums, nor be inf next to a zero value)
+        u32x4 keepw;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const int e = 2 * w2;  // elements e, e+1 <-> rows (e>>2)*16 + 4g + (e&3), +1
+          const int r0 = (e >> 2) * 16 + 4 * g + (e & 3);
+          keepw[w2] = (((msk >> r0) & 1u) ? 0x0000ffffu : 0u) | (((msk >> (r0 + 1)) & 1u) ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) P[ht] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, P[ht]) & keepw);
+      }
+
+      // ---- O^T += V^T P^T (V^T by transposing LDS reads); L += 1^T P^T
+      const int vrow = 4 * g + (l16 >> 2);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int piece = ((dt * 2 + ((l16 & 3) >> 1)) ^ vrow) & 15;  // (vrow + 16) & 15 == vrow & 15
+        const int boff = (piece << 4) + ((l16 & 1) << 3);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, kb + vrow * 256 + boff));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, kb + (vrow + 16) * 256 + boff));
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+          O[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[ht], O[dt][ht], 0, 0, 0);
+      }
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+        Lacc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, P[ht], Lacc[ht], 0, 0, 0);
+      slot = slot == kRing - 1 ? 0 : slot + 1;
+      slot_next = slot_next == kRing - 1 ? 0 : slot_next + 1;
+    }
+    // every load into the ring has landed before the ring is reused or released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    bool bad = false;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) bad |= !(Lacc[ht][0] < 0x1p100f && Lacc[ht][0] >= 0x1p-100f);
+    return any_wave(__ballot(bad) != 0);
+  };
+  // max-only pass: mref = max(sink logit, every valid score) per head
+  auto run_max = [&]() {
+    float m[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = h0 + ht * 16 + l16;
+      m[ht] = p.sink ? (h < p.H ? p.sink[h] : 0.0f) * LOG2E : -__builtin_inff();
+    }
+    __syncthreads();  // every wave is done with the ring
+    issue(0, 0);
+    issue(1, 1);
+    int slot = 0, slot_next = 2;
+    for (int c = 0; c < n_chunks; ++c) {
+      arrive();
+      issue(c + 2, slot_next);
+      const uint32_t msk = chunk_mask(c);
+      if (c >= n_ent_chunks && p.rope) {
+        rotate_window(c, slot);
+        __syncthreads();  // rotated rows visible to every wave
+      }
+      bf16x8 K[2][4];
+      load_k(&Ks[slot][0], K);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4 S2[NHT];
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+          S2[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(K[kt][0], Q[ht][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int ks = 1; ks < 4; ++ks)
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht)
+            S2[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(K[kt][ks], Q[ht][ks], S2[ht], 0, 0, 0);
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((msk >> (kt * 16 + 4 * g + i)) & 1u) m[ht] = fmaxf(m[ht], S2[ht][i]);
+      }
+      slot = slot == kRing - 1 ? 0 : slot + 1;
+      slot_next = slot_next == kRing - 1 ? 0 : slot_next + 1;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave is done with the ring before the rerun refills it
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) mref[ht] = fmaxf(max_over_groups(m[ht]), -1e30f);
+  };
+  if (run()) {
+    run_max();
+    run();
+  }
+
+  // ---- normalise, inverse RoPE on dims 64..127 (by -t), store bf16
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int h = h0 + ht * 16 + l16;
+    const float L = Lacc[ht][0];
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    if (h >= p.H) continue;
+    uint16_t* orow = p.out + (tok * p.H + h) * 128;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      float o0 = O[dt][ht][0] * inv, o1 = O[dt][ht][1] * inv;
+      float o2 = O[dt][ht][2] * inv, o3 = O[dt][ht][3] * inv;
+      if (p.rope && dt >= 4) {
+        const float2 r0c = Rt[8 * (dt - 4) + 2 * g], r1c = Rt[8 * (dt - 4) + 2 * g + 1];
+        const float r0 = o0 * r0c.x + o1 * r0c.y, r1 = o1 * r0c.x - o0 * r0c.y;
+        const float r2 = o2 * r1c.x + o3 * r1c.y, r3 = o3 * r1c.x - o2 * r1c.y;
+        o0 = r0; o1 = r1; o2 = r2; o3 = r3;
+      }
+      uint2 w;
+      w.x = pack_bf16(o0, o1);
+      w.y = pack_bf16(o2, o3);
+      *(uint2*)(orow + dt * 16 + 4 * g) = w;
+    }
+  }
+}
+
+template <int MODE>
+static hipError_t launch_ring(const AttendParams& p, hipStream_t stream) {
+  const int nht = (p.H + 15) / 16;
+  dim3 grid((unsigned)((int64_t)p.B * p.n));
+  // up to 32 heads: one wave; more: two waves of up to 32 heads each
+  switch (nht) {
+    case 1: hipLaunchKernelGGL((attend_ring_kernel<1, 1, MODE>), grid, dim3(64), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((attend_ring_kernel<2, 1, MODE>), grid, dim3(64), 0, stream, p); break;
+    case 3:
+    case 4: hipLaunchKernelGGL((attend_ring_kernel<2, 2, MODE>), grid, dim3(128), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int MODE>
 static hipError_t launch_mode(const AttendParams& p, hipStream_t stream) {
   const int nht = (p.H + 15) / 16;
@@ -379,9 +828,9 @@ static hipError_t launch_mode(const AttendParams& p, hipStream_t stream) {
 hipError_t launch_attend(const AttendParams& p, int mode, hipStream_t stream) {
   if ((int64_t)p.B * p.n == 0) return hipSuccess;
   switch (mode) {
-    case 0: return launch_mode<0>(p, stream);
+    case 0: return launch_ring<0>(p, stream);
     case 1: return launch_mode<1>(p, stream);
-    case 2: return launch_mode<2>(p, stream);
+    case 2: return launch_ring<2>(p, stream);
   }
   return hipErrorInvalidValue;
 }
