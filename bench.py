@@ -42,7 +42,7 @@ TRAFFIC = {  # profiles/csa_prefill_128k_hbm_counters.txt
     ("csa_compress", 3): {"sha256": "82c3e1fea99ff0128101cd4a89cfefe6bb708f379c3a3e689974d4dc357c12da",
                           "bytes": 7.279e7},
 }
-KERNEL_SOURCE = {"csa_compress": "compress.hip", "csa_index_topk": "index_topk.hip",
+KERNEL_SOURCE = {"csa_compress": "compress.hip", "hca_compress": "compress.hip", "csa_index_topk": "index_topk.hip",
                  "csa_attend": "attend.hip", "hca_attend": "attend.hip"}
 
 
@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3])
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="query rows of the oracle sample (default per config)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -238,8 +238,224 @@ class HcaLayer:
         return rows.size / total, rows.size, t_comp, t_rows
 
 
+def encode_cache(L, entries_bf16, keys_bf16, entry_fmt, out):
+    """Store given cache rows in the library's formats: csa_compress with
+    m = 1 (one-slot pooling is the identity) and no rotation writes the rows
+    as bf16 or FP8 + bf16 entries and MXFP4 indexer keys."""
+    import torch
+    beta = torch.zeros(1, dtype=torch.float32, device="cuda")
+    return L.csa_compress(entries_bf16, beta, 1, 0, ik=keys_bf16, rope_dims=0, entry_fmt=entry_fmt,
+                          kidx_fmt="mxfp4", out=out)
+
+
+class DecodeLayer:
+    """Config 4: single-token CSA decode, 64 sequences at t = 1,048,576 over
+    262,144 FP8 + bf16 entries and MXFP4 indexer keys each (caches given):
+    csa_index_topk -> csa_attend."""
+
+    def __init__(self, cfg_id):
+        import torch
+        import long_context_attention_21_amd as L
+        from long_context_attention_21_amd import synth
+        self.L = L
+        c = synth.config(cfg_id)
+        self.c = c
+        B, N, H = c["B"], c["N"], c["H"]
+        self.B, self.N, self.H, self.k = B, N, H, c["k"]
+        self.n = B  # query tokens per step
+        cu = "cuda"
+        self.codes = torch.empty((B, N, 64), dtype=torch.uint8, device=cu)
+        self.rope = torch.empty((B, N, 64), dtype=torch.bfloat16, device=cu)
+        self.scale = torch.empty((B, N), dtype=torch.float32, device=cu)
+        self.kc = torch.empty((B, N, 32), dtype=torch.uint8, device=cu)
+        self.ks = torch.empty((B, N, 2), dtype=torch.uint8, device=cu)
+        self.swa = torch.empty((B, c["n_win"], 128), dtype=torch.bfloat16, device=cu)
+        t0 = time.time()
+        self.host = []
+        for b in range(B):
+            ent, ik, swa = c["seq"](b)
+            from long_context_attention_21_amd.synth import to_bf16_bits
+            e16 = dev_bf16(to_bf16_bits(ent)[None])
+            k16 = dev_bf16(to_bf16_bits(ik)[None])
+            encode_cache(L, e16, k16, "fp8", {"entries": self.codes[b:b + 1], "entries_rope": self.rope[b:b + 1],
+                                              "entry_scale": self.scale[b:b + 1], "kidx": self.kc[b:b + 1],
+                                              "kidx_scale": self.ks[b:b + 1]})
+            self.swa[b] = dev_bf16(swa)
+        q, q_I, w_I, sink = c["tail"]()
+        log("decode caches generated and stored in %.1f s" % (time.time() - t0))
+        self.q, self.qI, self.w, self.sink = dev_bf16(q), dev_bf16(q_I), dev(w_I), dev(sink)
+        self.idx = torch.empty((B, 1, self.k), dtype=torch.int32, device=cu)
+        self.out = torch.empty((B, 1, H, 128), dtype=torch.bfloat16, device=cu)
+        self.kernels = ["csa_index_topk", "csa_attend"]
+        keys = B * (min(self.k, N) + c["n_win"])
+        # bytes: the indexer scans every key (34 B); attention gathers k entries (196 B) + window (256 B)
+        self.work = {
+            "csa_index_topk": ("hbm", B * N * 34),
+            "csa_attend": ("hbm", B * (min(self.k, N) * 196 + c["n_win"] * 256 + 2 * H * 256 + 4 * self.k)),
+        }
+        self.keys = keys
+
+    def step(self, ev=None):
+        L, c = self.L, self.c
+        if ev: ev[0].record()
+        L.csa_index_topk(self.qI, self.w, self.kc, self.k, 4, q_pos0=c["q_pos0"], fmt="mxfp4",
+                         kidx_scale=self.ks, idx_out=self.idx)
+        if ev: ev[1].record()
+        L.csa_attend(self.q, self.codes, self.idx, q_pos0=c["q_pos0"], m=4, win_kv=self.swa,
+                     win_pos0=c["win_pos0"], sink=self.sink, entries_rope=self.rope, entry_scale=self.scale,
+                     out=self.out)
+        if ev: ev[2].record()
+
+    cpu_desc = ("%d sequences (all): oracle top-k over 262144 entries + attention for each query "
+                "(%.1f s); reading back and decoding the stored caches (%.1f s) is not charged")
+
+    def cpu_baseline(self, sample):
+        """The oracle on `sample` of the sequences (decoded caches read back)."""
+        import oracle as orc
+        c = self.c
+        nb = min(sample, self.B)
+        t0 = time.time()
+        q = self.q.view(torch_int16()).cpu().numpy().view(np.uint16)
+        qI = self.qI.view(torch_int16()).cpu().numpy().view(np.uint16)
+        w = self.w.cpu().numpy()
+        sink = self.sink.cpu().numpy()
+        t_rows = 0.0
+        for b in range(nb):
+            kdec = orc.mxfp4_decode(self.kc[b].cpu().numpy(), self.ks[b].cpu().numpy())
+            E = orc.load_entries_fp8(self.codes[b].cpu().numpy(), self.rope[b].view(torch_int16()).cpu().numpy()
+                                     .view(np.uint16), self.scale[b].cpu().numpy())
+            swa = self.swa[b].view(torch_int16()).cpu().numpy().view(np.uint16)
+            qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(qI[b]).astype(np.float32))
+            t1 = time.time()
+            rows = np.zeros(1, np.int32)
+            idx = orc.index_topk_rows(orc.mxfp4_decode(qc, qs), w[b], kdec, 4, c["q_pos0"], rows, self.k)
+            orc.attend_rows(q[b], c["q_pos0"], E, 4, rows, "csa", idx=idx, win=swa, win_pos0=c["win_pos0"],
+                            sink=sink)
+            t_rows += time.time() - t1
+        return nb / t_rows, nb, time.time() - t0 - t_rows, t_rows
+
+
+class PairLayer:
+    """Config 5: chunked prefill of one CSA + HCA layer pair, 8192 new tokens
+    at P = 1,048,576 over given caches (CSA: 262,144 bf16 entries + MXFP4
+    indexer keys, Zipf-skewed; HCA: 8,192 entries) and 128-token state caches.
+    CSA: csa_compress (appends 2,048 entries) -> csa_index_topk -> csa_attend;
+    HCA: csa_compress (appends 64 entries) -> hca_attend."""
+
+    def __init__(self, cfg_id):
+        import torch
+        import long_context_attention_21_amd as L
+        from long_context_attention_21_amd import synth
+        self.L = L
+        t0 = time.time()
+        c = synth.config(cfg_id)
+        self.c = c
+        cs, hs = c["csa"], c["hca"]
+        n, P, H, k = c["n"], c["P"], c["H"], c["k"]
+        self.n, self.P, self.H, self.k = n, P, H, k
+        Nc0, Nh0 = c["N_csa_prior"], c["N_hca_prior"]
+        self.Nc, self.Nh = Nc0 + n // 4, Nh0 + n // 128
+        self.Nc0, self.Nh0 = Nc0, Nh0
+        cu = "cuda"
+        # CSA caches: prior rows stored by the library's encoder, room for the chunk's entries
+        self.c_ent = torch.empty((1, self.Nc, 128), dtype=torch.bfloat16, device=cu)
+        self.c_kc = torch.empty((1, self.Nc, 32), dtype=torch.uint8, device=cu)
+        self.c_ks = torch.empty((1, self.Nc, 2), dtype=torch.uint8, device=cu)
+        encode_cache(L, dev_bf16(cs["entries_prior"][None]),
+                     dev_bf16(synth.to_bf16_bits(cs["kI_prior_f32"])[None]), "bf16",
+                     {"entries": self.c_ent[:, :Nc0], "kidx": self.c_kc[:, :Nc0], "kidx_scale": self.c_ks[:, :Nc0]})
+        # window sources: state (positions P-128 .. P-1) followed by the chunk
+        self.c_win = dev_bf16(np.concatenate([cs["state_kv"], cs["kv_new"]])[None])
+        self.c_ik = dev_bf16(np.concatenate([cs["state_ik"], cs["ik_new"]])[None])
+        self.c_q, self.c_qI, self.c_w = dev_bf16(cs["q"][None]), dev_bf16(cs["q_I"][None]), dev(cs["w_I"][None])
+        self.c_beta, self.c_sink = dev(cs["beta"]), dev(cs["sink"])
+        self.h_ent = torch.empty((1, self.Nh, 128), dtype=torch.bfloat16, device=cu)
+        self.h_ent[:, :Nh0] = dev_bf16(hs["entries_prior"][None])
+        self.h_win = dev_bf16(np.concatenate([hs["state_kv"], hs["kv_new"]])[None])
+        self.h_q, self.h_beta, self.h_sink = dev_bf16(hs["q"][None]), dev(hs["beta"]), dev(hs["sink"])
+        self.idx = torch.empty((1, n, k), dtype=torch.int32, device=cu)
+        self.c_out = torch.empty((1, n, H, 128), dtype=torch.bfloat16, device=cu)
+        self.h_out = torch.empty((1, n, H, 128), dtype=torch.bfloat16, device=cu)
+        log("pair inputs generated in %.1f s" % (time.time() - t0))
+        self.kernels = ["csa_compress", "csa_index_topk", "csa_attend", "hca_compress", "hca_attend"]
+        t = P + np.arange(n, dtype=np.int64)
+        nv = np.minimum(self.Nc, (t + 1) // 4)
+        pairs = int(nv.sum())
+        keys_c = int((np.minimum(k, nv) + 128).sum())
+        keys_h = int((np.minimum(self.Nh, (t + 1) // 128) + 128).sum())
+        self.work = {
+            "csa_compress": ("hbm", n * (256 + 128) + (n // 4) * (256 + 34)),
+            "csa_index_topk": ("fp4", 2.0 * 8 * 64 * pairs),
+            "csa_attend": ("bf16", 4.0 * H * 128 * keys_c),
+            "hca_compress": ("hbm", n * 256 + (n // 128) * 256),
+            "hca_attend": ("bf16", 4.0 * H * 128 * keys_h),
+        }
+
+    def step(self, ev=None):
+        L, P, n = self.L, self.P, self.n
+        if ev: ev[0].record()
+        L.csa_compress(self.c_win[:, 128:], self.c_beta, 4, 1, pos0=P, ik=self.c_ik[:, 4:],
+                       prev_kv=self.c_win[:, 124:128], prev_ik=self.c_ik[:, :4], kidx_fmt="mxfp4",
+                       out={"entries": self.c_ent[:, self.Nc0:], "kidx": self.c_kc[:, self.Nc0:],
+                            "kidx_scale": self.c_ks[:, self.Nc0:]})
+        if ev: ev[1].record()
+        L.csa_index_topk(self.c_qI, self.c_w, self.c_kc, self.k, 4, q_pos0=P, fmt="mxfp4",
+                         kidx_scale=self.c_ks, idx_out=self.idx)
+        if ev: ev[2].record()
+        L.csa_attend(self.c_q, self.c_ent, self.idx, q_pos0=P, m=4, win_kv=self.c_win, win_pos0=P - 128,
+                     sink=self.c_sink, out=self.c_out)
+        if ev: ev[3].record()
+        L.csa_compress(self.h_win[:, 128:], self.h_beta, 128, 0, pos0=P, out={"entries": self.h_ent[:, self.Nh0:]})
+        if ev: ev[4].record()
+        L.hca_attend(self.h_q, self.h_ent, q_pos0=P, m=128, win_kv=self.h_win, win_pos0=P - 128,
+                     sink=self.h_sink, out=self.h_out)
+        if ev: ev[5].record()
+
+    cpu_desc = ("%d query rows of the 8192-token chunk drawn uniformly (seed 0): oracle CSA top-k + CSA "
+                "attention + HCA attention for those rows (%.1f s) plus the chunk's compression and cache "
+                "decoding (%.1f s, compression charged pro rata)")
+
+    def cpu_baseline(self, sample):
+        """The oracle on `sample` query rows of the chunk (both layers), the
+        chunk's compression charged pro rata."""
+        import oracle as orc
+        c, cs, hs = self.c, self.c["csa"], self.c["hca"]
+        rng = np.random.default_rng(0)
+        rows = np.sort(rng.choice(self.n, size=min(sample, self.n), replace=False)).astype(np.int32)
+        t0 = time.time()
+        ent_new, kid_new = orc.compress(cs["kv_new"], cs["beta"], 4, 1, pos0=self.P, ik=cs["ik_new"],
+                                        prev_kv=cs["state_kv"][124:], prev_ik=cs["state_ik"])
+        hent_new, _ = orc.compress(hs["kv_new"], hs["beta"], 128, 0, pos0=self.P)
+        t_comp = time.time() - t0
+        E = np.concatenate([orc.bf16_to_f64(cs["entries_prior"]),
+                            orc.bf16_to_f64(orc.bf16_from_f32(ent_new))])
+        kq, ks = orc.mxfp4_encode(orc.bf16_to_f64(orc.bf16_from_f32(cs["kI_prior_f32"])).astype(np.float32))
+        kn, ksn = orc.mxfp4_encode(kid_new)
+        kdec = np.concatenate([orc.mxfp4_decode(kq, ks), orc.mxfp4_decode(kn, ksn)])
+        qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(cs["q_I"]).astype(np.float32))
+        HE = np.concatenate([orc.bf16_to_f64(hs["entries_prior"]), orc.bf16_to_f64(orc.bf16_from_f32(hent_new))])
+        win_c = np.concatenate([cs["state_kv"], cs["kv_new"]])
+        win_h = np.concatenate([hs["state_kv"], hs["kv_new"]])
+        t_prep = time.time() - t0 - t_comp
+        t1 = time.time()
+        idx = orc.index_topk_rows(orc.mxfp4_decode(qc, qs), cs["w_I"], kdec, 4, self.P, rows, self.k)
+        orc.attend_rows(cs["q"], self.P, E, 4, rows, "csa", idx=idx, win=win_c, win_pos0=self.P - 128,
+                        sink=cs["sink"])
+        orc.attend_rows(hs["q"], self.P, HE, 128, rows, "hca", win=win_h, win_pos0=self.P - 128, sink=hs["sink"])
+        t_rows = time.time() - t1
+        total = t_rows + t_comp * rows.size / self.n
+        return rows.size / total, rows.size, t_comp + t_prep, t_rows
+
+
+def torch_int16():
+    import torch
+    return torch.int16
+
+
 WORKLOAD = {
     1: "CSA layer forward, batch 1, 1024 tokens, 8 heads x 128, m=4 overlapped, bf16 indexer 4x64, top-k 64, SWA 128, sink",
+    4: "CSA decode, 64 sequences x 1 token at t=1048576, 262144 FP8+bf16 entries + MXFP4 indexer keys each, top-k 2048, SWA 128, sink",
+    5: "CSA+HCA layer pair, chunked prefill of 8192 tokens at P=1048576 (CSA 262144 prior entries, Zipf-skewed indexer keys; HCA 8192 prior entries), 64 heads, top-k 2048, SWA 128, sink",
     2: "HCA layer forward, batch 1, 32768 tokens, 64 heads x 128, m'=128 (256 entries), SWA 128, sink",
     3: "CSA prefill, batch 1, 131072 tokens, 64 heads x 128, m=4 overlapped (32768 entries), MXFP4 indexer 8x64, top-k 2048, SWA 128, sink",
 }
@@ -260,7 +476,7 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
-    wl = CsaLayer(args.config) if args.config in (1, 3) else HcaLayer(args.config)
+    wl = {1: CsaLayer, 2: HcaLayer, 3: CsaLayer, 4: DecodeLayer, 5: PairLayer}[args.config](args.config)
     nk = len(wl.kernels)
     log("warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
@@ -301,27 +517,31 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        sample = args.cpu_sample or {1: 1024, 2: 32768, 3: 8192}[args.config]
+        sample = args.cpu_sample or {1: 1024, 2: 32768, 3: 8192, 4: 64, 5: 256}[args.config]
         log("cpu baseline: oracle on %d sampled query rows" % sample)
         import oracle
         oracle.build()
         v, rows, t_comp, t_rows = wl.cpu_baseline(sample)
+        desc = getattr(wl, "cpu_desc", None)
         cores = len(os.sched_getaffinity(0))
         omp = os.environ.get("OMP_NUM_THREADS")
         if omp:
             cores = min(cores, int(omp))
         cpu = {"value": round(v, 2), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
-               "sample": "%d query rows drawn uniformly over the sequence (seed 0): oracle top-k + "
+               "sample": (desc % (rows, t_rows, t_comp)) if desc else
+                         "%d query rows drawn uniformly over the sequence (seed 0): oracle top-k + "
                          "attention for those rows (%.1f s) plus whole-sequence compression "
                          "(%.1f s) charged pro rata" % (rows, t_rows, t_comp)}
 
-    cfg = {"workload": WORKLOAD[args.config], "global_batch": 1, "seq_len": wl.n,
+    cfg = {"workload": WORKLOAD[args.config], "global_batch": getattr(wl, "B", 1), "seq_len": wl.n,
            "heads": wl.H, "head_dim": 128}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 (attention MFMA) + mxfp4 (indexer MFMA)" if args.config == 3 else "bf16",
+        "dtype": {1: "bf16", 2: "bf16", 3: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)",
+                  4: "fp8 e4m3 + bf16 entries, bf16 MFMA (attention) + mxfp4 (indexer MFMA)",
+                  5: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)"}[args.config],
         "data": "synthetic (seeded, numpy default_rng)", "config": cfg,
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
     }

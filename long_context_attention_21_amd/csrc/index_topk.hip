@@ -667,6 +667,12 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
     if (want > kCap) want = kCap;
     S = (int)((maxnv + want - 1) / want);
   }
+  // Sparser than 1/32, kCap samples leave too few above the cut for a
+  // reliable count: the first sample then sets a low cut (about 4 x target
+  // entries above it) and a 4x denser second sample, filtered by that cut,
+  // sets the final one.
+  const bool two_stage = sampling && S >= 32;
+  const int target_a = two_stage ? 4 * target : target;
   if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = -__builtin_inff(); }
   if (tid == 0) { sm.fallback = 0; sm.ties = 0; }
   if (sampling) {
@@ -708,12 +714,81 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
       smask |= (i0 < nsj ? 1u : 0u) << m;
       kr[m] = i < nsj ? okey(sm.cand[grp_j][i].x) : 0u;
     }
-    int r = nsj > 0 ? (int)(((int64_t)target * nsj + nv[grp_j] - 1) / nv[grp_j]) : 0;
+    int r = nsj > 0 ? (int)(((int64_t)target_a * nsj + nv[grp_j] - 1) / nv[grp_j]) : 0;
     r = r < 1 ? 1 : (r > nsj ? nsj : r);
     // the cut need not be exact: a bin of up to r/16 samples is close enough
     const RadixOut ro = group_radix<QT, NS>(sm, kr, smask, (uint32_t)r, (uint32_t)nsj, nsj > 0, (uint32_t)(r >> 4));
     // never above the r-th sample; at least the order key of -inf
     if (nsj > 0 && grp_h == 0 && lane == 0) sm.thr[grp_j] = key_to_float(max(ro.T, 0x007fffffu));
+
+    if (two_stage) {
+      __syncthreads();  // first cuts visible; the sample buffers are free
+      float thr_a[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int j = jl0 + tt;
+        thr_a[tt] = (j < QT) ? sm.thr[j < QT ? j : 0] : 0.0f;
+        asm volatile("" : "+v"(thr_a[tt]));
+      }
+      // second sample (entries SB*i) filtered by the first cut into the
+      // wave-private regions of the token buffers
+      const int SB = S / 4;
+      const int ntile_b = ((maxnv + SB - 1) / SB + 31) / 32;
+      int wc2[2] = {0, 0};
+      BTile<FMT> t[kDepth];
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        t[u] = sc.load(SB * ((wave + u * kWaves) * 32 + l32));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int tile0 = wave; tile0 < ntile_b; tile0 += kDepth * kWaves) {
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+          const int tile = tile0 + u * kWaves;
+          const f32x16 C = sc.mfma(t[u]);
+          t[u] = sc.load(SB * ((tile + kDepth * kWaves) * 32 + l32));
+          float I[2];
+          sc.epilogue(C, I);
+          const int e = SB * (tile * 32 + l32);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            append_private<QT>(sm, e < nvl[tt] && I[tt] >= thr_a[tt], __float_as_uint(I[tt]), e, jl0 + tt, wc2[tt]);
+        }
+      }
+      if (l32 == 0) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          if (jl0 + tt < QT) sm.wcnt[wave][jl0 + tt] = wc2[tt];
+      }
+      __syncthreads();
+      // cut of the second sample among the kept ones (regions as in the final selection)
+      constexpr int kPer = kReg / 64;
+      uint32_t kb[NS];
+      uint32_t smb = 0u;
+      int kept = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) kept += min(sm.wcnt[w][grp_j], kReg);
+#pragma unroll
+      for (int rr = 0; rr < QT; ++rr) {
+        const int w = grp_h * QT + rr;
+        const int cw = min(sm.wcnt[w][grp_j], kReg);
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+          const int sl = rr * kPer + m;
+          const int pos = lane + 64 * m;
+          smb |= (64 * m < cw ? 1u : 0u) << sl;
+          const uint32_t x = sm.cand[grp_j][w * kReg + (pos < cw ? pos : 0)].x;
+          kb[sl] = pos < cw ? okey(x) : 0u;
+        }
+      }
+      const int nsb = nsj > 0 ? (nv[grp_j] + SB - 1) / SB : 0;
+      const int rb = nsb > 0 ? (int)(((int64_t)target * nsb + nv[grp_j] - 1) / nv[grp_j]) : 0;
+      // too few kept (the first cut was too high): keep the first cut
+      const bool act = nsj > 0 && rb >= 1 && kept >= rb;
+      const RadixOut rob = group_radix<QT, NS>(sm, kb, smb, (uint32_t)(rb < 1 ? 1 : rb), (uint32_t)kept, act,
+                                               (uint32_t)(rb >> 4));
+      if (act && grp_h == 0 && lane == 0) sm.thr[grp_j] = key_to_float(max(rob.T, 0x007fffffu));
+    }
   }
   __syncthreads();
 
