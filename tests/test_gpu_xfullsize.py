@@ -1,0 +1,134 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times (the same workload classes build the inputs and run the step).
+
+Where the oracle can recompute the whole output (compression) the check is
+bit-exact over every row; top-k and attention are checked on sampled query
+rows (the first, last and ragged rows included), top-k bit-exactly (MXFP4
+scores are exact), attention to max-abs 2e-2 / mean-rel 5e-3 against the
+fp64 oracle.
+"""
+import numpy as np
+import pytest
+
+from _helpers import assert_close, canon_idx
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _rows(n, count, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    r = set(int(x) for x in rng.choice(n, size=min(count, n), replace=False))
+    r.update(int(x) for x in extra if 0 <= x < n)
+    return np.array(sorted(r), np.int32)
+
+
+@pytest.mark.timeout(600)
+def test_config2_hca_full(orc):
+    import bench
+    wl = bench.HcaLayer(2)
+    wl.step()
+    torch.cuda.synchronize()
+    c = wl.c
+    ent, _ = orc.compress(c["kv"][0], c["beta"], wl.m, 0)
+    e_bits = orc.bf16_from_f32(ent)
+    assert np.array_equal(_bits(wl.bufs["entries"])[0], e_bits)
+    rows = _rows(wl.n, 96, 1, extra=(0, 1, 126, 127, 128, 255, 256, wl.n - 1))
+    ref = orc.attend_rows(c["q"][0], 0, orc.bf16_to_f64(e_bits), wl.m, rows, "hca", win=c["kv"][0],
+                          sink=c["sink"])
+    assert_close(_bits(wl.out)[0][rows], ref, "config 2 hca_attend")
+
+
+@pytest.mark.timeout(600)
+def test_config3_csa_full(orc):
+    import bench
+    wl = bench.CsaLayer(3)
+    wl.step()
+    torch.cuda.synchronize()
+    c = wl.c
+    ent, kid = orc.compress(c["kv"][0], c["beta"], 4, 1, ik=c["ik"][0])
+    e_bits = orc.bf16_from_f32(ent)
+    kc, ks = orc.mxfp4_encode(kid)
+    assert np.array_equal(_bits(wl.bufs["entries"])[0], e_bits)
+    assert np.array_equal(wl.bufs["kidx"].cpu().numpy()[0], kc)
+    assert np.array_equal(wl.bufs["kidx_scale"].cpu().numpy()[0], ks)
+    # rows around n_vis = k (8192), the fast path (n_vis <= k) and the end
+    rows = _rows(wl.n, 40, 2, extra=(0, 3, 8190, 8191, 8192, 8195, 65536, wl.n - 4, wl.n - 1))
+    qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(c["q_I"][0]).astype(np.float32))
+    ref_idx = orc.index_topk_rows(orc.mxfp4_decode(qc, qs), c["w_I"][0], orc.mxfp4_decode(kc, ks), 4, 0,
+                                  rows, wl.k)
+    got_idx = wl.idx.cpu().numpy()[0][rows]
+    bad = np.nonzero(~np.all(canon_idx(got_idx) == ref_idx, axis=1))[0]
+    assert bad.size == 0, "config 3 top-k rows %s differ" % rows[bad[:5]]
+    ref = orc.attend_rows(c["q"][0], 0, orc.bf16_to_f64(e_bits), 4, rows, "csa", idx=ref_idx, win=c["kv"][0],
+                          sink=c["sink"])
+    assert_close(_bits(wl.out)[0][rows], ref, "config 3 csa_attend")
+
+
+@pytest.mark.timeout(900)
+def test_config4_decode_full(orc):
+    import bench
+    wl = bench.DecodeLayer(4)
+    wl.step()
+    torch.cuda.synchronize()
+    c = wl.c
+    t = c["q_pos0"]
+    q = _bits(wl.q)
+    qI = _bits(wl.qI)
+    w = wl.w.cpu().numpy()
+    sink = wl.sink.cpu().numpy()
+    got_idx = wl.idx.cpu().numpy()
+    got_out = _bits(wl.out)
+    for b in (0, 21, 42, wl.B - 1):
+        kdec = orc.mxfp4_decode(wl.kc[b].cpu().numpy(), wl.ks[b].cpu().numpy())
+        E = orc.load_entries_fp8(wl.codes[b].cpu().numpy(), _bits(wl.rope[b]), wl.scale[b].cpu().numpy())
+        qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(qI[b]).astype(np.float32))
+        rows = np.zeros(1, np.int32)
+        ref_idx = orc.index_topk_rows(orc.mxfp4_decode(qc, qs), w[b], kdec, 4, t, rows, wl.k)
+        assert np.array_equal(canon_idx(got_idx[b]), ref_idx), "config 4 top-k of sequence %d differs" % b
+        ref = orc.attend_rows(q[b], t, E, 4, rows, "csa", idx=ref_idx, win=_bits(wl.swa[b]),
+                              win_pos0=c["win_pos0"], sink=sink)
+        assert_close(got_out[b], ref, "config 4 csa_attend (sequence %d)" % b)
+
+
+@pytest.mark.timeout(600)
+def test_config5_pair_full(orc):
+    import bench
+    wl = bench.PairLayer(5)
+    wl.step()
+    torch.cuda.synchronize()
+    cs, hs = wl.c["csa"], wl.c["hca"]
+    P, n = wl.P, wl.n
+    # the chunk's new entries (state of the previous block given)
+    ent_new, kid_new = orc.compress(cs["kv_new"], cs["beta"], 4, 1, pos0=P, ik=cs["ik_new"],
+                                    prev_kv=cs["state_kv"][124:], prev_ik=cs["state_ik"])
+    e_new = orc.bf16_from_f32(ent_new)
+    kn, ksn = orc.mxfp4_encode(kid_new)
+    assert np.array_equal(_bits(wl.c_ent)[0][wl.Nc0:], e_new)
+    assert np.array_equal(wl.c_kc.cpu().numpy()[0][wl.Nc0:], kn)
+    assert np.array_equal(wl.c_ks.cpu().numpy()[0][wl.Nc0:], ksn)
+    hent_new, _ = orc.compress(hs["kv_new"], hs["beta"], 128, 0, pos0=P)
+    h_new = orc.bf16_from_f32(hent_new)
+    assert np.array_equal(_bits(wl.h_ent)[0][wl.Nh0:], h_new)
+    # the given caches as the library stored them
+    kdec = orc.mxfp4_decode(wl.c_kc.cpu().numpy()[0], wl.c_ks.cpu().numpy()[0])
+    E = orc.bf16_to_f64(_bits(wl.c_ent)[0])
+    HE = orc.bf16_to_f64(_bits(wl.h_ent)[0])
+    rows = _rows(n, 24, 5, extra=(0, 1, 3, 4, 127, 128, n - 1))
+    qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(cs["q_I"]).astype(np.float32))
+    ref_idx = orc.index_topk_rows(orc.mxfp4_decode(qc, qs), cs["w_I"], kdec, 4, P, rows, wl.k)
+    got_idx = wl.idx.cpu().numpy()[0][rows]
+    bad = np.nonzero(~np.all(canon_idx(got_idx) == ref_idx, axis=1))[0]
+    assert bad.size == 0, "config 5 top-k rows %s differ" % rows[bad[:5]]
+    win_c = np.concatenate([cs["state_kv"], cs["kv_new"]])
+    ref = orc.attend_rows(cs["q"], P, E, 4, rows, "csa", idx=ref_idx, win=win_c, win_pos0=P - 128,
+                          sink=cs["sink"])
+    assert_close(_bits(wl.c_out)[0][rows], ref, "config 5 csa_attend")
+    win_h = np.concatenate([hs["state_kv"], hs["kv_new"]])
+    ref = orc.attend_rows(hs["q"], P, HE, 128, rows, "hca", win=win_h, win_pos0=P - 128, sink=hs["sink"])
+    assert_close(_bits(wl.h_out)[0][rows], ref, "config 5 hca_attend")
