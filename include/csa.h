@@ -133,7 +133,13 @@ int csa_compress(const void* kv, const void* ik, const float* z, const float* be
  *  H_I         1..8; d_idx = 64; 1 <= k <= 2048
  *  idx_out     [B, n, k] int32
  *  ws, ws_bytes  device scratch of at least csa_index_topk_workspace_bytes()
- *              bytes (may be NULL when that is 0)
+ *              bytes, 16-byte aligned (may be NULL when that is 0).  It is
+ *              non-zero for few query rows over long entry lists (n <= 4,
+ *              B*n <= 512, at least 65536 visible entries), where the entry
+ *              list is split over many work-groups: 32784 bytes per query
+ *              row.  Its contents need no initialisation and are undefined
+ *              after the call; calls that share a workspace must be ordered
+ *              on one stream.
  */
 int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* widx,
                    const void* kidx, const uint8_t* kidx_scale, int fmt,
@@ -141,6 +147,16 @@ int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* wid
                    int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
 size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m, int k);
+
+/*
+ * csa_index_topk_fallbacks -- diagnostic: the number of csa_index_topk
+ * work-groups on the current device that took the exact streaming path since
+ * the last reset (the sampled threshold left fewer than k or more than 4096
+ * candidates for one of their query rows, e.g. under massive score ties).
+ * Results are exact either way; the count only explains a slow call.
+ * Synchronises the device.  reset != 0 clears the counter after reading it.
+ */
+int csa_index_topk_fallbacks(uint64_t* count, int reset);
 
 /*
  * csa_attend -- CSA core attention: sparse entries + sliding window + sink.

@@ -14,7 +14,8 @@ import torch
 
 from ._lib import (FMT_BF16, FMT_FP8_ROPE_BF16, FMT_MXFP4, CsaError, check, lib)
 
-__all__ = ["csa_compress", "csa_index_topk", "csa_attend", "hca_attend", "version", "CsaError",
+__all__ = ["csa_compress", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend", "version",
+           "CsaError",
            "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16"]
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
@@ -96,6 +97,16 @@ def csa_index_topk(qidx, widx, kidx, k, m, q_pos0=0, fmt="mxfp4", qidx_scale=Non
         int(q_pos0), H_I, 64, N, m, k, _ptr(idx_out), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
     return idx_out
+
+
+def csa_index_topk_fallbacks(reset=False):
+    """Work-groups of csa_index_topk on the current device that took the
+    exact streaming path since the last reset (a diagnostic of slow calls;
+    results are exact either way).  Synchronises the device."""
+    import ctypes
+    c = ctypes.c_uint64(0)
+    check(lib().csa_index_topk_fallbacks(ctypes.byref(c), 1 if reset else 0))
+    return int(c.value)
 
 
 def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=128, sink=None,

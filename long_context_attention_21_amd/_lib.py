@@ -20,8 +20,8 @@ FMT_BF16 = 0
 FMT_MXFP4 = 1
 FMT_FP8_ROPE_BF16 = 2
 
-EXPORTS = ("csa_compress", "csa_index_topk", "csa_index_topk_workspace_bytes", "csa_attend",
-           "hca_attend", "csa_last_error", "csa_version")
+EXPORTS = ("csa_compress", "csa_index_topk", "csa_index_topk_workspace_bytes", "csa_index_topk_fallbacks",
+           "csa_attend", "hca_attend", "csa_last_error", "csa_version")
 
 
 class CsaError(RuntimeError):
@@ -48,11 +48,13 @@ def lib():
                                  sz, P]
     L.csa_index_topk_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.csa_index_topk_workspace_bytes.restype = sz
+    L.csa_index_topk_fallbacks.argtypes = [P, i32]
     L.csa_attend.argtypes = [P, i32, i32, i64, i32, i32, P, P, P, i32, i32, i32, P, i32, P, i64, i32,
                              i32, P, i32, f32, P, P]
     L.hca_attend.argtypes = [P, i32, i32, i64, i32, i32, P, i32, i32, P, i64, i32, i32, P, i32, f32,
                              P, P]
-    for f in ("csa_compress", "csa_index_topk", "csa_attend", "hca_attend", "csa_version"):
+    for f in ("csa_compress", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend",
+              "csa_version"):
         getattr(L, f).restype = i32
     L.csa_last_error.restype = C.c_char_p
     L.csa_last_error.argtypes = []

@@ -129,6 +129,14 @@ size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m
   return csa::index_topk_workspace(B, n, q_pos0, N, m, k);
 }
 
+int csa_index_topk_fallbacks(uint64_t* count, int reset) {
+  REQUIRE(count != nullptr, "csa_index_topk_fallbacks: count is NULL");
+  unsigned long long c = 0;
+  const int st = hip_status(csa::index_topk_fallbacks(&c, reset != 0), "csa_index_topk_fallbacks");
+  *count = (uint64_t)c;
+  return st;
+}
+
 int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* widx,
                    const void* kidx, const uint8_t* kidx_scale, int fmt, int B, int n,
                    int64_t q_pos0, int H_I, int d_idx, int N, int m, int k, int32_t* idx_out,
@@ -150,6 +158,7 @@ int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* wid
   const size_t need = csa::index_topk_workspace(B, n, q_pos0, N, m, k);
   if (ws_bytes < need)
     return fail(CSA_WORKSPACE_TOO_SMALL, "csa_index_topk: workspace of %zu bytes < %zu needed", ws_bytes, need);
+  REQUIRE(need == 0 || (ws != nullptr && aligned16(ws)), "csa_index_topk: ws must be non-NULL and 16-byte aligned");
   csa::IndexParams p{};
   p.q = qidx;
   p.q_scale = (fmt == CSA_FMT_MXFP4) ? qidx_scale : nullptr;

@@ -431,8 +431,9 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   const float LOG2E = 1.4426950408889634f;
   const int h0 = wave * NHT * 16;  // first head of this wave
 
-  // ---- the token's rotation (angle formed in fp64), the index row (CSA) and
-  // a zeroed ring (rows of missing keys stay finite)
+  // ---- the token's rotation (angle formed in fp64) and the index row (CSA).
+  // The ring needs no clearing: every chunk's loads rewrite all 32 rows (a
+  // missing key's row reads as zeros).
   if (tid < 32 && p.rope) {
     float cs, sn;
     rope_cs((double)t, p.rev[tid], cs, sn);
@@ -447,7 +448,6 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
       for (int i = tid; i < p.k; i += 64 * NW) Is[i] = irow[i];
     }
   }
-  for (int i = tid; i < kRing * 32 * 16; i += 64 * NW) ((u32x4*)&Ks[0][0])[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
   // ---- Q^T operand: lane l holds head h0 + ht*16 + l16, dims ks*32 + 8g .. +7

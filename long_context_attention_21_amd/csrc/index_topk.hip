@@ -528,43 +528,15 @@ __device__ __forceinline__ void append_private(TopkSmem<QT>& sm, bool pass, uint
   wcnt += lane < 32 ? plo : __builtin_popcount(hi);
 }
 
+// Scorer of a work-group's QT query tokens q0 .. q0+QT-1 of batch row b:
+// the MFMA A operand (rows = (token, head); MXFP4 quantised in-kernel from
+// bf16 q when no scales are given), the head weights, and the entry-key
+// buffer descriptors.  nvl[tt]: visible entries of this lane's token
+// jl0 + tt (0 for tokens past n).
 template <int QT, int FMT>
-__global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
-  __shared__ TopkSmem<QT> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nblk = (p.n + QT - 1) / QT;
-  const int b = blockIdx.x / nblk;
-  const int q0 = (nblk - 1 - (int)(blockIdx.x % nblk)) * QT;  // heavy (late) blocks first
+__device__ __forceinline__ void init_scorer(Scorer<FMT>& sc, const IndexParams& p, int b, int q0, int nvl[2]) {
+  const int lane = threadIdx.x & 63;
 
-  int nv[QT];
-  int maxnv = 0;
-  bool all_small = true;
-#pragma unroll
-  for (int j = 0; j < QT; ++j) {
-    const int q = q0 + j;
-    int v = 0;
-    if (q < p.n) {
-      const int64_t c = (p.q_pos0 + q + 1) / p.m;
-      v = (int)(c < p.N ? c : p.N);
-      if (v > p.k) all_small = false;
-    }
-    nv[j] = v;
-    maxnv = v > maxnv ? v : maxnv;
-  }
-  if (all_small) {
-#pragma unroll
-    for (int j = 0; j < QT; ++j) {
-      const int q = q0 + j;
-      if (q < p.n) {
-        int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
-        for (int i = tid; i < p.k; i += kThreads) o[i] = i < nv[j] ? i : -1;
-      }
-    }
-    return;
-  }
-
-  // ---- A operand: rows (token, head); lane row = lane % 32, k-block = lane / 32
-  Scorer<FMT> sc;
   {
     int arow_j, arow_h;
     row_to_token_head(lane & 31, arow_j, arow_h);
@@ -618,7 +590,6 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
     }
   }
   const int jl0 = 2 * (lane >> 5);
-  int nvl[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const int q = q0 + jl0 + tt;
@@ -651,6 +622,70 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
     sc.voff_k = (lane >> 5) * 16;
     sc.voff_s = lane >> 5;
   }
+}
+
+// Token groups that took the exact streaming fallback (this device), for
+// diagnostics: the sampled threshold normally leaves between k and kCap
+// candidates.
+__device__ unsigned long long g_fallbacks;
+
+// Workspace row of the split path (few query rows over long entry lists):
+// the row's threshold, then the candidates the partitions append.
+struct SplitRow {
+  int cnt;
+  float thr;
+  int pad[2];
+  uint2 cand[kCap];
+};
+
+// SPLIT 0: the whole selection.  SPLIT 1: only the threshold of each token
+// row, written to its workspace row.  SPLIT 2: the exact selection among the
+// candidates the partitions appended to the workspace row.
+template <int QT, int FMT, int SPLIT = 0>
+__global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
+  __shared__ TopkSmem<QT> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = (p.n + QT - 1) / QT;
+  const int b = blockIdx.x / nblk;
+  const int q0 = (nblk - 1 - (int)(blockIdx.x % nblk)) * QT;  // heavy (late) blocks first
+
+  int nv[QT];
+  int maxnv = 0;
+  bool all_small = true;
+#pragma unroll
+  for (int j = 0; j < QT; ++j) {
+    const int q = q0 + j;
+    int v = 0;
+    if (q < p.n) {
+      const int64_t c = (p.q_pos0 + q + 1) / p.m;
+      v = (int)(c < p.N ? c : p.N);
+      if (v > p.k) all_small = false;
+    }
+    nv[j] = v;
+    maxnv = v > maxnv ? v : maxnv;
+  }
+  SplitRow* srow = SPLIT != 0 ? (SplitRow*)p.ws + ((int64_t)b * p.n + q0) : nullptr;
+  if (all_small) {
+    if (SPLIT == 1) {  // nothing to score: the selection stage writes 0 .. n_vis-1
+      if (tid == 0) { srow->cnt = 0; srow->thr = __builtin_inff(); }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < QT; ++j) {
+      const int q = q0 + j;
+      if (q < p.n) {
+        int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
+        for (int i = tid; i < p.k; i += kThreads) o[i] = i < nv[j] ? i : -1;
+      }
+    }
+    return;
+  }
+
+  // ---- A operand: rows (token, head); lane row = lane % 32, k-block = lane / 32
+  Scorer<FMT> sc;
+  int nvl[2];
+  init_scorer<QT, FMT>(sc, p, b, q0, nvl);
+  const int jl0 = 2 * (lane >> 5);
   const int l32 = lane & 31;
   const int grp_j = wave % QT, grp_h = wave / QT;  // this wave's token group and member index
   constexpr int G = kWaves / QT;                    // waves per token group
@@ -675,7 +710,7 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
   const int target_a = two_stage ? 4 * target : target;
   if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = -__builtin_inff(); }
   if (tid == 0) { sm.fallback = 0; sm.ties = 0; }
-  if (sampling) {
+  if (SPLIT != 2 && sampling) {
     // sample tiles wave, wave + kWaves, ...; kDepth tiles in flight per wave
     const int ntile = ((maxnv + S - 1) / S + 31) / 32;
     BTile<FMT> t[kDepth];
@@ -693,6 +728,11 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
         t[u] = sc.load(S * ((tile + kDepth * kWaves) * 32 + l32));
         float I[2];
         sc.epilogue(C, I);
+        // The MFMA takes operands from all 64 lanes.  Its result must be used
+        // outside the lane-masked store below, or the compiler may move the
+        // MFMA and its operand set-up under that mask, where the masked-off
+        // lanes would feed stale registers.
+        asm volatile("" : "+v"(I[0]), "+v"(I[1]));
         const int i = tile * 32 + l32;
         const int e = S * i;
 #pragma unroll
@@ -791,45 +831,61 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
     }
   }
   __syncthreads();
-
-  // ---- phase 2: every entry scored once; candidates >= threshold appended
-  float thr2[2];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int j = jl0 + tt;
-    thr2[tt] = (j < QT) ? sm.thr[j < QT ? j : 0] : 0.0f;
-    // the LDS read completes here, not inside the scoring loop (whose LDS
-    // stores would otherwise be waited for on every tile)
-    asm volatile("" : "+v"(thr2[tt]));
+  if constexpr (SPLIT == 1) {
+    if (tid == 0) { srow->cnt = 0; srow->thr = sm.thr[0]; }
+    return;
   }
-  {
-    // kDepth tiles in flight per wave; each tile's registers are reloaded
-    // right after its MFMA has read them
-    const int ecol = wave * 32 + l32;
-    int wcnt[2] = {0, 0};
-    BTile<FMT> t[kDepth];
-#pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      t[u] = sc.load(u * kTile + ecol);
-      __builtin_amdgcn_sched_barrier(0);  // issue order = consumption order (tight waits)
+
+  if constexpr (SPLIT == 2) {
+    // ---- the candidates appended by the partitions, laid out as the regions
+    const int cnt = srow->cnt;
+    const int cc = cnt < kCap ? cnt : kCap;
+    for (int i = tid; i < cc; i += kThreads) sm.cand[0][i] = srow->cand[i];
+    if (tid < kWaves) {
+      const int c0 = cc - tid * kReg;
+      sm.wcnt[tid][0] = c0 < 0 ? 0 : (c0 > kReg ? kReg : c0);
     }
-    for (int base = 0; base < maxnv; base += kDepth * kTile) {
-#pragma unroll
-      for (int u = 0; u < kDepth; ++u) {  // unconditional: tiles past the end never pass
-        const f32x16 C = sc.mfma(t[u]);
-        t[u] = sc.load(base + (u + kDepth) * kTile + ecol);
-        const int e = base + u * kTile + ecol;
-        float I[2];
-        sc.epilogue(C, I);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          append_private<QT>(sm, e < nvl[tt] && I[tt] >= thr2[tt], __float_as_uint(I[tt]), e, jl0 + tt, wcnt[tt]);
+    if (tid == 0 && cnt > kCap) sm.fallback = 1;  // candidates were dropped
+  } else {
+  // ---- phase 2: every entry scored once; candidates >= threshold appended
+    float thr2[2];
+  #pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int j = jl0 + tt;
+      thr2[tt] = (j < QT) ? sm.thr[j < QT ? j : 0] : 0.0f;
+      // the LDS read completes here, not inside the scoring loop (whose LDS
+      // stores would otherwise be waited for on every tile)
+      asm volatile("" : "+v"(thr2[tt]));
+    }
+    {
+      // kDepth tiles in flight per wave; each tile's registers are reloaded
+      // right after its MFMA has read them
+      const int ecol = wave * 32 + l32;
+      int wcnt[2] = {0, 0};
+      BTile<FMT> t[kDepth];
+  #pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        t[u] = sc.load(u * kTile + ecol);
+        __builtin_amdgcn_sched_barrier(0);  // issue order = consumption order (tight waits)
       }
-    }
-    if (l32 == 0) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-        if (jl0 + tt < QT) sm.wcnt[wave][jl0 + tt] = wcnt[tt];
+      for (int base = 0; base < maxnv; base += kDepth * kTile) {
+  #pragma unroll
+        for (int u = 0; u < kDepth; ++u) {  // unconditional: tiles past the end never pass
+          const f32x16 C = sc.mfma(t[u]);
+          t[u] = sc.load(base + (u + kDepth) * kTile + ecol);
+          const int e = base + u * kTile + ecol;
+          float I[2];
+          sc.epilogue(C, I);
+  #pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            append_private<QT>(sm, e < nvl[tt] && I[tt] >= thr2[tt], __float_as_uint(I[tt]), e, jl0 + tt, wcnt[tt]);
+        }
+      }
+      if (l32 == 0) {
+  #pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          if (jl0 + tt < QT) sm.wcnt[wave][jl0 + tt] = wcnt[tt];
+      }
     }
   }
   __syncthreads();
@@ -848,6 +904,7 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
 
   if (sm.fallback) {
     // ---- exact streaming fallback for every token of this work-group
+    if (tid == 0) atomicAdd(&g_fallbacks, 1ull);
     if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = __uint_as_float(0u); }
     __syncthreads();
     for (int base = 0; base < maxnv; base += kTile) {
@@ -961,16 +1018,102 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
           const uint64_t bal = __ballot(kp);
           const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-          if (kp && pos + rank < p.k) o[pos + rank] = (int32_t)ir[sl];
+          if (SPLIT == 2) {
+            if (kp && pos + rank < kCap) sm.cand[0][pos + rank].y = ir[sl];  // staged for sorting
+          } else {
+            if (kp && pos + rank < p.k) o[pos + rank] = (int32_t)ir[sl];
+          }
           pos += __builtin_popcountll(bal);
         }
       }
-      for (int i = kk + grp_h * 64 + lane; i < p.k; i += G * 64) o[i] = -1;
+      if (SPLIT != 2)
+        for (int i = kk + grp_h * 64 + lane; i < p.k; i += G * 64) o[i] = -1;
+    }
+    if constexpr (SPLIT == 2) {
+      // the candidates arrived in atomic order: sort the kept indices so
+      // the output is the same on every run
+      __syncthreads();
+      wg_bitonic_sort(sm, 0, kk);
+      int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
+      for (int i = tid; i < p.k; i += kThreads) o[i] = i < kk ? (int32_t)sm.cand[0][i].y : -1;
     }
   }
 }
 
-size_t index_topk_workspace(int, int, int64_t, int, int, int) { return 0; }
+// Split path, partition stage: one work-group of 4 waves scores entries
+// [part*part_len, (part+1)*part_len) of one token row against the row's
+// threshold and appends the passing ones to the row's workspace candidates
+// (one atomic per wave and tile with a passing lane).
+template <int FMT>
+__global__ __launch_bounds__(256) void index_split_score_kernel(IndexParams p, int parts, int part_len) {
+  constexpr int W = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x / parts;
+  const int part = (int)(blockIdx.x % parts);
+  const int b = (int)(row / p.n), q = (int)(row % p.n);
+  SplitRow* srow = (SplitRow*)p.ws + row;
+  const float thr = srow->thr;
+  if (!(thr < __builtin_inff())) return;  // n_vis <= k: nothing to select
+  const int64_t c = (p.q_pos0 + q + 1) / p.m;
+  const int nv = (int)(c < p.N ? c : p.N);
+  const int e0 = part * part_len;
+  const int e1 = nv < e0 + part_len ? nv : e0 + part_len;
+  if (e0 >= e1) return;
+  Scorer<FMT> sc;
+  int nvl[2];
+  init_scorer<1, FMT>(sc, p, b, q, nvl);
+  const int l32 = lane & 31;
+  const int ntile = (e1 - e0 + 31) / 32;
+  BTile<FMT> t[kDepth];
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u) {
+    t[u] = sc.load(e0 + (wave + u * W) * 32 + l32);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int tile0 = wave; tile0 < ntile; tile0 += kDepth * W) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int tile = tile0 + u * W;
+      const f32x16 C = sc.mfma(t[u]);
+      t[u] = sc.load(e0 + (tile + kDepth * W) * 32 + l32);
+      float I[2];
+      sc.epilogue(C, I);
+      const int e = e0 + tile * 32 + l32;
+      const bool pass = lane < 32 && e < e1 && I[0] >= thr;  // token 0 lives in lanes 0..31
+      const uint64_t bal = __ballot(pass);
+      if (bal) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&srow->cnt, __builtin_popcountll(bal));
+        base = __builtin_amdgcn_readfirstlane(base);
+        const int rank = (int)__builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u);
+        if (pass && base + rank < kCap) srow->cand[base + rank] = make_uint2(__float_as_uint(I[0]), (uint32_t)e);
+      }
+    }
+  }
+}
+
+// Few query rows over long entry lists (decode): the split path keeps every
+// CU busy (threshold per row, entries scored by partitions, selection per row).
+constexpr int kSplitPart = 8192;
+static bool split_path(int B, int n, int64_t q_pos0, int N, int m) {
+  if (n > 4 || (int64_t)B * n > 512) return false;
+  int64_t nv = (q_pos0 + n) / m;
+  if (nv > N) nv = N;
+  return nv >= 65536;
+}
+
+hipError_t index_topk_fallbacks(unsigned long long* count, bool reset) {
+  hipError_t e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_fallbacks), sizeof(*count), 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && reset) {
+    const unsigned long long z = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_fallbacks), &z, sizeof(z), 0, hipMemcpyHostToDevice);
+  }
+  return e;
+}
+
+size_t index_topk_workspace(int B, int n, int64_t q_pos0, int N, int m, int) {
+  return split_path(B, n, q_pos0, N, m) ? (size_t)B * n * sizeof(SplitRow) : 0;
+}
 
 template <int QT>
 static hipError_t launch_q(const IndexParams& p, hipStream_t stream) {
@@ -983,8 +1126,22 @@ static hipError_t launch_q(const IndexParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int FMT>
+static hipError_t launch_split(const IndexParams& p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.B * p.n;
+  int64_t nv = (p.q_pos0 + p.n) / p.m;
+  if (nv > p.N) nv = p.N;
+  const int parts = (int)((nv + kSplitPart - 1) / kSplitPart);
+  hipLaunchKernelGGL((index_topk_kernel<1, FMT, 1>), dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((index_split_score_kernel<FMT>), dim3((unsigned)(rows * parts)), dim3(256), 0, stream, p,
+                     parts, kSplitPart);
+  hipLaunchKernelGGL((index_topk_kernel<1, FMT, 2>), dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream) {
   if ((int64_t)p.B * p.n == 0) return hipSuccess;
+  if (split_path(p.B, p.n, p.q_pos0, p.N, p.m)) return p.fmt == 1 ? launch_split<1>(p, stream) : launch_split<0>(p, stream);
   if (p.n == 1) return launch_q<1>(p, stream);
   return launch_q<4>(p, stream);
 }

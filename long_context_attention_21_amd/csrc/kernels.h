@@ -68,5 +68,6 @@ struct IndexParams {
 
 hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream);
 size_t index_topk_workspace(int B, int n, int64_t q_pos0, int N, int m, int k);
+hipError_t index_topk_fallbacks(unsigned long long* count, bool reset);
 
 }  // namespace csa

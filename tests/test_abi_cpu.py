@@ -119,6 +119,20 @@ def test_index_rejects(L, kw, needle):
 
 def test_index_workspace_query(L):
     assert L.csa_index_topk_workspace_bytes(1, 16, 0, 4, 4, 16) == 0
+    # split path: few query rows over >= 65536 visible entries, one 32784-byte row each
+    assert L.csa_index_topk_workspace_bytes(64, 1, 4 * 262144, 262144, 4, 2048) == 64 * 32784
+    assert L.csa_index_topk_workspace_bytes(2, 4, 4 * 70000 - 4, 90000, 4, 2048) == 8 * 32784
+    assert L.csa_index_topk_workspace_bytes(1, 5, 4 * 70000, 90000, 4, 2048) == 0     # too many rows
+    assert L.csa_index_topk_workspace_bytes(64, 1, 4 * 60000, 262144, 4, 2048) == 0  # too few visible
+
+
+def test_index_rejects_small_or_misaligned_workspace(L):
+    need = L.csa_index_topk_workspace_bytes(1, 1, 4 * 70000, 70000, 4, 512)
+    base = dict(B=1, n=1, q_pos0=4 * 70000, N=70000, k=512)
+    assert _index(L, **base, ws=FAKE, ws_bytes=need - 1) == _lib.CSA_WORKSPACE_TOO_SMALL
+    assert _index(L, **base, ws=MIS, ws_bytes=need) == _lib.CSA_INVALID_ARG
+    assert "ws must be" in _msg(L)
+    assert _index(L, **base, ws=None, ws_bytes=need) == _lib.CSA_INVALID_ARG
 
 
 def _attend(L, **kw):

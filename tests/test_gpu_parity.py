@@ -82,7 +82,7 @@ def test_compress_chunked_with_prev_rows(orc):
 # ------------------------------------------------------------------- indexer --
 
 def _index_case(orc, rng, B, n, N, H_I, k, q_pos0, fmt, m=4, dup_rows=0, prequant=False,
-                key_scale=1.0):
+                key_scale=1.0, fallback=False):
     q = _bf16(rng, (B, n, H_I, 64), 1 / 8)
     w = (rng.standard_normal((B, n, H_I)) / np.sqrt(H_I)).astype(np.float32)
     kf = (rng.standard_normal((B, N, 64)) * key_scale / 8).astype(np.float32)
@@ -97,6 +97,7 @@ def _index_case(orc, rng, B, n, N, H_I, k, q_pos0, fmt, m=4, dup_rows=0, prequan
         kdec = orc.bf16_to_f64(kc).astype(np.float32)
         kdev, ksdev = dev(kc), None
     qdec = oracle_q_dec(orc, q, fmt)
+    L.csa_index_topk_fallbacks(reset=True)
     if prequant:
         qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(q).astype(np.float32))
         got = L.csa_index_topk(dev(qc), dev(w), kdev, k, m, q_pos0=q_pos0, fmt=fmt,
@@ -104,6 +105,11 @@ def _index_case(orc, rng, B, n, N, H_I, k, q_pos0, fmt, m=4, dup_rows=0, prequan
     else:
         got = L.csa_index_topk(dev(q), dev(w), kdev, k, m, q_pos0=q_pos0, fmt=fmt, kidx_scale=ksdev)
     torch.cuda.synchronize()
+    nfb = L.csa_index_topk_fallbacks()
+    # the sampled threshold leaves between k and 4096 candidates on untied
+    # scores; the exact streaming path is for massive ties only
+    if fallback is not None:
+        assert (nfb > 0) == fallback, "%d work-groups took the exact streaming path" % nfb
     got = host(got)
     rows = np.arange(n, dtype=np.int32)
     for b in range(B):
@@ -124,13 +130,19 @@ def _index_case(orc, rng, B, n, N, H_I, k, q_pos0, fmt, m=4, dup_rows=0, prequan
 @pytest.mark.parametrize("B,n,N,H_I,k,q_pos0,fmt,extra", [
     (2, 301, 75, 8, 16, 0, "mxfp4", {}),             # fast path + selection, ragged tail
     (1, 37, 20000, 8, 2048, 80000 - 37, "mxfp4", {}),  # several exact shrinks per token
-    (1, 50, 3000, 8, 64, 12000, "mxfp4", {"dup_rows": 40}),  # massive exact ties
-    (1, 40, 20000, 8, 2048, 80000 - 40, "mxfp4", {"dup_rows": 3}),  # ties overflow -> exact fallback
+    (1, 50, 3000, 8, 64, 12000, "mxfp4", {"dup_rows": 40, "fallback": None}),  # massive exact ties
+    (1, 40, 20000, 8, 2048, 80000 - 40, "mxfp4", {"dup_rows": 3, "fallback": True}),  # ties overflow -> exact path
     (1, 41, 9000, 8, 2048, 36000 - 41, "mxfp4", {}),  # sampled threshold, stride 3
     (3, 1, 20000, 8, 2048, 80000, "mxfp4", {}),       # decode path, one token per sequence
     (1, 64, 2000, 8, 100, 8000, "mxfp4", {"prequant": True}),
     (1, 301, 75, 4, 16, 0, "bf16", {}),               # bf16 indexer, 4 heads
     (1, 40, 5000, 1, 300, 20000, "bf16", {}),
+    # split path (few query rows over >= 65536 visible entries): threshold per
+    # row, partitions append candidates, selection per row
+    (3, 1, 70000, 8, 512, 280000, "mxfp4", {}),          # ragged last partition
+    (2, 4, 90000, 8, 2048, 280000 - 4, "mxfp4", {}),     # entries past the causal bound
+    (1, 2, 70000, 8, 512, 280000, "mxfp4", {"dup_rows": 3, "fallback": True}),  # candidates overflow
+    (2, 1, 66000, 4, 300, 264000, "bf16", {}),
 ])
 def test_index_topk_matches_oracle(orc, B, n, N, H_I, k, q_pos0, fmt, extra):
     print("index case B=%d n=%d N=%d H_I=%d k=%d pos0=%d %s %s" % (B, n, N, H_I, k, q_pos0, fmt, extra),

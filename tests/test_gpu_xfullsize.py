@@ -48,7 +48,10 @@ def test_config2_hca_full(orc):
 def test_config3_csa_full(orc):
     import bench
     wl = bench.CsaLayer(3)
+    import long_context_attention_21_amd as L
+    L.csa_index_topk_fallbacks(reset=True)
     wl.step()
+    assert L.csa_index_topk_fallbacks() == 0, "indexer took the exact streaming path"
     torch.cuda.synchronize()
     c = wl.c
     ent, kid = orc.compress(c["kv"][0], c["beta"], 4, 1, ik=c["ik"][0])
@@ -74,7 +77,10 @@ def test_config3_csa_full(orc):
 def test_config4_decode_full(orc):
     import bench
     wl = bench.DecodeLayer(4)
+    import long_context_attention_21_amd as L
+    L.csa_index_topk_fallbacks(reset=True)
     wl.step()
+    assert L.csa_index_topk_fallbacks() == 0, "indexer took the exact streaming path"
     torch.cuda.synchronize()
     c = wl.c
     t = c["q_pos0"]
@@ -100,7 +106,15 @@ def test_config4_decode_full(orc):
 def test_config5_pair_full(orc):
     import bench
     wl = bench.PairLayer(5)
+    import long_context_attention_21_amd as L
+    L.csa_index_topk_fallbacks(reset=True)
     wl.step()
+    # a few query rows whose head weights are (nearly) all negative have their
+    # k-th score on the point mass of exact zeros (every head's dot product
+    # <= 0): the cut then keeps more than a wave region holds and those work
+    # groups take the exact path (2,048 work-groups of 4 rows here)
+    nfb = L.csa_index_topk_fallbacks()
+    assert nfb <= 8, "%d indexer work-groups took the exact streaming path" % nfb
     torch.cuda.synchronize()
     cs, hs = wl.c["csa"], wl.c["hca"]
     P, n = wl.P, wl.n
