@@ -35,9 +35,9 @@ PEAK = {"bf16": 2500.0, "fp4": 10100.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s
 # sha256 of the kernel source they were taken on: a changed kernel reports
 # null until it is measured again.
 TRAFFIC = {  # profiles/csa_prefill_128k_hbm_counters.txt
-    ("csa_attend", 3): {"sha256": "9eea36c3279a74f73dae90780ffc27f42e859a4a1dc7597a592f457362a2c3c5",
-                        "bytes": 1.852e10},
-    ("csa_index_topk", 3): {"sha256": "ea442c78d7fa3476a387827a409882b532a752cc74ff43be7668878dfc8062eb",
+    ("csa_attend", 3): {"sha256": "9a4a5819b599698cd5536b5362ca364b5962b86ea45f212a615147278fc6dff7",
+                        "bytes": 1.843e10},
+    ("csa_index_topk", 3): {"sha256": "268f5e31237b685af9460a786f4112011eb8dba1e2d29d683d785ceabf0e60f4",
                             "bytes": 1.219e9},
     ("csa_compress", 3): {"sha256": "82c3e1fea99ff0128101cd4a89cfefe6bb708f379c3a3e689974d4dc357c12da",
                           "bytes": 7.279e7},
