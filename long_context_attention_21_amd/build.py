@@ -26,7 +26,9 @@ SOURCES = {
     "compress.hip": DEVICE + ["-ffp-contract=off"],
     # no NaN ever reaches these kernels: non-IEEE mode drops the NaN
     # canonicalisation that IEEE-mode max/min would otherwise add
-    "attend.hip": DEVICE + ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    # MFMA results in VGPRs: the scores feed the exponentials directly and the
+    # accumulators need no copies out of AGPRs
+    "attend.hip": DEVICE + ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     # the score MFMA result feeds VALU code directly: keep it in VGPRs
     "index_topk.hip": DEVICE + ["-ffp-contract=off", "-fno-honor-nans", "-mno-amdgpu-ieee",
                                 "-mllvm", "-amdgpu-mfma-vgpr-form"],

@@ -524,11 +524,18 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     int rows[QPW];
     const int kb0 = c * 32 + 8 * hq + wave * QPW;  // key of this lane's first row
     if (c < n_ent_chunks) {
+      if constexpr (MODE == 0) {
+        // kb0 is a multiple of 4 and kb0 + QPW <= 32 * n_ent_chunks <= kMaxK:
+        // 16-byte reads inside the index row (entries past k are not used)
 #pragma unroll
-      for (int e = 0; e < QPW; ++e) {
-        const int kk = kb0 + e;
-        if (MODE == 0) rows[e] = kk < p.k ? Is[kk] : -1;
-        else rows[e] = kk < n_ent ? kk : -1;
+        for (int e0 = 0; e0 < QPW; e0 += 4) {
+          const u32x4 v = *(const u32x4*)&Is[kb0 + e0];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rows[e0 + e] = kb0 + e0 + e < p.k ? (int)v[e] : -1;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < QPW; ++e) rows[e] = kb0 + e < n_ent ? kb0 + e : -1;
       }
     } else {
 #pragma unroll

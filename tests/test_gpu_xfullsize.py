@@ -51,7 +51,11 @@ def test_config3_csa_full(orc):
     import long_context_attention_21_amd as L
     L.csa_index_topk_fallbacks(reset=True)
     wl.step()
-    assert L.csa_index_topk_fallbacks() == 0, "indexer took the exact streaming path"
+    # rows whose k-th score falls on the point mass of exact zeros (every head
+    # product <= 0 under mostly negative head weights) may take the exact
+    # path: allow one work-group in 4096 (30,720 work-groups here)
+    nfb = L.csa_index_topk_fallbacks()
+    assert nfb <= 8, "%d indexer work-groups took the exact streaming path" % nfb
     torch.cuda.synchronize()
     c = wl.c
     ent, kid = orc.compress(c["kv"][0], c["beta"], 4, 1, ik=c["ik"][0])
@@ -112,7 +116,7 @@ def test_config5_pair_full(orc):
     # a few query rows whose head weights are (nearly) all negative have their
     # k-th score on the point mass of exact zeros (every head's dot product
     # <= 0): the cut then keeps more than a wave region holds and those work
-    # groups take the exact path (2,048 work-groups of 4 rows here)
+    # groups take the exact path (2,048 work-groups of 4 rows here; 3 seen)
     nfb = L.csa_index_topk_fallbacks()
     assert nfb <= 8, "%d indexer work-groups took the exact streaming path" % nfb
     torch.cuda.synchronize()
