@@ -256,7 +256,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   auto scores = [&](const ChunkRegs& R, f32x4 S[2][NHT], uint32_t vmask[2], int buf) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      vmask[kt] = (uint32_t)(__ballot(R.v[kt]) & 0xffffull);
+      vmask[kt] = (uint32_t)(__builtin_amdgcn_ballot_w64(R.v[kt]) & 0xffffull);
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) S[kt][ht] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
                        fmaxf(fmaxf(S[1][ht][0], S[1][ht][1]), fmaxf(S[1][ht][2], S[1][ht][3])));
         over |= lm[ht] > mref[ht] + kSlack;
       }
-      if (__ballot(over)) {
+      if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) mref[ht] = fmaxf(mref[ht], max_over_groups(lm[ht]));
         again = true;
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     } else if (c < n_chunks) {
       v = (c - n_ent_chunks) * 32 + kk < n_wk;
     }
-    return (uint32_t)__ballot(v && lane < 32);
+    return (uint32_t)__builtin_amdgcn_ballot_w64(v && lane < 32);
   };
   // true on every wave if `mine` is true on some wave (flags double-buffered by `par`)
   int par = 0;
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     bool bad = false;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) bad |= !(Lacc[ht][0] < 0x1p100f && Lacc[ht][0] >= 0x1p-100f);
-    return any_wave(__ballot(bad) != 0);
+    return any_wave(__builtin_amdgcn_ballot_w64(bad) != 0);
   };
   // max-only pass: mref = max(sink logit, every valid score) per head
   auto run_max = [&]() {

@@ -52,6 +52,9 @@ constexpr int kDepth = 4;              // score tiles in flight per wave
 constexpr int kMinAbove = 256;         // sampled entries expected above the threshold
 constexpr int kList = 512;             // per-member key list after the first radix digit
 
+// Lane mask of a predicate (the compare result itself, no int round trip).
+__device__ __forceinline__ uint64_t ballot(bool pred) { return __builtin_amdgcn_ballot_w64(pred); }
+
 __device__ __forceinline__ uint32_t okey(uint32_t fbits) {
   return (fbits & 0x80000000u) ? ~fbits : (fbits | 0x80000000u);
 }
@@ -218,7 +221,7 @@ __device__ __forceinline__ RadixOut group_radix(TopkSmem<QT>& sm, const uint32_t
       const u32x4 hv = *(const u32x4*)(hc + 252 - 4 * lane);
       const uint32_t c = hv[0] + hv[1] + hv[2] + hv[3];
       const uint32_t incl = wave_prefix_sum(c);
-      const int L = __builtin_ctzll(__ballot(incl >= r_left));
+      const int L = __builtin_ctzll(ballot(incl >= r_left));
       uint32_t acc = incl - c, d = 0u, hd = 0u;
       if (lane == L) {
         d = 252 - 4 * lane;
@@ -252,7 +255,7 @@ __device__ __forceinline__ RadixOut group_radix(TopkSmem<QT>& sm, const uint32_t
           for (int m = 0; m < NS; ++m) {
             if ((smask >> m) & 1u) {
               const bool in = ((max(kr[m], base) - base) >> lo) - pb == d;
-              const uint64_t bal = __ballot(in);
+              const uint64_t bal = ballot(in);
               const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
               if (in) list[lcnt + rank] = kr[m];
@@ -267,7 +270,7 @@ __device__ __forceinline__ RadixOut group_radix(TopkSmem<QT>& sm, const uint32_t
             const int i = s0 + lane;
             const uint32_t key = i < lcnt ? list[i] : 0u;
             const bool in = i < lcnt && ((max(key, base) - base) >> lo) - pb == d;
-            const uint64_t bal = __ballot(in);
+            const uint64_t bal = ballot(in);
             const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
             if (in) list[nc + rank] = key;
@@ -318,7 +321,7 @@ __device__ uint32_t wg_radix_select(uint32_t* hist, uint32_t* sel, int cnt, uint
         const uint32_t o = (uint32_t)__shfl_down((int)suf, off);
         if (lane + off < 64) suf += o;
       }
-      const uint64_t bal = __ballot(suf >= r_left);
+      const uint64_t bal = ballot(suf >= r_left);
       const int L = 63 - __builtin_clzll(bal);
       if (lane == L) {
         uint32_t acc = suf - c;
@@ -499,7 +502,7 @@ __device__ __forceinline__ void append(TopkSmem<QT>& sm, const bool pass[2], con
   const uint64_t halfmask = (lane < 32) ? 0x00000000ffffffffull : 0xffffffff00000000ull;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const uint64_t mine = __ballot(pass[tt]) & halfmask;
+    const uint64_t mine = ballot(pass[tt]) & halfmask;
     const int pc = __builtin_popcountll(mine);
     const int rank = __builtin_popcountll(mine & ((1ull << lane) - 1ull));
     const int j = jl0 + tt;
@@ -515,17 +518,18 @@ __device__ __forceinline__ void append(TopkSmem<QT>& sm, const bool pass[2], con
 // region of the token's buffer.  The running count wcnt is uniform over the
 // half-wave and lives in a register: no LDS atomic, no cross-lane round trip.
 template <int QT>
-__device__ __forceinline__ void append_private(TopkSmem<QT>& sm, bool pass, uint32_t val, int e, int j, int& wcnt) {
+__device__ __forceinline__ void append_private(TopkSmem<QT>& sm, bool vis, bool ge, uint32_t val, int e, int j,
+                                               int& wcnt) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const uint64_t bal = __ballot(pass);
+  // the two compares' lane masks, combined on the scalar unit
+  const uint64_t bal = ballot(vis) & ballot(ge);
   const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
-  const int plo = __builtin_popcount(lo);
-  // passing lanes below this one in the whole wave, minus the lower half for upper-half lanes
-  const int rank = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u)) - (lane < 32 ? 0 : plo);
-  const int pos = wcnt + rank;
-  if (pass && pos < kReg) sm.cand[j][wave * kReg + pos] = make_uint2(val, (uint32_t)e);
-  wcnt += lane < 32 ? plo : __builtin_popcount(hi);
+  // position = count + passing lanes below this one in its half-wave: the
+  // lower half counts bits of lo, the upper half bits of hi
+  const int pos = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lane < 32 ? lo : 0u, (uint32_t)wcnt));
+  if (vis && ge && pos < kReg) sm.cand[j][wave * kReg + pos] = make_uint2(val, (uint32_t)e);
+  wcnt += __builtin_popcount(lane < 32 ? lo : hi);
 }
 
 // Scorer of a work-group's QT query tokens q0 .. q0+QT-1 of batch row b:
@@ -792,7 +796,7 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
           const int e = SB * (tile * 32 + l32);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
-            append_private<QT>(sm, e < nvl[tt] && I[tt] >= thr_a[tt], __float_as_uint(I[tt]), e, jl0 + tt, wc2[tt]);
+            append_private<QT>(sm, e < nvl[tt], I[tt] >= thr_a[tt], __float_as_uint(I[tt]), e, jl0 + tt, wc2[tt]);
         }
       }
       if (l32 == 0) {
@@ -878,7 +882,7 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
           sc.epilogue(C, I);
   #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
-            append_private<QT>(sm, e < nvl[tt] && I[tt] >= thr2[tt], __float_as_uint(I[tt]), e, jl0 + tt, wcnt[tt]);
+            append_private<QT>(sm, e < nvl[tt], I[tt] >= thr2[tt], __float_as_uint(I[tt]), e, jl0 + tt, wcnt[tt]);
         }
       }
       if (l32 == 0) {
@@ -1001,7 +1005,7 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
     for (int rr = 0; rr < QT; ++rr) {
       int cnt = 0;
 #pragma unroll
-      for (int m = 0; m < kPer; ++m) cnt += __builtin_popcountll(__ballot((keep >> (rr * kPer + m)) & 1u));
+      for (int m = 0; m < kPer; ++m) cnt += __builtin_popcountll(ballot((keep >> (rr * kPer + m)) & 1u));
       if (lane == 0) sm.kept[j][grp_h * QT + rr] = cnt;
     }
     __syncthreads();
@@ -1015,7 +1019,7 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
         for (int m = 0; m < kPer; ++m) {
           const int sl = rr * kPer + m;
           const bool kp = (keep >> sl) & 1u;
-          const uint64_t bal = __ballot(kp);
+          const uint64_t bal = ballot(kp);
           const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
           if (SPLIT == 2) {
@@ -1080,7 +1084,7 @@ __global__ __launch_bounds__(256) void index_split_score_kernel(IndexParams p, i
       sc.epilogue(C, I);
       const int e = e0 + tile * 32 + l32;
       const bool pass = lane < 32 && e < e1 && I[0] >= thr;  // token 0 lives in lanes 0..31
-      const uint64_t bal = __ballot(pass);
+      const uint64_t bal = ballot(pass);
       if (bal) {
         int base = 0;
         if (lane == 0) base = atomicAdd(&srow->cnt, __builtin_popcountll(bal));
