@@ -109,6 +109,45 @@ int csa_compress(const void* kv, const void* ik, const float* z, const float* be
                  void* stream);
 
 /*
+ * csa_cache_append -- decode cache write path: one new token per sequence.
+ * Wiki summary, Training infrastructure item 5 (inference keeps a state cache
+ * of recent raw tokens and a compressed cache: RoPE dims BF16, other dims
+ * FP8) and Proposed method item 1 (an entry every m tokens).  The new row of
+ * position t is stored in the state rings; if t completes block i (t + 1 =
+ * (i+1)m), entry i is pooled exactly as csa_compress pools it (same
+ * weights, order, RoPE at p_i = t and storage codes, so the caches are
+ * byte-identical to a whole-sequence csa_compress) and written to row i.
+ *
+ *  kv_new    [B, 128] bf16 raw (pre-RoPE) row of position t
+ *  ik_new    [B, 64] bf16 indexer-stream row, or NULL (no indexer, e.g. HCA)
+ *  z_new     [B, 2] fp32 slot-logit offsets of the row, or NULL (z = 0)
+ *  t         position of the new rows (the same for every sequence)
+ *  kv_ring   [B, 2W, 128] bf16 state ring: row j sits at slots j % W and
+ *            j % W + W, so the window rows max(0, t-W+1) .. t are contiguous
+ *            from slot s0 = max(0, t-W+1) % W.  csa_attend / hca_attend can
+ *            read it directly as win_kv with win_len = 2W and win_pos0 =
+ *            max(0, t-W+1) - s0.
+ *  ik_ring   [B, W, 64] bf16 (slot j % W), with ik_new, else NULL
+ *  z_ring    [B, W, 2] fp32 (slot j % W), with z_new, else NULL
+ *  W         ring length in rows, >= L (2m with overlap, else m); 128 holds
+ *            the sliding window
+ *  beta, m, overlap, rope_dims, rope_base: as csa_compress
+ *  entries, entries_rope, entry_scale, entry_fmt, kidx, kidx_scale,
+ *  kidx_fmt: the caches, as csa_compress's outputs but with N_cap rows per
+ *            sequence (entry i of sequence b at row b * N_cap + i)
+ * The rings must hold the rows of the L - 1 positions before t (earlier
+ * calls, or a prefill that filled them the same way).  Cache arguments may be
+ * NULL on calls that complete no block.  Calls for one sequence must be
+ * ordered on one stream.  Returns CSA_INVALID_ARG for a bad shape, W < L, or
+ * an entry index >= N_cap.
+ */
+int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new, int B, int64_t t,
+                     void* kv_ring, void* ik_ring, float* z_ring, int W, const float* beta, int m,
+                     int overlap, int rope_dims, float rope_base, void* entries, void* entries_rope,
+                     float* entry_scale, int entry_fmt, void* kidx, uint8_t* kidx_scale, int kidx_fmt,
+                     int N_cap, void* stream);
+
+/*
  * csa_index_topk -- Lightning Indexer scores and per-query top-k selection.
  * Wiki summary item 1 (indexer scores in FP4), "deepseek V4 技术论文" 1.1
  * (low-rank + FP4 indexer selects the top-k entries per query token),

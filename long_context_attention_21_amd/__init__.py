@@ -14,7 +14,7 @@ import torch
 
 from ._lib import (FMT_BF16, FMT_FP8_ROPE_BF16, FMT_MXFP4, CsaError, check, lib)
 
-__all__ = ["csa_compress", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend", "version",
+__all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend", "version",
            "CsaError",
            "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16"]
 
@@ -77,6 +77,24 @@ def csa_compress(kv, beta, m, overlap, pos0=0, ik=None, z=None, prev_kv=None, pr
         _ptr(out.get("entry_scale")), ef, _ptr(out.get("kidx")), _ptr(out.get("kidx_scale")), kf,
         _stream(stream)))
     return out
+
+
+def csa_cache_append(kv_new, beta, m, overlap, t, kv_ring, caches, ik_new=None, ik_ring=None,
+                     z_new=None, z_ring=None, rope_dims=64, rope_base=10000.0, entry_fmt="bf16",
+                     kidx_fmt="mxfp4", stream=None):
+    """Decode write path: kv_new [B, 128] (ik_new [B, 64], z_new [B, 2]) of
+    position t into the rings kv_ring [B, 2W, 128] (ik_ring [B, W, 64],
+    z_ring [B, W, 2]); the block it completes, if any, into ``caches``
+    (entries [B, N_cap, ...], entries_rope, entry_scale, kidx, kidx_scale)."""
+    B = kv_new.shape[0]
+    W = kv_ring.shape[1] // 2
+    ents = caches.get("entries")
+    N_cap = 0 if ents is None else ents.shape[1]
+    check(lib().csa_cache_append(
+        _ptr(kv_new), _ptr(ik_new), _ptr(z_new), B, int(t), _ptr(kv_ring), _ptr(ik_ring), _ptr(z_ring), W,
+        _ptr(beta), m, int(overlap), rope_dims, float(rope_base), _ptr(ents), _ptr(caches.get("entries_rope")),
+        _ptr(caches.get("entry_scale")), _fmt(entry_fmt), _ptr(caches.get("kidx")), _ptr(caches.get("kidx_scale")),
+        _fmt(kidx_fmt), N_cap, _stream(stream)))
 
 
 def csa_index_topk(qidx, widx, kidx, k, m, q_pos0=0, fmt="mxfp4", qidx_scale=None,

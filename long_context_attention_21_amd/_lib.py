@@ -20,8 +20,8 @@ FMT_BF16 = 0
 FMT_MXFP4 = 1
 FMT_FP8_ROPE_BF16 = 2
 
-EXPORTS = ("csa_compress", "csa_index_topk", "csa_index_topk_workspace_bytes", "csa_index_topk_fallbacks",
-           "csa_attend", "hca_attend", "csa_last_error", "csa_version")
+EXPORTS = ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_workspace_bytes",
+           "csa_index_topk_fallbacks", "csa_attend", "hca_attend", "csa_last_error", "csa_version")
 
 
 class CsaError(RuntimeError):
@@ -44,6 +44,8 @@ def lib():
     P, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
     L.csa_compress.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, i32, f32,
                                P, P, P, i32, P, P, i32, P]
+    L.csa_cache_append.argtypes = [P, P, P, i32, i64, P, P, P, i32, P, i32, i32, i32, f32, P, P, P, i32, P, P,
+                                   i32, i32, P]
     L.csa_index_topk.argtypes = [P, P, P, P, P, i32, i32, i32, i64, i32, i32, i32, i32, i32, P, P,
                                  sz, P]
     L.csa_index_topk_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
@@ -53,8 +55,8 @@ def lib():
                              i32, P, i32, f32, P, P]
     L.hca_attend.argtypes = [P, i32, i32, i64, i32, i32, P, i32, i32, P, i64, i32, i32, P, i32, f32,
                              P, P]
-    for f in ("csa_compress", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend",
-              "csa_version"):
+    for f in ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend",
+              "hca_attend", "csa_version"):
         getattr(L, f).restype = i32
     L.csa_last_error.restype = C.c_char_p
     L.csa_last_error.argtypes = []

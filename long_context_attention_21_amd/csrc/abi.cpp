@@ -125,6 +125,75 @@ int csa_compress(const void* kv, const void* ik, const float* z, const float* be
   return hip_status(csa::launch_compress(p, (hipStream_t)stream), "csa_compress launch");
 }
 
+int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new, int B, int64_t t,
+                     void* kv_ring, void* ik_ring, float* z_ring, int W, const float* beta, int m,
+                     int overlap, int rope_dims, float rope_base, void* entries, void* entries_rope,
+                     float* entry_scale, int entry_fmt, void* kidx, uint8_t* kidx_scale, int kidx_fmt,
+                     int N_cap, void* stream) {
+  REQUIRE(B >= 0, "csa_cache_append: B=%d must be >= 0", B);
+  REQUIRE(t >= 0, "csa_cache_append: t must be >= 0");
+  REQUIRE(m >= 1 && m <= 128, "csa_cache_append: m=%d must be in [1, 128]", m);
+  REQUIRE(overlap == 0 || overlap == 1, "csa_cache_append: overlap=%d must be 0 or 1", overlap);
+  const int L = overlap ? 2 * m : m;
+  REQUIRE(W >= L && W <= 4096, "csa_cache_append: W=%d must be in [%d, 4096] (the pooled rows must be in the ring)",
+          W, L);
+  REQUIRE(rope_dims == 0 || rope_dims == 64, "csa_cache_append: rope_dims=%d must be 0 or 64", rope_dims);
+  REQUIRE(rope_dims == 0 || (std::isfinite(rope_base) && rope_base > 1.0f),
+          "csa_cache_append: rope_base must be finite and > 1");
+  REQUIRE(N_cap >= 0, "csa_cache_append: N_cap=%d must be >= 0", N_cap);
+  if (B == 0) return ok();
+  REQUIRE(kv_new && kv_ring && beta, "csa_cache_append: kv_new, kv_ring and beta must be non-NULL");
+  REQUIRE((ik_new == nullptr) == (ik_ring == nullptr), "csa_cache_append: ik_new and ik_ring go together");
+  REQUIRE((z_new == nullptr) == (z_ring == nullptr), "csa_cache_append: z_new and z_ring go together");
+  const bool complete = (t + 1) % m == 0;
+  if (complete) {
+    const int64_t i = (t + 1) / m - 1;
+    REQUIRE(i < N_cap, "csa_cache_append: entry %lld does not fit the caches (N_cap=%d)", (long long)i, N_cap);
+    REQUIRE(entries != nullptr, "csa_cache_append: entries is NULL");
+    REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16,
+            "csa_cache_append: entry_fmt=%d unsupported", entry_fmt);
+    if (entry_fmt == CSA_FMT_FP8_ROPE_BF16)
+      REQUIRE(entries_rope && entry_scale, "csa_cache_append: FP8 entries need entries_rope and entry_scale");
+    if (ik_new) {
+      REQUIRE(kidx != nullptr, "csa_cache_append: kidx is NULL");
+      REQUIRE(kidx_fmt == CSA_FMT_BF16 || kidx_fmt == CSA_FMT_MXFP4, "csa_cache_append: kidx_fmt=%d unsupported",
+              kidx_fmt);
+      if (kidx_fmt == CSA_FMT_MXFP4) REQUIRE(kidx_scale != nullptr, "csa_cache_append: MXFP4 kidx needs kidx_scale");
+    }
+  }
+  REQUIRE(((uintptr_t)kv_new & 3u) == 0 && ((uintptr_t)ik_new & 3u) == 0 && ((uintptr_t)kv_ring & 3u) == 0 &&
+              ((uintptr_t)ik_ring & 3u) == 0 && ((uintptr_t)entries & 3u) == 0 &&
+              ((uintptr_t)entries_rope & 3u) == 0 && ((uintptr_t)kidx & 3u) == 0,
+          "csa_cache_append: tensor pointers must be 4-byte aligned");
+
+  csa::CompressParams p{};
+  p.append = 1;
+  p.kv_new = (const uint32_t*)kv_new;
+  p.ik_new = (const uint32_t*)ik_new;
+  p.z_new = z_new;
+  p.kv_ring = (uint32_t*)kv_ring;
+  p.ik_ring = (uint32_t*)ik_ring;
+  p.z_ring = z_ring;
+  p.W = W;
+  p.N_cap = N_cap;
+  p.t = t;
+  p.beta = beta;
+  p.B = B;
+  p.m = m;
+  p.L = L;
+  p.overlap = overlap;
+  p.rope_dims = rope_dims;
+  p.entries_out = entries;
+  p.entries_rope_out = entries_rope;
+  p.entry_scale_out = entry_scale;
+  p.entry_fmt = entry_fmt;
+  p.kidx_out = ik_new ? kidx : nullptr;
+  p.kidx_scale_out = kidx_scale;
+  p.kidx_fmt = kidx_fmt;
+  for (int f = 0; f < 32; ++f) p.theta[f] = std::pow((double)rope_base, -2.0 * f / 64.0);
+  return hip_status(csa::launch_compress(p, (hipStream_t)stream), "csa_cache_append launch");
+}
+
 size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m, int k) {
   return csa::index_topk_workspace(B, n, q_pos0, N, m, k);
 }

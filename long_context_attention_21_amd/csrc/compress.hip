@@ -33,13 +33,34 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int64_t task = (int64_t)blockIdx.x * kCompressWaves + wv;
-  const int64_t total = (int64_t)p.B * p.n_new;
-  const bool active = task < total;
-  const int b = active ? (int)(task / p.n_new) : 0;
-  const int e = active ? (int)(task % p.n_new) : 0;
   const int m = p.m, L = p.L;
-  const int64_t i = p.pos0 / m + e;  // absolute entry index
   const float NEG_INF = -__builtin_inff();
+  bool active;
+  int b, e;
+  int64_t i;  // absolute entry index
+  if (p.append) {
+    // one wave per sequence: store the new row in the rings, then pool the
+    // block it completes (if any)
+    const bool live = task < p.B;
+    b = live ? (int)task : 0;
+    e = 0;
+    if (live) {
+      const int s = (int)(p.t % p.W);
+      const uint32_t x = p.kv_new[(int64_t)b * 64 + lane];
+      p.kv_ring[((int64_t)b * 2 * p.W + s) * 64 + lane] = x;
+      p.kv_ring[((int64_t)b * 2 * p.W + s + p.W) * 64 + lane] = x;
+      if (p.ik_new && lane < 32) p.ik_ring[((int64_t)b * p.W + s) * 32 + lane] = p.ik_new[(int64_t)b * 32 + lane];
+      if (p.z_new && lane < 2) p.z_ring[((int64_t)b * p.W + s) * 2 + lane] = p.z_new[(int64_t)b * 2 + lane];
+    }
+    active = live && (p.t + 1) % m == 0;
+    i = (p.t + 1) / m - 1;
+  } else {
+    const int64_t total = (int64_t)p.B * p.n_new;
+    active = task < total;
+    b = active ? (int)(task / p.n_new) : 0;
+    e = active ? (int)(task % p.n_new) : 0;
+    i = p.pos0 / m + e;
+  }
 
   // ---- slot logits
   for (int r = lane; r < L; r += 64) {
@@ -53,7 +74,12 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
       j = i * m + r;
     }
     double lg = (double)NEG_INF;
-    if (active && j >= 0) {
+    if (active && j >= 0 && p.append) {
+      double zz = 0.0;
+      if (p.z_new)
+        zz = (double)(j == p.t ? p.z_new[(int64_t)b * 2 + role] : p.z_ring[((int64_t)b * p.W + j % p.W) * 2 + role]);
+      lg = (double)p.beta[r] + zz;
+    } else if (active && j >= 0) {
       double zz = 0.0;
       if (j >= p.pos0) {
         if (p.z) zz = (double)p.z[((int64_t)b * p.T + (j - p.pos0)) * 2 + role];
@@ -83,14 +109,22 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
 
   // ---- pooling: fp32 fma chain in ascending slot order
   float a0 = 0.0f, a1 = 0.0f, k0 = 0.0f, k1 = 0.0f;
-  const bool has_ik = p.ik != nullptr;
+  const bool has_ik = p.append ? p.ik_new != nullptr : p.ik != nullptr;
   for (int r = 0; r < L; ++r) {
     float w = s_w[wv][r];
     if (w == NEG_INF) continue;  // absent slot (before token 0)
     int64_t j = p.overlap ? ((r < m) ? (i - 1) * m + r : i * m + (r - m)) : i * m + r;
     const uint32_t* xr;
     const uint32_t* ur = nullptr;
-    if (j >= p.pos0) {
+    if (p.append) {
+      if (j == p.t) {
+        xr = p.kv_new + (int64_t)b * 64;
+        if (has_ik) ur = p.ik_new + (int64_t)b * 32;
+      } else {
+        xr = p.kv_ring + ((int64_t)b * 2 * p.W + j % p.W) * 64;
+        if (has_ik) ur = p.ik_ring + ((int64_t)b * p.W + j % p.W) * 32;
+      }
+    } else if (j >= p.pos0) {
       int64_t row = (int64_t)b * p.T + (j - p.pos0);
       xr = p.kv + row * 64;
       if (has_ik) ur = p.ik + row * 32;
@@ -122,7 +156,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
   }
 
   // ---- store the KV entry
-  const int64_t orow = (int64_t)b * p.n_new + e;
+  const int64_t orow = p.append ? (int64_t)b * p.N_cap + i : (int64_t)b * p.n_new + e;
   if (p.entry_fmt == 0) {
     ((uint32_t*)p.entries_out)[orow * 64 + lane] = pack_bf16(a0, a1);
   } else {
@@ -168,7 +202,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
 }
 
 hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
-  int64_t total = (int64_t)p.B * p.n_new;
+  int64_t total = p.append ? (int64_t)p.B : (int64_t)p.B * p.n_new;
   if (total == 0) return hipSuccess;
   dim3 grid((unsigned)((total + kCompressWaves - 1) / kCompressWaves));
   hipLaunchKernelGGL(compress_kernel, grid, dim3(64 * kCompressWaves), 0, stream, p);

@@ -24,6 +24,20 @@ struct CompressParams {
   uint8_t* kidx_scale_out;
   int kidx_fmt;  // 0 bf16, 1 mxfp4
   double theta[32];  // rope_base^(-2f/64), fp64
+  // Cache append (decode): one new row per sequence at position t.  Rows
+  // j < t come from the rings (slot j % W; the KV ring keeps each row at
+  // slots j % W and j % W + W), row t from the *_new arrays, which are also
+  // written to the rings.  When t completes a block, its entry is stored at
+  // row (t + 1) / m - 1 of caches with N_cap rows per sequence.
+  int append;
+  const uint32_t* kv_new;  // [B, 128] bf16
+  const uint32_t* ik_new;  // [B, 64] bf16 or null
+  const float* z_new;      // [B, 2] or null
+  uint32_t* kv_ring;       // [B, 2W, 128] bf16
+  uint32_t* ik_ring;       // [B, W, 64] bf16 or null
+  float* z_ring;           // [B, W, 2] or null
+  int W, N_cap;
+  int64_t t;
   __device__ uint8_t* kidx_out_u8() const { return (uint8_t*)kidx_out; }
 };
 

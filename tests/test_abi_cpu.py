@@ -195,3 +195,33 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def _append(L, **kw):
+    a = dict(kv_new=FAKE, ik_new=None, z_new=None, B=2, t=3, kv_ring=FAKE2, ik_ring=None, z_ring=None,
+             W=128, beta=FAKE, m=4, overlap=1, rope_dims=64, rope_base=10000.0, entries=FAKE,
+             entries_rope=None, entry_scale=None, entry_fmt=0, kidx=None, kidx_scale=None, kidx_fmt=1,
+             N_cap=8, stream=None)
+    a.update(kw)
+    return L.csa_cache_append(*a.values())
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(W=7), "W=7"),                       # the 2m = 8 pooled rows do not fit the ring
+    (dict(N_cap=0), "does not fit"),          # t = 3 completes entry 0
+    (dict(ik_new=FAKE), "ik_new and ik_ring"),
+    (dict(z_ring=FAKE), "z_new and z_ring"),
+    (dict(entries=None), "entries is NULL"),
+    (dict(t=-1), "t must be"),
+    (dict(entry_fmt=1), "entry_fmt=1"),
+    (dict(kv_ring=MIS + 2), "aligned"),
+])
+def test_cache_append_rejects(L, kw, needle):
+    assert _append(L, **kw) == _lib.CSA_INVALID_ARG
+    assert needle in _msg(L)
+
+
+def test_cache_append_needs_no_cache_between_blocks(L):
+    # t = 4 completes no block (m = 4): caches may be NULL.  Validation only:
+    # B = 0 launches nothing.
+    assert _append(L, B=0, t=4, entries=None) == _lib.CSA_OK
