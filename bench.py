@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (HBM counter calibration)")
     ap.add_argument("--print-sha", action="store_true", help="print the kernel source hashes and exit")
+    ap.add_argument("--append-probe", action="store_true",
+                    help="only time the decode cache write path (csa_cache_append), 64 sequences at 1M")
     return ap.parse_args()
 
 
@@ -89,6 +91,58 @@ def copy_probe():
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": src.numel() * 4, "copy_probe_bytes_written": dst.numel() * 4,
                       "launches": 3}), flush=True)
+
+
+def append_probe(steps=1024):
+    """The decode cache write path at config 4's shape: 64 sequences append
+    one token per call at positions 1,048,576 .. +steps-1, into a CSA layer
+    (m = 4 overlapped, FP8 + bf16-RoPE entries, MXFP4 indexer keys) and an
+    HCA layer (m' = 128, bf16 entries), each with a 128-row state ring.
+    Inputs are synthetic (ring contents do not affect the work)."""
+    import torch
+    import long_context_attention_21_amd as L
+    B, P, W = 64, 1 << 20, 128
+    cu = "cuda"
+    g = torch.Generator(device=cu).manual_seed(5)
+    kv = (torch.randn((steps, B, 128), generator=g, device=cu) * 0.1).to(torch.bfloat16)
+    ik = (torch.randn((steps, B, 64), generator=g, device=cu) * 0.1).to(torch.bfloat16)
+    res = {}
+    for name, m, ov, efmt, with_ik in (("csa", 4, 1, "fp8", True), ("hca", 128, 0, "bf16", False)):
+        N_cap = (P + steps) // m
+        beta = torch.randn((2 * m if ov else m,), generator=g, device=cu)
+        ring = (torch.randn((B, 2 * W, 128), generator=g, device=cu) * 0.1).to(torch.bfloat16)
+        ik_ring = (torch.randn((B, W, 64), generator=g, device=cu) * 0.1).to(torch.bfloat16) if with_ik else None
+        caches = {}
+        if efmt == "bf16":
+            caches["entries"] = torch.empty((B, N_cap, 128), dtype=torch.bfloat16, device=cu)
+        else:
+            caches["entries"] = torch.empty((B, N_cap, 64), dtype=torch.uint8, device=cu)
+            caches["entries_rope"] = torch.empty((B, N_cap, 64), dtype=torch.bfloat16, device=cu)
+            caches["entry_scale"] = torch.empty((B, N_cap), dtype=torch.float32, device=cu)
+        if with_ik:
+            caches["kidx"] = torch.empty((B, N_cap, 32), dtype=torch.uint8, device=cu)
+            caches["kidx_scale"] = torch.empty((B, N_cap, 2), dtype=torch.uint8, device=cu)
+
+        def call(i):
+            L.csa_cache_append(kv[i], beta, m, ov, P + i, ring, caches, ik_new=ik[i] if with_ik else None,
+                               ik_ring=ik_ring, entry_fmt=efmt, kidx_fmt="mxfp4")
+        for i in range(8):
+            call(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        Lr = 2 * m if ov else m
+        row_in = 256 + (128 if with_ik else 0)
+        entry_out = (196 if efmt == "fp8" else 256) + (34 if with_ik else 0)
+        per_call = B * ((2 * 256 + (128 if with_ik else 0)) + (Lr * row_in + entry_out) / m)
+        res[name] = {"us_per_call": round(us, 3), "tokens_per_s": round(B / us * 1e6, 1),
+                     "algorithmic_bytes_per_call": int(per_call), "achieved_GBps": round(per_call / us * 1e-3, 2)}
+    print(json.dumps({"append_probe": res, "sequences": B, "calls": steps, "q_pos": P}), flush=True)
 
 
 # ---------------------------------------------------------------- workloads --
@@ -475,6 +529,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.append_probe:
+        append_probe()
         return
     wl = {1: CsaLayer, 2: HcaLayer, 3: CsaLayer, 4: DecodeLayer, 5: PairLayer}[args.config](args.config)
     nk = len(wl.kernels)

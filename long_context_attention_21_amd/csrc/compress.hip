@@ -52,7 +52,10 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
       if (p.ik_new && lane < 32) p.ik_ring[((int64_t)b * p.W + s) * 32 + lane] = p.ik_new[(int64_t)b * 32 + lane];
       if (p.z_new && lane < 2) p.z_ring[((int64_t)b * p.W + s) * 2 + lane] = p.z_new[(int64_t)b * 2 + lane];
     }
-    active = live && (p.t + 1) % m == 0;
+    // t is the same for every wave: a call that completes no block ends here
+    // on the whole work-group, before any barrier
+    if ((p.t + 1) % m != 0) return;
+    active = live;
     i = (p.t + 1) / m - 1;
   } else {
     const int64_t total = (int64_t)p.B * p.n_new;
@@ -107,15 +110,13 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
   __syncthreads();
   if (!active) return;
 
-  // ---- pooling: fp32 fma chain in ascending slot order
+  // ---- pooling: fp32 fma chain in ascending slot order.  The rows of 8
+  // slots are loaded before their fmas so the loads overlap.
   float a0 = 0.0f, a1 = 0.0f, k0 = 0.0f, k1 = 0.0f;
   const bool has_ik = p.append ? p.ik_new != nullptr : p.ik != nullptr;
-  for (int r = 0; r < L; ++r) {
-    float w = s_w[wv][r];
-    if (w == NEG_INF) continue;  // absent slot (before token 0)
-    int64_t j = p.overlap ? ((r < m) ? (i - 1) * m + r : i * m + (r - m)) : i * m + r;
-    const uint32_t* xr;
-    const uint32_t* ur = nullptr;
+  auto rows_of = [&](int r, const uint32_t*& xr, const uint32_t*& ur) {
+    const int64_t j = p.overlap ? ((r < m) ? (i - 1) * m + r : i * m + (r - m)) : i * m + r;
+    ur = nullptr;
     if (p.append) {
       if (j == p.t) {
         xr = p.kv_new + (int64_t)b * 64;
@@ -125,21 +126,41 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
         if (has_ik) ur = p.ik_ring + ((int64_t)b * p.W + j % p.W) * 32;
       }
     } else if (j >= p.pos0) {
-      int64_t row = (int64_t)b * p.T + (j - p.pos0);
+      const int64_t row = (int64_t)b * p.T + (j - p.pos0);
       xr = p.kv + row * 64;
       if (has_ik) ur = p.ik + row * 32;
     } else {
-      int64_t row = (int64_t)b * m + (j - (p.pos0 - m));
+      const int64_t row = (int64_t)b * m + (j - (p.pos0 - m));
       xr = p.prev_kv + row * 64;
       if (has_ik) ur = p.prev_ik + row * 32;
     }
-    uint32_t x = xr[lane];
-    a0 = __builtin_fmaf(w, bf16lo(x), a0);
-    a1 = __builtin_fmaf(w, bf16hi(x), a1);
-    if (has_ik && lane < 32) {
-      uint32_t u = ur[lane];
-      k0 = __builtin_fmaf(w, bf16lo(u), k0);
-      k1 = __builtin_fmaf(w, bf16hi(u), k1);
+  };
+  for (int r0 = 0; r0 < L; r0 += 8) {
+    float ws[8];
+    uint32_t xs[8], us[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + u;
+      ws[u] = r < L ? s_w[wv][r] : NEG_INF;
+      xs[u] = 0u;
+      us[u] = 0u;
+      if (ws[u] != NEG_INF) {  // absent slots (before token 0, or past L) are skipped
+        const uint32_t* xr;
+        const uint32_t* ur;
+        rows_of(r, xr, ur);
+        xs[u] = xr[lane];
+        if (has_ik && lane < 32) us[u] = ur[lane];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (ws[u] == NEG_INF) continue;
+      a0 = __builtin_fmaf(ws[u], bf16lo(xs[u]), a0);
+      a1 = __builtin_fmaf(ws[u], bf16hi(xs[u]), a1);
+      if (has_ik && lane < 32) {
+        k0 = __builtin_fmaf(ws[u], bf16lo(us[u]), k0);
+        k1 = __builtin_fmaf(ws[u], bf16hi(us[u]), k1);
+      }
     }
   }
 
