@@ -11,11 +11,14 @@
 // written followed by -1 padding (the order within a row is unspecified).
 //
 // Design for CDNA4
-//  * A work-group of 8 waves serves QT = 4 query tokens (1 for single-token
-//    decode).  Scores: one v_mfma_scale_f32_32x32x64_f8f6f4 (MXFP4) or four
-//    v_mfma_f32_32x32x16_bf16 per 32 entries.  The 32 A rows are 4 tokens x 8
-//    heads, placed so each lane's 16 accumulator rows are all 8 heads of two
-//    tokens: the head sum is an in-lane fma chain in ascending head order
+//  * A work-group serves QT query tokens: 4 waves and 2 tokens for rows of up
+//    to 64K entries (two work-groups per CU), 8 waves and 4 tokens for
+//    longer rows, 8 waves and 1 token for single-token decode.  Scores: one
+//    v_mfma_scale_f32_32x32x64_f8f6f4 (MXFP4) or four
+//    v_mfma_f32_32x32x16_bf16 per 32 entries.  The 32 A rows are 4 token
+//    slots x 8 heads, placed so each lane's accumulator rows are all 8 heads
+//    of its token(s): lanes 0..31 hold tokens 0 and 2, lanes 32..63 tokens 1
+//    and 3.  The head sum is an in-lane fma chain in ascending head order
 //    (MXFP4 dot products are exact, so MXFP4 scores are bit-identical to a
 //    sequential evaluation).  Entry rows come through range-checked buffer
 //    loads, four tiles in flight per wave.
@@ -43,11 +46,19 @@
 
 namespace csa {
 
-constexpr int kWaves = 8;              // waves per work-group (2 per SIMD)
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 32 * kWaves;     // entries per round of the work-group
 constexpr int kCap = 4096;             // candidate buffer per token
-constexpr int kReg = kCap / kWaves;    // per-wave candidate region of a token's buffer
+// Work-group shape for QT tokens: 8 waves (2 per SIMD) for 1 or 4 tokens; 4
+// waves for 2 tokens, whose 70 KB of LDS lets two work-groups share a CU so
+// that one's scoring overlaps the other's selections.  Each lane scores TPL
+// tokens of a tile (all 64 lanes are busy once QT >= 2).
+template <int QT>
+struct Shape {
+  static constexpr int W = QT == 2 ? 4 : 8;  // waves per work-group
+  static constexpr int T = 64 * W;          // threads
+  static constexpr int Tile = 32 * W;       // entries per round of the work-group
+  static constexpr int Reg = kCap / W;      // per-wave candidate region of a token's buffer
+  static constexpr int TPL = QT > 2 ? 2 : 1;
+};
 constexpr int kDepth = 4;              // score tiles in flight per wave
 constexpr int kMinAbove = 256;         // sampled entries expected above the threshold
 constexpr int kList = 512;             // per-member key list after the first radix digit
@@ -66,14 +77,15 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 __device__ __forceinline__ void row_to_token_head(int r, int& j, int& h) {
   const int half = (r >> 2) & 1;
   const int ic = 4 * (r >> 3) + (r & 3);
-  j = 2 * half + (ic >> 3);
+  j = half + 2 * (ic >> 3);
   h = ic & 7;
 }
 
 // Token j of a work-group is served by the "group" of waves w with
-// w % QT == j (kWaves / QT of them); group member h = w / QT.
+// w % QT == j (W / QT of them); group member h = w / QT.
 template <int QT>
 struct TopkSmem {
+  static constexpr int kWaves = Shape<QT>::W;
   uint2 cand[QT][kCap];       // {fp32 score bits, entry}; samples in phase 1; output bitmap at the end
   uint32_t hist[2][QT][256];  // double-buffered radix histograms, one per token group
   uint32_t xchg[kWaves][2];   // per-wave values read by the other group members
@@ -150,7 +162,7 @@ struct RadixOut {
 template <int QT, int NS>
 __device__ __forceinline__ RadixOut group_radix(TopkSmem<QT>& sm, const uint32_t (&kr)[NS], uint32_t smask, uint32_t r,
                                                 uint32_t n_valid, bool active, uint32_t slack = 0u) {
-  constexpr int G = kWaves / QT;
+  constexpr int G = Shape<QT>::W / QT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = wave % QT, h = wave / QT;
   uint32_t kmax = 0u, kmin1 = 0xffffffffu;  // kmin1 = min(key - 1): empty (0) keys wrap to the top
@@ -298,7 +310,7 @@ __device__ __forceinline__ RadixOut group_radix(TopkSmem<QT>& sm, const uint32_t
 // Exact streaming fallback (work-group wide): buffers hold order keys and are
 // shrunk to exactly k whenever they fill.
 
-template <class KeyFn, class FiltFn>
+template <int kThreads, class KeyFn, class FiltFn>
 __device__ uint32_t wg_radix_select(uint32_t* hist, uint32_t* sel, int cnt, uint32_t r, KeyFn keyfn,
                                     FiltFn filt, uint32_t* above, uint32_t* equal) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -352,20 +364,21 @@ __device__ uint32_t wg_radix_select(uint32_t* hist, uint32_t* sel, int cnt, uint
 
 template <int QT>
 __device__ void wg_shrink_exact(TopkSmem<QT>& sm, int j, int kk) {
+  constexpr int kThreads = Shape<QT>::T;
   const int tid = threadIdx.x;
   const int cnt = sm.cnt[j];
   if (cnt <= kk) return;
   uint32_t above, equal;
   uint2* cd = sm.cand[j];
   uint32_t* hist = &sm.hist[0][0][0];
-  const uint32_t tau = wg_radix_select(hist, sm.sel, cnt, (uint32_t)kk, [&](int i) { return cd[i].x; },
+  const uint32_t tau = wg_radix_select<kThreads>(hist, sm.sel, cnt, (uint32_t)kk, [&](int i) { return cd[i].x; },
                                        [](int) { return true; }, &above, &equal);
   const uint32_t need = (uint32_t)kk - above;
   uint32_t tau_inv = 0;
   const bool cut_ties = need < equal;
   if (cut_ties) {
     uint32_t a2, e2;
-    tau_inv = wg_radix_select(hist, sm.sel, cnt, need, [&](int i) { return ~cd[i].y; },
+    tau_inv = wg_radix_select<kThreads>(hist, sm.sel, cnt, need, [&](int i) { return ~cd[i].y; },
                               [&](int i) { return cd[i].x == tau; }, &a2, &e2);
   }
   constexpr int PER = kCap / kThreads;
@@ -397,6 +410,7 @@ __device__ void wg_shrink_exact(TopkSmem<QT>& sm, int j, int kk) {
 
 template <int QT>
 __device__ void wg_bitonic_sort(TopkSmem<QT>& sm, int j, int cnt) {
+  constexpr int kThreads = Shape<QT>::T;
   const int tid = threadIdx.x;
   int P = 1;
   while (P < cnt) P <<= 1;
@@ -476,11 +490,13 @@ struct Scorer {
     return C;
   }
 
-  // C rows: heads 0..7 of token jl0 (i = 0..7) and of token jl0 + 1 (i = 8..15).
+  // C rows: heads 0..7 of the lane's token jl0 (i = 0..7) and of token
+  // jl0 + 2 (i = 8..15); TPL = 1 scores only the first.
   // The chain starts from +0 and can never produce -0.
+  template <int TPL = 2>
   __device__ __forceinline__ void epilogue(const f32x16& C, float I[2]) const {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < TPL; ++tt) {
       float s = 0.0f;
 #pragma unroll
       for (int h = 0; h < 8; ++h) s = __builtin_fmaf(wv[tt][h], fmaxf(C[tt * 8 + h], 0.0f), s);
@@ -488,24 +504,24 @@ struct Scorer {
     }
   }
 
-  __device__ __forceinline__ void compute(const BTile<FMT>& t, float I[2]) const { epilogue(mfma(t), I); }
-
-  __device__ __forceinline__ void score(int e, float I[2]) const { compute(load(e), I); }
+  template <int TPL = 2>
+  __device__ __forceinline__ void score(int e, float I[2]) const { epilogue<TPL>(mfma(load(e)), I); }
 };
 
 // Appends the passing lanes of each half-wave to their token's buffer
 // (exact fallback: shared count, LDS atomic).
 template <int QT>
 __device__ __forceinline__ void append(TopkSmem<QT>& sm, const bool pass[2], const uint32_t val[2], int e, int jl0) {
+  constexpr int TPL = Shape<QT>::TPL;
   const int lane = threadIdx.x & 63;
   const int leader = (lane < 32) ? 0 : 32;
   const uint64_t halfmask = (lane < 32) ? 0x00000000ffffffffull : 0xffffffff00000000ull;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < TPL; ++tt) {
     const uint64_t mine = ballot(pass[tt]) & halfmask;
     const int pc = __builtin_popcountll(mine);
     const int rank = __builtin_popcountll(mine & ((1ull << lane) - 1ull));
-    const int j = jl0 + tt;
+    const int j = jl0 + 2 * tt;
     int basepos = 0;
     if (lane == leader && pc > 0) basepos = atomicAdd(&sm.cnt[j < QT ? j : 0], pc);
     basepos = __shfl(basepos, leader);
@@ -520,6 +536,7 @@ __device__ __forceinline__ void append(TopkSmem<QT>& sm, const bool pass[2], con
 template <int QT>
 __device__ __forceinline__ void append_private(TopkSmem<QT>& sm, bool vis, bool ge, uint32_t val, int e, int j,
                                                int& wcnt) {
+  constexpr int kReg = Shape<QT>::Reg;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // the two compares' lane masks, combined on the scalar unit
@@ -593,12 +610,12 @@ __device__ __forceinline__ void init_scorer(Scorer<FMT>& sc, const IndexParams& 
       }
     }
   }
-  const int jl0 = 2 * (lane >> 5);
+  const int jl0 = lane >> 5;  // this lane scores tokens jl0 and jl0 + 2
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const int q = q0 + jl0 + tt;
+    const int q = q0 + jl0 + 2 * tt;
     int v = 0;
-    if (jl0 + tt < QT && q < p.n) {
+    if (jl0 + 2 * tt < QT && q < p.n) {
       const int64_t c = (p.q_pos0 + q + 1) / p.m;
       v = (int)(c < p.N ? c : p.N);
     }
@@ -646,7 +663,9 @@ struct SplitRow {
 // row, written to its workspace row.  SPLIT 2: the exact selection among the
 // candidates the partitions appended to the workspace row.
 template <int QT, int FMT, int SPLIT = 0>
-__global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
+__global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p) {
+  constexpr int kWaves = Shape<QT>::W, kThreads = Shape<QT>::T, kTile = Shape<QT>::Tile, kReg = Shape<QT>::Reg;
+  constexpr int TPL = Shape<QT>::TPL;
   __shared__ TopkSmem<QT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = (p.n + QT - 1) / QT;
@@ -689,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
   Scorer<FMT> sc;
   int nvl[2];
   init_scorer<QT, FMT>(sc, p, b, q0, nvl);
-  const int jl0 = 2 * (lane >> 5);
+  const int jl0 = lane >> 5;  // this lane's tokens: jl0 + 2 tt, tt < TPL
   const int l32 = lane & 31;
   const int grp_j = wave % QT, grp_h = wave / QT;  // this wave's token group and member index
   constexpr int G = kWaves / QT;                    // waves per token group
@@ -731,7 +750,7 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
         const f32x16 C = sc.mfma(t[u]);
         t[u] = sc.load(S * ((tile + kDepth * kWaves) * 32 + l32));
         float I[2];
-        sc.epilogue(C, I);
+        sc.template epilogue<TPL>(C, I);
         // The MFMA takes operands from all 64 lanes.  Its result must be used
         // outside the lane-masked store below, or the compiler may move the
         // MFMA and its operand set-up under that mask, where the masked-off
@@ -740,8 +759,8 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
         const int i = tile * 32 + l32;
         const int e = S * i;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int j = jl0 + tt;
+        for (int tt = 0; tt < TPL; ++tt) {
+          const int j = jl0 + 2 * tt;
           if (j < QT && e < nvl[tt]) sm.cand[j][i].x = __float_as_uint(I[tt]);
         }
       }
@@ -769,8 +788,8 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
       __syncthreads();  // first cuts visible; the sample buffers are free
       float thr_a[2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int j = jl0 + tt;
+      for (int tt = 0; tt < TPL; ++tt) {
+        const int j = jl0 + 2 * tt;
         thr_a[tt] = (j < QT) ? sm.thr[j < QT ? j : 0] : 0.0f;
         asm volatile("" : "+v"(thr_a[tt]));
       }
@@ -792,17 +811,17 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
           const f32x16 C = sc.mfma(t[u]);
           t[u] = sc.load(SB * ((tile + kDepth * kWaves) * 32 + l32));
           float I[2];
-          sc.epilogue(C, I);
+          sc.template epilogue<TPL>(C, I);
           const int e = SB * (tile * 32 + l32);
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-            append_private<QT>(sm, e < nvl[tt], I[tt] >= thr_a[tt], __float_as_uint(I[tt]), e, jl0 + tt, wc2[tt]);
+          for (int tt = 0; tt < TPL; ++tt)
+            append_private<QT>(sm, e < nvl[tt], I[tt] >= thr_a[tt], __float_as_uint(I[tt]), e, jl0 + 2 * tt, wc2[tt]);
         }
       }
       if (l32 == 0) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          if (jl0 + tt < QT) sm.wcnt[wave][jl0 + tt] = wc2[tt];
+        for (int tt = 0; tt < TPL; ++tt)
+          if (jl0 + 2 * tt < QT) sm.wcnt[wave][jl0 + 2 * tt] = wc2[tt];
       }
       __syncthreads();
       // cut of the second sample among the kept ones (regions as in the final selection)
@@ -854,8 +873,8 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
   // ---- phase 2: every entry scored once; candidates >= threshold appended
     float thr2[2];
   #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int j = jl0 + tt;
+    for (int tt = 0; tt < TPL; ++tt) {
+      const int j = jl0 + 2 * tt;
       thr2[tt] = (j < QT) ? sm.thr[j < QT ? j : 0] : 0.0f;
       // the LDS read completes here, not inside the scoring loop (whose LDS
       // stores would otherwise be waited for on every tile)
@@ -879,16 +898,16 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
           t[u] = sc.load(base + (u + kDepth) * kTile + ecol);
           const int e = base + u * kTile + ecol;
           float I[2];
-          sc.epilogue(C, I);
+          sc.template epilogue<TPL>(C, I);
   #pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-            append_private<QT>(sm, e < nvl[tt], I[tt] >= thr2[tt], __float_as_uint(I[tt]), e, jl0 + tt, wcnt[tt]);
+          for (int tt = 0; tt < TPL; ++tt)
+            append_private<QT>(sm, e < nvl[tt], I[tt] >= thr2[tt], __float_as_uint(I[tt]), e, jl0 + 2 * tt, wcnt[tt]);
         }
       }
       if (l32 == 0) {
   #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          if (jl0 + tt < QT) sm.wcnt[wave][jl0 + tt] = wcnt[tt];
+        for (int tt = 0; tt < TPL; ++tt)
+          if (jl0 + 2 * tt < QT) sm.wcnt[wave][jl0 + 2 * tt] = wcnt[tt];
       }
     }
   }
@@ -918,10 +937,10 @@ __global__ __launch_bounds__(kThreads) void index_topk_kernel(IndexParams p) {
       uint32_t val[2] = {0u, 0u};
       if (e0 < maxnv) {
         float I[2];
-        sc.score(e, I);
+        sc.template score<TPL>(e, I);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int j = jl0 + tt;
+        for (int tt = 0; tt < TPL; ++tt) {
+          const int j = jl0 + 2 * tt;
           const uint32_t u = okey(__float_as_uint(I[tt]));
           val[tt] = u;
           pass[tt] = (j < QT) && (e < nvl[tt]) && (u >= __float_as_uint(sm.thr[j < QT ? j : 0]));
@@ -1081,7 +1100,7 @@ __global__ __launch_bounds__(256) void index_split_score_kernel(IndexParams p, i
       const f32x16 C = sc.mfma(t[u]);
       t[u] = sc.load(e0 + (tile + kDepth * W) * 32 + l32);
       float I[2];
-      sc.epilogue(C, I);
+      sc.template epilogue<1>(C, I);
       const int e = e0 + tile * 32 + l32;
       const bool pass = lane < 32 && e < e1 && I[0] >= thr;  // token 0 lives in lanes 0..31
       const uint64_t bal = ballot(pass);
@@ -1122,7 +1141,7 @@ size_t index_topk_workspace(int B, int n, int64_t q_pos0, int N, int m, int) {
 template <int QT>
 static hipError_t launch_q(const IndexParams& p, hipStream_t stream) {
   const int nblk = (p.n + QT - 1) / QT;
-  dim3 grid((unsigned)((int64_t)p.B * nblk)), block(kThreads);
+  dim3 grid((unsigned)((int64_t)p.B * nblk)), block(Shape<QT>::T);
   if (p.fmt == 1)
     hipLaunchKernelGGL((index_topk_kernel<QT, 1>), grid, block, 0, stream, p);
   else
@@ -1136,10 +1155,10 @@ static hipError_t launch_split(const IndexParams& p, hipStream_t stream) {
   int64_t nv = (p.q_pos0 + p.n) / p.m;
   if (nv > p.N) nv = p.N;
   const int parts = (int)((nv + kSplitPart - 1) / kSplitPart);
-  hipLaunchKernelGGL((index_topk_kernel<1, FMT, 1>), dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((index_topk_kernel<1, FMT, 1>), dim3((unsigned)rows), dim3(Shape<1>::T), 0, stream, p);
   hipLaunchKernelGGL((index_split_score_kernel<FMT>), dim3((unsigned)(rows * parts)), dim3(256), 0, stream, p,
                      parts, kSplitPart);
-  hipLaunchKernelGGL((index_topk_kernel<1, FMT, 2>), dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((index_topk_kernel<1, FMT, 2>), dim3((unsigned)rows), dim3(Shape<1>::T), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1147,6 +1166,12 @@ hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream) {
   if ((int64_t)p.B * p.n == 0) return hipSuccess;
   if (split_path(p.B, p.n, p.q_pos0, p.N, p.m)) return p.fmt == 1 ? launch_split<1>(p, stream) : launch_split<0>(p, stream);
   if (p.n == 1) return launch_q<1>(p, stream);
+  // Rows of up to 64K entries: 2-token work-groups, two per CU, so one
+  // work-group's selections overlap the other's scoring.  Longer rows are
+  // dominated by scoring, where 4 tokens per loaded key tile are cheaper.
+  int64_t nv = (p.q_pos0 + p.n) / p.m;
+  if (nv > p.N) nv = p.N;
+  if (nv <= 65536) return launch_q<2>(p, stream);
   return launch_q<4>(p, stream);
 }
 

@@ -139,6 +139,7 @@ def _index_case(orc, rng, B, n, N, H_I, k, q_pos0, fmt, m=4, dup_rows=0, prequan
     (1, 40, 5000, 1, 300, 20000, "bf16", {}),
     # split path (few query rows over >= 65536 visible entries): threshold per
     # row, partitions append candidates, selection per row
+    (1, 9, 70000, 8, 2048, 280000 - 9, "mxfp4", {}),     # long rows: 4-token work-groups
     (3, 1, 70000, 8, 512, 280000, "mxfp4", {}),          # ragged last partition
     (2, 4, 90000, 8, 2048, 280000 - 4, "mxfp4", {}),     # entries past the causal bound
     (1, 2, 70000, 8, 512, 280000, "mxfp4", {"dup_rows": 3, "fallback": True}),  # candidates overflow
