@@ -209,7 +209,7 @@ int csa_index_topk_fallbacks(uint64_t* count, int reset);
  * the inverse rotation by t.  bf16 MFMA products, fp32 softmax and
  * accumulation, bf16 output.
  *
- *  q            [B, n, H, 128] bf16 pre-RoPE; H a multiple of 16, <= 128
+ *  q            [B, n, H, 128] bf16 pre-RoPE; 1 <= H <= 64
  *  entries      BF16: [B, N, 128] bf16 post-RoPE.  FP8_ROPE_BF16:
  *               [B, N, 64] e4m3 codes (value = code * entry_scale)
  *  entries_rope FP8_ROPE_BF16: [B, N, 64] bf16 (dims 64..127); else NULL
@@ -223,12 +223,24 @@ int csa_index_topk_fallbacks(uint64_t* count, int reset);
  *  n_win        0 (no window) .. 128
  *  sink         [H] fp32 or NULL (no sink)
  *  out          [B, n, H, 128] bf16
+ *  ws, ws_bytes device scratch of at least csa_attend_workspace_bytes()
+ *               bytes, 16-byte aligned (may be NULL when that is 0).  It is
+ *               non-zero for FP8 entries with few query rows (B*n <= 512)
+ *               and at least 16 chunks of 32 keys (k + n_win >= 512): each
+ *               token's keys are then split over several work-groups whose
+ *               partial softmax sums are merged in a fixed order (the result
+ *               does not depend on the split).  33280 bytes per (query row,
+ *               part of 8 chunks).  Contents are undefined after the call;
+ *               calls that share a workspace must be ordered on one stream.
  */
 int csa_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D,
                const void* entries, const void* entries_rope, const float* entry_scale,
                int entry_fmt, int N, int m, const int32_t* idx, int k,
                const void* win_kv, int64_t win_pos0, int win_len, int n_win,
-               const float* sink, int rope_dims, float rope_base, void* out, void* stream);
+               const float* sink, int rope_dims, float rope_base, void* out, void* ws,
+               size_t ws_bytes, void* stream);
+
+size_t csa_attend_workspace_bytes(int B, int n, int k, int n_win, int entry_fmt);
 
 /*
  * hca_attend -- HCA dense attention over every visible entry + window + sink

@@ -129,9 +129,11 @@ def csa_index_topk_fallbacks(reset=False):
 
 def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=128, sink=None,
                entries_rope=None, entry_scale=None, rope_dims=64, rope_base=10000.0, N=None,
-               out=None, stream=None):
+               out=None, ws=None, stream=None):
     """q [B, n, H, 128] bf16; entries [B, N, 128] bf16 (or e4m3 [B, N, 64] with
-    entries_rope/entry_scale); idx [B, n, k] int32; win_kv [B, W, 128] bf16."""
+    entries_rope/entry_scale); idx [B, n, k] int32; win_kv [B, W, 128] bf16.
+    ``ws``: workspace of csa_attend_workspace_bytes() bytes (allocated here
+    when needed and not given)."""
     B, n, H, D = q.shape
     if N is None:
         N = entries.shape[1]
@@ -139,10 +141,14 @@ def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=12
     if out is None:
         out = torch.empty_like(q, dtype=torch.bfloat16)
     win_len = 0 if win_kv is None else win_kv.shape[1]
+    nw = int(n_win) if win_kv is not None else 0
+    need = lib().csa_attend_workspace_bytes(B, n, idx.shape[2], nw, ef)
+    if ws is None and need > 0:
+        ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
     check(lib().csa_attend(
         _ptr(q), B, n, int(q_pos0), H, D, _ptr(entries), _ptr(entries_rope), _ptr(entry_scale), ef,
-        N, m, _ptr(idx), idx.shape[2], _ptr(win_kv), int(win_pos0), win_len,
-        int(n_win) if win_kv is not None else 0, _ptr(sink), rope_dims, float(rope_base), _ptr(out),
+        N, m, _ptr(idx), idx.shape[2], _ptr(win_kv), int(win_pos0), win_len, nw, _ptr(sink), rope_dims,
+        float(rope_base), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
     return out
 

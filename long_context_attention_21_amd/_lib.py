@@ -21,7 +21,8 @@ FMT_MXFP4 = 1
 FMT_FP8_ROPE_BF16 = 2
 
 EXPORTS = ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_workspace_bytes",
-           "csa_index_topk_fallbacks", "csa_attend", "hca_attend", "csa_last_error", "csa_version")
+           "csa_index_topk_fallbacks", "csa_attend", "csa_attend_workspace_bytes", "hca_attend", "csa_last_error",
+           "csa_version")
 
 
 class CsaError(RuntimeError):
@@ -52,7 +53,9 @@ def lib():
     L.csa_index_topk_workspace_bytes.restype = sz
     L.csa_index_topk_fallbacks.argtypes = [P, i32]
     L.csa_attend.argtypes = [P, i32, i32, i64, i32, i32, P, P, P, i32, i32, i32, P, i32, P, i64, i32,
-                             i32, P, i32, f32, P, P]
+                             i32, P, i32, f32, P, P, sz, P]
+    L.csa_attend_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.csa_attend_workspace_bytes.restype = sz
     L.hca_attend.argtypes = [P, i32, i32, i64, i32, i32, P, i32, i32, P, i64, i32, i32, P, i32, f32,
                              P, P]
     for f in ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend",

@@ -252,8 +252,8 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
                          const void* entries, const void* entries_rope, const float* entry_scale,
                          int N, int m, const int32_t* idx, int k, const void* win_kv,
                          int64_t win_pos0, int win_len, int n_win, const float* sink,
-                         int rope_dims, float rope_base, void* out, void* stream,
-                         const char* name) {
+                         int rope_dims, float rope_base, void* out, void* ws, size_t ws_bytes,
+                         void* stream, const char* name) {
   REQUIRE(B >= 0 && n >= 0 && N >= 0 && k >= 0, "%s: B, n, N and k must be >= 0", name);
   REQUIRE(D == 128, "%s: D=%d unsupported (head dim must be 128)", name, D);
   REQUIRE(H >= 1 && H <= 64, "%s: H=%d must be in [1, 64]", name, H);
@@ -287,6 +287,10 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   REQUIRE(aligned16(q) && aligned16(entries) && aligned16(entries_rope) && aligned16(win_kv) &&
               aligned16(out),
           "%s: q, entries, entries_rope, win_kv and out must be 16-byte aligned", name);
+  const size_t need = csa::attend_workspace(mode, B, n, k, n_win);
+  if (ws_bytes < need)
+    return fail(CSA_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes < %zu needed", name, ws_bytes, need);
+  REQUIRE(need == 0 || (ws != nullptr && aligned16(ws)), "%s: ws must be non-NULL and 16-byte aligned", name);
   csa::AttendParams p{};
   p.q = (const uint16_t*)q;
   p.B = B;
@@ -308,6 +312,7 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   p.rope = rope_dims == 64 ? 1 : 0;
   p.qscale = (float)(1.4426950408889634 / std::sqrt(128.0));
   p.out = (uint16_t*)out;
+  p.ws = need > 0 ? (float*)ws : nullptr;
   for (int f = 0; f < 32; ++f) p.rev[f] = std::pow((double)rope_base, -2.0 * f / 64.0) / (2.0 * kPi);
   return hip_status(csa::launch_attend(p, mode == 2 ? 2 : mode, (hipStream_t)stream), name);
 }
@@ -315,21 +320,26 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
 int csa_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const void* entries,
                const void* entries_rope, const float* entry_scale, int entry_fmt, int N, int m,
                const int32_t* idx, int k, const void* win_kv, int64_t win_pos0, int win_len,
-               int n_win, const float* sink, int rope_dims, float rope_base, void* out,
-               void* stream) {
+               int n_win, const float* sink, int rope_dims, float rope_base, void* out, void* ws,
+               size_t ws_bytes, void* stream) {
   REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16,
           "csa_attend: entry_fmt=%d unsupported", entry_fmt);
   return attend_common(entry_fmt == CSA_FMT_BF16 ? 0 : 1, q, B, n, q_pos0, H, D, entries,
                        entries_rope, entry_scale, N, m, idx, k, win_kv, win_pos0, win_len, n_win,
-                       sink, rope_dims, rope_base, out, stream, "csa_attend");
+                       sink, rope_dims, rope_base, out, ws, ws_bytes, stream, "csa_attend");
+}
+
+size_t csa_attend_workspace_bytes(int B, int n, int k, int n_win, int entry_fmt) {
+  if (B < 0 || n < 0 || k < 0 || n_win < 0) return 0;
+  return csa::attend_workspace(entry_fmt == CSA_FMT_FP8_ROPE_BF16 ? 1 : 0, B, n, k, n_win);
 }
 
 int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const void* entries,
                int N, int m, const void* win_kv, int64_t win_pos0, int win_len, int n_win,
                const float* sink, int rope_dims, float rope_base, void* out, void* stream) {
   return attend_common(2, q, B, n, q_pos0, H, D, entries, nullptr, nullptr, N, m, nullptr, 0,
-                       win_kv, win_pos0, win_len, n_win, sink, rope_dims, rope_base, out, stream,
-                       "hca_attend");
+                       win_kv, win_pos0, win_len, n_win, sink, rope_dims, rope_base, out, nullptr, 0,
+                       stream, "hca_attend");
 }
 
 }  // extern "C"

@@ -43,13 +43,17 @@ struct ChunkRegs {
   bool v[2];      // key validity
 };
 
-template <int NHT, int MODE>  // MODE 0: CSA bf16 entries, 1: CSA fp8+bf16 entries, 2: HCA
+// SPLIT: work-group (token, part) takes chunks [part * cpp, (part+1) * cpp)
+// and leaves its unnormalised O, reference and row sums in the workspace for
+// attend_combine_kernel.
+template <int NHT, int MODE, bool SPLIT = false>  // MODE 0: CSA bf16 entries, 1: CSA fp8+bf16 entries, 2: HCA
 __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][32 * KP];
   __shared__ __attribute__((aligned(16))) int32_t Is[MODE == 2 ? 4 : kMaxK];  // the token's idx row
   const int lane = threadIdx.x;
   const int g = lane >> 4, l16 = lane & 15;
-  const int64_t tok = blockIdx.x;  // b * n + q
+  const int64_t tok = SPLIT ? blockIdx.x / p.parts : blockIdx.x;  // b * n + q
+  const int part = SPLIT ? (int)(blockIdx.x % p.parts) : 0;
   const int b = (int)(tok / p.n);
   const int qi = (int)(tok % p.n);
   const int64_t t = p.q_pos0 + qi;
@@ -129,6 +133,8 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
     n_wk = (int)(t - j0 + 1);
   }
   const int n_chunks = n_ent_chunks + ((n_wk + 31) >> 5);
+  const int c_lo = SPLIT ? part * p.cpp : 0;  // this work-group's chunks [c_lo, c_hi)
+  const int c_hi = SPLIT ? (c_lo + p.cpp < n_chunks ? c_lo + p.cpp : n_chunks) : n_chunks;
 
   // CSA: stage the token's index row in LDS once (coalesced 16-byte loads),
   // so the loop reads indices from LDS and never waits on them in HBM
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
         const int wj = (c - n_ent_chunks) * 32 + kt * 16 + l16;
         row = wj < n_wk ? win_row0 + wj : -1;
       }
-      if (c >= n_chunks) row = -1;
+      if (c >= c_hi) row = -1;
       R.v[kt] = row >= 0;
       R.sc[kt] = 1.0f;
       if (MODE == 1 && ent) {
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   };
   // post-process a loaded chunk: fp8 dequantisation, window-row rotation
   auto finish = [&](int c, ChunkRegs& R) {
-    if (c >= n_chunks) return;
+    if (c >= c_hi) return;
     if (MODE == 1 && c < n_ent_chunks) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -281,7 +287,9 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = ht * 16 + l16;
-      const float l0 = p.sink ? __builtin_amdgcn_exp2f((h < p.H ? p.sink[h] : 0.0f) * LOG2E - mref[ht]) : 0.0f;
+      // the sink weight belongs to one part only
+      const float l0 =
+          (p.sink && part == 0) ? __builtin_amdgcn_exp2f((h < p.H ? p.sink[h] : 0.0f) * LOG2E - mref[ht]) : 0.0f;
       Lacc[ht] = f32x4{l0, l0, l0, l0};
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) O[dt][ht] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -289,11 +297,11 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
     ChunkRegs R;
     {
       int i0[2];
-      fetch_idx(0, i0);
-      issue(0, i0, R);
+      fetch_idx(c_lo, i0);
+      issue(c_lo, i0, R);
     }
     bool again = false;
-    for (int c = 0; c < n_chunks; ++c) {
+    for (int c = c_lo; c < c_hi; ++c) {
       f32x4 S[2][NHT];
       uint32_t msk[2];
       int inext[2];
@@ -356,6 +364,23 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
 
     }
     if (!again) break;
+  }
+
+  if constexpr (SPLIT) {
+    // ---- partial results: O[h][d] unnormalised, then mref[h], L[h]
+    float* w = p.ws + ((int64_t)tok * p.parts + part) * kAttendPartFloats;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int h = ht * 16 + l16;
+      if (h >= p.H) continue;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(w + h * 128 + dt * 16 + 4 * g) = O[dt][ht];
+      if (g == 0) {
+        w[64 * 128 + h] = mref[ht];
+        w[64 * 128 + 64 + h] = Lacc[ht][0];
+      }
+    }
+    return;
   }
 
   // ---- normalise, inverse RoPE on dims 64..127, store bf16
@@ -818,10 +843,66 @@ static hipError_t launch_ring(const AttendParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Split decode, second kernel: per token, thread (head h, 32 dims) merges
+// the parts in ascending order: O = sum_p O_p 2^(m_p - M), L likewise, with
+// M the largest part reference; then normalise, inverse RoPE, store bf16.
+__global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p) {
+  const int64_t tok = blockIdx.x;
+  const int h = threadIdx.x >> 2, d0 = (threadIdx.x & 3) * 32;
+  if (h >= p.H) return;
+  const float* w0 = p.ws + (int64_t)tok * p.parts * kAttendPartFloats;
+  float M = -__builtin_inff();
+  for (int q = 0; q < p.parts; ++q) M = fmaxf(M, w0[q * kAttendPartFloats + 64 * 128 + h]);
+  float acc[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
+  float L = 0.0f;
+  for (int q = 0; q < p.parts; ++q) {
+    const float* w = w0 + q * kAttendPartFloats;
+    const float lq = w[64 * 128 + 64 + h];
+    if (!(lq > 0.0f)) continue;  // no keys and no sink in this part
+    const float sc = __builtin_amdgcn_exp2f(w[64 * 128 + h] - M);
+    L = __builtin_fmaf(lq, sc, L);
+#pragma unroll
+    for (int e = 0; e < 32; e += 4) {
+      const f32x4 v = *(const f32x4*)(w + h * 128 + d0 + e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[e + i] = __builtin_fmaf(v[i], sc, acc[e + i]);
+    }
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const int64_t t = p.q_pos0 + (int)(tok % p.n);
+  uint16_t* orow = p.out + (tok * p.H + h) * 128 + d0;
+#pragma unroll
+  for (int e = 0; e < 32; e += 2) {
+    float o0 = acc[e] * inv, o1 = acc[e + 1] * inv;
+    if (p.rope && d0 + e >= 64) {
+      float c, s;
+      rope_cs((double)t, p.rev[(d0 + e - 64) >> 1], c, s);
+      const float r0 = o0 * c + o1 * s, r1 = o1 * c - o0 * s;
+      o0 = r0;
+      o1 = r1;
+    }
+    *(uint32_t*)(orow + e) = pack_bf16(o0, o1);
+  }
+}
+
 template <int MODE>
 static hipError_t launch_mode(const AttendParams& p, hipStream_t stream) {
   const int nht = (p.H + 15) / 16;
-  dim3 grid((unsigned)((int64_t)p.B * p.n)), block(64);
+  const bool split = MODE == 1 && p.ws != nullptr && p.parts > 1;
+  dim3 grid((unsigned)((int64_t)p.B * p.n * (split ? p.parts : 1))), block(64);
+  if (split) {
+    switch (nht) {
+      case 1: hipLaunchKernelGGL((attend_kernel<1, MODE, true>), grid, block, 0, stream, p); break;
+      case 2: hipLaunchKernelGGL((attend_kernel<2, MODE, true>), grid, block, 0, stream, p); break;
+      case 3: hipLaunchKernelGGL((attend_kernel<3, MODE, true>), grid, block, 0, stream, p); break;
+      case 4: hipLaunchKernelGGL((attend_kernel<4, MODE, true>), grid, block, 0, stream, p); break;
+      default: return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)((int64_t)p.B * p.n)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   switch (nht) {
     case 1: hipLaunchKernelGGL((attend_kernel<1, MODE>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((attend_kernel<2, MODE>), grid, block, 0, stream, p); break;
@@ -832,8 +913,25 @@ static hipError_t launch_mode(const AttendParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attend(const AttendParams& p, int mode, hipStream_t stream) {
-  if ((int64_t)p.B * p.n == 0) return hipSuccess;
+// FP8 entries with few query rows: one work-group per token would leave most
+// CUs idle, so each token's chunks are split over several work-groups.
+static int attend_parts(int mode, int B, int n, int k, int n_win) {
+  if (mode != 1 || (int64_t)B * n > 512) return 1;
+  const int chunks = (k + 31) / 32 + (n_win + 31) / 32;
+  if (chunks < 2 * kAttendChunksPerPart) return 1;
+  return (chunks + kAttendChunksPerPart - 1) / kAttendChunksPerPart;
+}
+
+size_t attend_workspace(int mode, int B, int n, int k, int n_win) {
+  const int parts = attend_parts(mode, B, n, k, n_win);
+  return parts > 1 ? (size_t)B * n * parts * kAttendPartFloats * sizeof(float) : 0;
+}
+
+hipError_t launch_attend(const AttendParams& p_in, int mode, hipStream_t stream) {
+  if ((int64_t)p_in.B * p_in.n == 0) return hipSuccess;
+  AttendParams p = p_in;
+  p.parts = attend_parts(mode, p.B, p.n, p.k, p.n_win);
+  p.cpp = kAttendChunksPerPart;
   switch (mode) {
     case 0: return launch_ring<0>(p, stream);
     case 1: return launch_mode<1>(p, stream);

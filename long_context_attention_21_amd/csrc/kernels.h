@@ -61,7 +61,17 @@ struct AttendParams {
   float qscale;       // log2(e) / sqrt(128), folded into q
   uint16_t* out;      // [B, n, H, 128]
   double rev[32];     // theta_f / (2 pi): revolutions per position
+  // split decode (FP8 entries, few query rows): `parts` work-groups per token
+  // take `cpp` chunks each and leave partial results in ws
+  float* ws;
+  int parts, cpp;
 };
+
+// Workspace of the split decode path: per (token, part) the unnormalised
+// O[64][128], then the softmax reference and the row sum of each head.
+constexpr int kAttendPartFloats = 64 * 128 + 2 * 64;
+constexpr int kAttendChunksPerPart = 8;
+size_t attend_workspace(int mode, int B, int n, int k, int n_win);
 
 // mode: 0 = CSA with bf16 entries, 1 = CSA with fp8+bf16 entries, 2 = HCA
 hipError_t launch_attend(const AttendParams& p, int mode, hipStream_t stream);

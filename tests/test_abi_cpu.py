@@ -139,7 +139,7 @@ def _attend(L, **kw):
     a = dict(q=FAKE, B=1, n=8, q_pos0=200, H=64, D=128, entries=FAKE, entries_rope=None,
              entry_scale=None, entry_fmt=0, N=50, m=4, idx=FAKE, k=16, win_kv=FAKE,
              win_pos0=73, win_len=200, n_win=128, sink=None, rope_dims=64, rope_base=10000.0,
-             out=FAKE2, stream=None)
+             out=FAKE2, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.csa_attend(*a.values())
 
@@ -225,3 +225,21 @@ def test_cache_append_needs_no_cache_between_blocks(L):
     # t = 4 completes no block (m = 4): caches may be NULL.  Validation only:
     # B = 0 launches nothing.
     assert _append(L, B=0, t=4, entries=None) == _lib.CSA_OK
+
+
+def test_attend_workspace_query(L):
+    # bf16 entries never split; FP8 entries with few rows and >= 16 chunks do
+    assert L.csa_attend_workspace_bytes(64, 1, 2048, 128, 0) == 0
+    assert L.csa_attend_workspace_bytes(64, 1, 2048, 128, 2) == 64 * 9 * 33280
+    assert L.csa_attend_workspace_bytes(64, 1, 512, 128, 2) == 64 * 3 * 33280  # 20 chunks
+    assert L.csa_attend_workspace_bytes(64, 1, 64, 128, 2) == 0       # 6 chunks: one work-group
+    assert L.csa_attend_workspace_bytes(600, 1, 2048, 128, 2) == 0    # enough rows already
+
+
+def test_attend_rejects_small_workspace(L):
+    kw = dict(B=2, n=1, q_pos0=4000, N=1000, k=2048, entry_fmt=2, entries_rope=FAKE, entry_scale=FAKE,
+              win_pos0=3873, win_len=128)
+    need = L.csa_attend_workspace_bytes(2, 1, 2048, 128, 2)
+    assert _attend(L, **kw, ws=FAKE, ws_bytes=need - 16) == _lib.CSA_WORKSPACE_TOO_SMALL
+    assert _attend(L, **kw, ws=None, ws_bytes=need) == _lib.CSA_INVALID_ARG
+    assert "ws must be" in _msg(L)

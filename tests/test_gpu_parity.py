@@ -209,6 +209,14 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
     # sink far below the scores: weights exceed the sink reference by > 2^64,
     # which forces the restart with a larger reference
     dict(B=1, n=20, H=32, q_pos0=300, m=4, mode="csa", k=40, sink_shift=-60.0, q_scale=24.0),
+    # FP8 entries with few query rows: each token's 20 chunks are split over
+    # 3 work-groups and merged
+    dict(B=3, n=2, H=64, q_pos0=2200, m=4, mode="csa", k=512, efmt="fp8", kv_scale=1.0),
+    dict(B=2, n=1, H=40, q_pos0=2200, m=4, mode="csa", k=512, efmt="fp8", kv_scale=1.0, sink=False,
+         q_scale=24.0),
+    dict(B=1, n=3, H=16, q_pos0=2200, m=4, mode="csa", k=500, efmt="fp8", kv_scale=1.0, sink_shift=-60.0,
+         q_scale=24.0),
+    dict(B=2, n=1, H=64, q_pos0=60, m=4, mode="csa", k=512, efmt="fp8", kv_scale=1.0),  # parts without keys
 ])
 def test_attend_matches_oracle(orc, case):
     print("attend case %s" % case, flush=True)
