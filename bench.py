@@ -35,12 +35,12 @@ PEAK = {"bf16": 2500.0, "fp4": 10100.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s
 # sha256 of the kernel source they were taken on: a changed kernel reports
 # null until it is measured again.
 TRAFFIC = {  # profiles/csa_prefill_128k_hbm_counters.txt
-    ("csa_attend", 3): {"sha256": "9a4a5819b599698cd5536b5362ca364b5962b86ea45f212a615147278fc6dff7",
-                        "bytes": 1.843e10},
-    ("csa_index_topk", 3): {"sha256": "268f5e31237b685af9460a786f4112011eb8dba1e2d29d683d785ceabf0e60f4",
-                            "bytes": 1.219e9},
-    ("csa_compress", 3): {"sha256": "82c3e1fea99ff0128101cd4a89cfefe6bb708f379c3a3e689974d4dc357c12da",
-                          "bytes": 7.279e7},
+    ("csa_attend", 3): {"sha256": "d2b79735b286193d92301ee488cc90676415c17ee74511916df725a7bdac664a",
+                        "bytes": 1.892e10},
+    ("csa_index_topk", 3): {"sha256": "ada64fe8f93a0955d7ff56bda206aa179d0e7c562b8687c43a7f870c6ba6fe35",
+                            "bytes": 1.223e9},
+    ("csa_compress", 3): {"sha256": "2fed75a38f059725fadc6fcd774c1ecff134c35a77219ff3ac6f1019203b2a06",
+                          "bytes": 7.296e7},
 }
 KERNEL_SOURCE = {"csa_compress": "compress.hip", "hca_compress": "compress.hip", "csa_index_topk": "index_topk.hip",
                  "csa_attend": "attend.hip", "hca_attend": "attend.hip"}

@@ -843,19 +843,18 @@ static hipError_t launch_ring(const AttendParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Split decode, second kernel: per token, thread (head h, 32 dims) merges
-// the parts in ascending order: O = sum_p O_p 2^(m_p - M), L likewise, with
-// M the largest part reference; then normalise, inverse RoPE, store bf16.
+// Split decode, second kernel: work-group (token, 8 heads), thread (head h,
+// 4 dims) merges the parts in ascending order: O = sum_p O_p 2^(m_p - M), L
+// likewise, with M the largest part reference; then normalise, inverse
+// RoPE, store bf16.
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p) {
-  const int64_t tok = blockIdx.x;
-  const int h = threadIdx.x >> 2, d0 = (threadIdx.x & 3) * 32;
+  const int64_t tok = blockIdx.x >> 3;
+  const int h = (int)(blockIdx.x & 7) * 8 + (threadIdx.x >> 5), d0 = (threadIdx.x & 31) * 4;
   if (h >= p.H) return;
-  const float* w0 = p.ws + (int64_t)tok * p.parts * kAttendPartFloats;
+  const float* w0 = p.ws + tok * p.parts * kAttendPartFloats;
   float M = -__builtin_inff();
   for (int q = 0; q < p.parts; ++q) M = fmaxf(M, w0[q * kAttendPartFloats + 64 * 128 + h]);
-  float acc[32];
-#pragma unroll
-  for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float L = 0.0f;
   for (int q = 0; q < p.parts; ++q) {
     const float* w = w0 + q * kAttendPartFloats;
@@ -863,28 +862,26 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p) {
     if (!(lq > 0.0f)) continue;  // no keys and no sink in this part
     const float sc = __builtin_amdgcn_exp2f(w[64 * 128 + h] - M);
     L = __builtin_fmaf(lq, sc, L);
+    const f32x4 v = *(const f32x4*)(w + h * 128 + d0);
 #pragma unroll
-    for (int e = 0; e < 32; e += 4) {
-      const f32x4 v = *(const f32x4*)(w + h * 128 + d0 + e);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[e + i] = __builtin_fmaf(v[i], sc, acc[e + i]);
-    }
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(v[i], sc, acc[i]);
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const int64_t t = p.q_pos0 + (int)(tok % p.n);
-  uint16_t* orow = p.out + (tok * p.H + h) * 128 + d0;
+  uint32_t o[2];
 #pragma unroll
-  for (int e = 0; e < 32; e += 2) {
+  for (int e = 0; e < 4; e += 2) {
     float o0 = acc[e] * inv, o1 = acc[e + 1] * inv;
-    if (p.rope && d0 + e >= 64) {
+    if (p.rope && d0 >= 64) {
       float c, s;
       rope_cs((double)t, p.rev[(d0 + e - 64) >> 1], c, s);
       const float r0 = o0 * c + o1 * s, r1 = o1 * c - o0 * s;
       o0 = r0;
       o1 = r1;
     }
-    *(uint32_t*)(orow + e) = pack_bf16(o0, o1);
+    o[e >> 1] = pack_bf16(o0, o1);
   }
+  *(uint2*)(p.out + (tok * p.H + h) * 128 + d0) = make_uint2(o[0], o[1]);
 }
 
 template <int MODE>
@@ -900,7 +897,7 @@ static hipError_t launch_mode(const AttendParams& p, hipStream_t stream) {
       case 4: hipLaunchKernelGGL((attend_kernel<4, MODE, true>), grid, block, 0, stream, p); break;
       default: return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)((int64_t)p.B * p.n)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)((int64_t)p.B * p.n * 8)), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
   switch (nht) {
