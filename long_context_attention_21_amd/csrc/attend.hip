@@ -433,6 +433,33 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
 // 4q + h holds key 8h + q of the chunk, so a lane fetches the indices of 8
 // consecutive keys.
 constexpr int kRing = 3;
+
+// Buffer descriptor words (base, stride 0, byte extent, 32-bit data format):
+// reads past the extent return zeros.
+__device__ __forceinline__ u32x4 dma_rsrc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
+}
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes at `voff` land at
+// LDS address lds + 16 l.  Issued from inline asm so that the compiler does
+// not track it: otherwise it makes every LDS read wait for all outstanding
+// loads (vmcnt(0)), including the prefetch of the chunks ahead, which
+// serialises the ring.  The caller waits with s_waitcnt vmcnt and a barrier
+// before it reads the slot.  M0 carries the LDS address; the leading
+// s_nop 4 covers an M0 or descriptor write just before the load.
+__device__ __forceinline__ void dma_b128(const u32x4& r, uint32_t lds, int voff) {
+  u32x4 rs;  // wave-uniform: make that explicit so it is taken from SGPRs
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rs[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)r[i]);
+  asm volatile(
+      "s_nop 4\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "{m0}"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rs)
+      : "memory");
+}
+
 template <bool B>
 struct PassTag {
   static constexpr bool value = B;
@@ -440,14 +467,22 @@ struct PassTag {
 
 __device__ __forceinline__ int ring_key(int r) { return 8 * (r & 3) + (r >> 2); }  // key of ring row r
 
+template <int S>
+struct SlotTag {
+  static constexpr int value = S;
+};
+
 template <int NHT, int NW, int MODE>  // MODE 0: CSA bf16 entries, 2: HCA
 __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kRing][32 * 256];
-  __shared__ __attribute__((aligned(16))) int32_t Is[MODE == 2 ? 4 : kMaxK];  // the token's idx row
+  // CSA: the token's idx row, padded with -1 up to a multiple of 32
+  __shared__ __attribute__((aligned(16))) int32_t Is[MODE == 2 ? 4 : kMaxK];
   __shared__ float2 Rt[32];    // (cos, sin) of the token's angle t * theta_f, f = 0..31
   __shared__ float Rv[32];     // theta_f / 2pi (revolutions per position)
   __shared__ int flag[2][NW];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int first_bad[NW];  // per wave: first idx position holding a missing key
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t tok = blockIdx.x;  // b * n + q
   const int b = (int)(tok / p.n);
@@ -465,13 +500,25 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     Rt[tid] = make_float2(cs, sn);
     Rv[tid] = (float)p.rev[tid];
   }
+  const int kpad = (p.k + 31) & ~31;  // <= kMaxK (a multiple of 32)
   if (MODE == 0) {
     const int32_t* irow = p.idx + tok * p.k;
-    if ((p.k & 3) == 0) {
-      for (int i = 4 * tid; i < p.k; i += 256 * NW) *(u32x4*)&Is[i] = *(const u32x4*)&irow[i];
-    } else {
-      for (int i = tid; i < p.k; i += 64 * NW) Is[i] = irow[i];
+    int fb = kpad;
+    for (int i = 4 * tid; i < kpad; i += 256 * NW) {
+      u32x4 v;
+      if ((p.k & 3) == 0 && i < p.k) {
+        v = *(const u32x4*)&irow[i];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = i + e < p.k ? (uint32_t)irow[i + e] : 0xffffffffu;
+      }
+      *(u32x4*)&Is[i] = v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((int)v[e] < 0 && i + e < fb) fb = i + e;
     }
+    for (int off = 32; off >= 1; off >>= 1) fb = min(fb, __shfl_xor(fb, off));
+    if (lane == 0) first_bad[wave] = fb;
   }
   __syncthreads();
 
@@ -513,7 +560,18 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   } else {
     n_ent = p.k;
   }
+  n_ent = __builtin_amdgcn_readfirstlane(n_ent);  // uniform: keep the loop control scalar
   const int n_ent_chunks = (n_ent + 31) >> 5;
+  // chunks before n_full hold 32 present keys each (no mask to form)
+  int n_full;
+  if (MODE == 2) {
+    n_full = n_ent >> 5;
+  } else {
+    int fb = first_bad[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) fb = min(fb, first_bad[w]);
+    n_full = __builtin_amdgcn_readfirstlane(fb) >> 5;
+  }
   int64_t j0 = 0;
   int n_wk = 0;
   if (p.n_win > 0) {
@@ -521,8 +579,9 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     if (j0 < 0) j0 = 0;
     n_wk = (int)(t - j0 + 1);
   }
+  n_wk = __builtin_amdgcn_readfirstlane(n_wk);
   const int n_chunks = n_ent_chunks + ((n_wk + 31) >> 5);
-  const int dt0 = (int)(t - j0);  // t - j of window key 0
+  const int dt0 = __builtin_amdgcn_readfirstlane((int)(t - j0));  // t - j of window key 0
 
   auto uniform_ptr = [](const void* ptr) {
     const uint64_t v = (uint64_t)ptr;
@@ -530,33 +589,34 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
     return (void*)(((uint64_t)hi << 32) | lo);
   };
-  constexpr int kOOB = 0x7fff0000;  // past every row source (the host bounds them below this)
   const int bu = __builtin_amdgcn_readfirstlane(b);
-  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(p.win ? p.win + (int64_t)bu * p.win_len * 128 : p.q), (short)0,
-      p.win ? __builtin_amdgcn_readfirstlane(p.win_len * 256) : 0, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rE = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(p.entries + (int64_t)bu * p.N * 128), (short)0, __builtin_amdgcn_readfirstlane(p.N * 256),
-      0x00020000);
-  const int win_row0 = (int)(j0 - p.win_pos0);  // window source row of key j0
+  const u32x4 rW = dma_rsrc(uniform_ptr(p.win ? p.win + (int64_t)bu * p.win_len * 128 : p.q),
+                            p.win ? __builtin_amdgcn_readfirstlane(p.win_len * 256) : 0);
+  const u32x4 rE = dma_rsrc(uniform_ptr(p.entries + (int64_t)bu * p.N * 128), __builtin_amdgcn_readfirstlane(p.N * 256));
+  const int win_row0 = __builtin_amdgcn_readfirstlane((int)(j0 - p.win_pos0));  // window source row of key j0
 
   // This wave's share of the loads of chunk c into ring slot `slot`: load
-  // instructions q = wave*QPW .. +QPW-1, each 4 rows.  Always issued: missing
-  // keys and chunks past the end read as zeros.
+  // instructions q = wave*QPW .. +QPW-1, each 4 rows.  Always issued: a
+  // missing key has row -1, whose offset (0xffffff00 + piece) lies past every
+  // row source and reads as zeros; so do chunks past the end.
   constexpr int QPW = 8 / NW;
   const int hq = lane >> 4;
+  uint32_t colq[QPW];  // this lane's piece offset in load q (XOR swizzle of ring row 4q + hq)
+#pragma unroll
+  for (int e = 0; e < QPW; ++e) colq[e] = (uint32_t)(((lane & 15) ^ ((4 * (wave * QPW + e) + hq) & 15)) << 4);
+  const uint32_t ks_lds = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)((uint32_t)(uintptr_t)LDS_PTR(uint8_t, &Ks[0][0]) + (uint32_t)(wave * QPW * 1024)));
   auto issue = [&](int c, int slot) {
     int rows[QPW];
     const int kb0 = c * 32 + 8 * hq + wave * QPW;  // key of this lane's first row
     if (c < n_ent_chunks) {
       if constexpr (MODE == 0) {
-        // kb0 is a multiple of 4 and kb0 + QPW <= 32 * n_ent_chunks <= kMaxK:
-        // 16-byte reads inside the index row (entries past k are not used)
+        // kb0 + QPW <= 32 * n_ent_chunks = kpad: inside the padded row
 #pragma unroll
         for (int e0 = 0; e0 < QPW; e0 += 4) {
           const u32x4 v = *(const u32x4*)&Is[kb0 + e0];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) rows[e0 + e] = kb0 + e0 + e < p.k ? (int)v[e] : -1;
+          for (int e = 0; e < 4; ++e) rows[e0 + e] = (int)v[e];
         }
       } else {
 #pragma unroll
@@ -569,25 +629,21 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
         rows[e] = (c < n_chunks && wj < n_wk) ? win_row0 + wj : -1;
       }
     }
-    const __amdgpu_buffer_rsrc_t rs = c < n_ent_chunks ? rE : rW;
+    const u32x4 rs = c < n_ent_chunks ? rE : rW;
 #pragma unroll
-    for (int e = 0; e < QPW; ++e) {
-      const int q = wave * QPW + e;
-      const int r = 4 * q + hq;
-      const int col = (lane & 15) ^ (r & 15);
-      const int off = rows[e] >= 0 ? rows[e] * 256 + col * 16 : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, &Ks[slot][q * 1024]), 16, off, 0, 0, 0);
-    }
+    for (int e = 0; e < QPW; ++e)
+      dma_b128(rs, ks_lds + (uint32_t)(slot * 8192 + e * 1024), (int)(((uint32_t)rows[e] << 8) | colq[e]));
   };
   // validity of ring rows r = 0..31 of chunk c (bit r)
   auto chunk_mask = [&](int c) -> uint32_t {
+    if (c < n_full) return 0xffffffffu;
     const int r = lane & 31;
     const int kk = ring_key(r);
     bool v = false;
     if (c < n_ent_chunks) {
       const int e = c * 32 + kk;
       if (MODE == 2) v = e < n_ent;
-      else v = e < p.k && Is[e < p.k ? e : 0] >= 0;
+      else v = Is[e] >= 0;  // e < kpad; the padding is -1
     } else if (c < n_chunks) {
       v = (c - n_ent_chunks) * 32 + kk < n_wk;
     }
@@ -605,12 +661,13 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     return a;
   };
   // wait for chunk c's rows (this wave's loads: only chunk c+1's may still be
-  // outstanding); the barrier makes every wave's loads visible and ends all
-  // reads of chunk c-1, whose slot is refilled right after
+  // outstanding); with several waves the barrier makes every wave's loads
+  // visible and ends all reads of chunk c-1, whose slot is refilled right
+  // after.  A single wave orders its own LDS accesses.
   auto arrive = [&]() {
     if constexpr (NW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    __syncthreads();
+    if constexpr (NW > 1) __syncthreads();
   };
   // Window chunk c: rotate its rows in place in the ring (dims 64..127 of
   // each key at its position j = t - d).  R(j) = R(t) R(-d) with d in
@@ -675,12 +732,12 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) O[dt][ht] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    issue(0, 0);
-    issue(1, 1);
-    int slot = 0, slot_next = 2;
-    for (int c = 0; c < n_chunks; ++c) {
+    // chunk c in ring slot c % kRing; the loop is unrolled kRing times so that
+    // every slot address is a constant
+    auto body = [&](int c, auto tag) {
+      constexpr int slot = decltype(tag)::value;
       arrive();
-      issue(c + 2, slot_next);
+      issue(c + 2, (slot + 2) % kRing);
       const uint8_t* kb = &Ks[slot][0];
       const uint32_t msk = chunk_mask(c);
       if (c >= n_ent_chunks && p.rope) {
@@ -710,38 +767,51 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) P[ht][kt * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(S[kt][ht][i]);
+      // ---- O^T += V^T P^T (V^T by transposing LDS reads); L += 1^T P^T
+      auto pv = [&](const bf16x8 (&Pw)[NHT]) {
+        const int vrow = 4 * g + (l16 >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int piece = ((dt * 2 + ((l16 & 3) >> 1)) ^ vrow) & 15;  // (vrow + 16) & 15 == vrow & 15
+          const int boff = (piece << 4) + ((l16 & 1) << 3);
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, kb + vrow * 256 + boff));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, kb + (vrow + 16) * 256 + boff));
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht)
+            O[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Pw[ht], O[dt][ht], 0, 0, 0);
+        }
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+          Lacc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, Pw[ht], Lacc[ht], 0, 0, 0);
+      };
       if (msk != 0xffffffffu) {
-        // missing keys get weight 0 (their rows are zero, but the weight
-        // must not reach the row sums, nor be inf next to a zero value)
         u32x4 keepw;
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) {
-          const int e = 2 * w2;  // elements e, e+1 <-> rows (e>>2)*16 + 4g + (e&3), +1
+          const int e = 2 * w2;
           const int r0 = (e >> 2) * 16 + 4 * g + (e & 3);
           keepw[w2] = (((msk >> r0) & 1u) ? 0x0000ffffu : 0u) | (((msk >> (r0 + 1)) & 1u) ? 0xffff0000u : 0u);
         }
+        // in place (tied asm operands): the weights stay in the registers the
+        // unmasked path uses, so the common path copies nothing
 #pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) P[ht] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, P[ht]) & keepw);
+        for (int ht = 0; ht < NHT; ++ht) {
+          u32x4 pu = __builtin_bit_cast(u32x4, P[ht]);
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) asm volatile("v_and_b32 %0, %0, %1" : "+v"(pu[w2]) : "v"(keepw[w2]));
+          P[ht] = __builtin_bit_cast(bf16x8, pu);
+        }
       }
-
-      // ---- O^T += V^T P^T (V^T by transposing LDS reads); L += 1^T P^T
-      const int vrow = 4 * g + (l16 >> 2);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int piece = ((dt * 2 + ((l16 & 3) >> 1)) ^ vrow) & 15;  // (vrow + 16) & 15 == vrow & 15
-        const int boff = (piece << 4) + ((l16 & 1) << 3);
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, kb + vrow * 256 + boff));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, kb + (vrow + 16) * 256 + boff));
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht)
-          O[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, P[ht], O[dt][ht], 0, 0, 0);
-      }
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht)
-        Lacc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, P[ht], Lacc[ht], 0, 0, 0);
-      slot = slot == kRing - 1 ? 0 : slot + 1;
-      slot_next = slot_next == kRing - 1 ? 0 : slot_next + 1;
+      pv(P);
+    };
+    static_assert(kRing == 3, "the chunk loop is unrolled over 3 ring slots");
+    issue(0, 0);
+    issue(1, 1);
+    for (int c = 0; c < n_chunks; c += 3) {
+      body(c, SlotTag<0>{});
+      if (c + 1 < n_chunks) body(c + 1, SlotTag<1>{});
+      if (c + 2 < n_chunks) body(c + 2, SlotTag<2>{});
     }
     // every load into the ring has landed before the ring is reused or released
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
