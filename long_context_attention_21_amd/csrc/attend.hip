@@ -606,8 +606,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   for (int e = 0; e < QPW; ++e) colq[e] = (uint32_t)(((lane & 15) ^ ((4 * (wave * QPW + e) + hq) & 15)) << 4);
   const uint32_t ks_lds = (uint32_t)__builtin_amdgcn_readfirstlane(
       (int)((uint32_t)(uintptr_t)LDS_PTR(uint8_t, &Ks[0][0]) + (uint32_t)(wave * QPW * 1024)));
-  auto issue = [&](int c, int slot) {
-    int rows[QPW];
+  auto chunk_rows = [&](int c, int (&rows)[QPW]) {
     const int kb0 = c * 32 + 8 * hq + wave * QPW;  // key of this lane's first row
     if (c < n_ent_chunks) {
       if constexpr (MODE == 0) {
@@ -629,10 +628,17 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
         rows[e] = (c < n_chunks && wj < n_wk) ? win_row0 + wj : -1;
       }
     }
+  };
+  auto issue_rows = [&](int c, int slot, const int (&rows)[QPW]) {
     const u32x4 rs = c < n_ent_chunks ? rE : rW;
 #pragma unroll
     for (int e = 0; e < QPW; ++e)
       dma_b128(rs, ks_lds + (uint32_t)(slot * 8192 + e * 1024), (int)(((uint32_t)rows[e] << 8) | colq[e]));
+  };
+  auto issue = [&](int c, int slot) {
+    int rows[QPW];
+    chunk_rows(c, rows);
+    issue_rows(c, slot, rows);
   };
   // validity of ring rows r = 0..31 of chunk c (bit r)
   auto chunk_mask = [&](int c) -> uint32_t {
@@ -734,18 +740,23 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     }
     // chunk c in ring slot c % kRing; the loop is unrolled kRing times so that
     // every slot address is a constant
+    // The rows of chunk c+2's loads were read from the index row one chunk
+    // earlier, so the loads issue without waiting on LDS; the K reads of the
+    // chunk go out first.
+    int rows_next[QPW];
     auto body = [&](int c, auto tag) {
       constexpr int slot = decltype(tag)::value;
       arrive();
-      issue(c + 2, (slot + 2) % kRing);
       const uint8_t* kb = &Ks[slot][0];
-      const uint32_t msk = chunk_mask(c);
       if (c >= n_ent_chunks && p.rope) {
         rotate_window(c, slot);
         __syncthreads();  // rotated rows visible to every wave
       }
       bf16x8 K[2][4];
       load_k(kb, K);
+      issue_rows(c + 2, (slot + 2) % kRing, rows_next);
+      chunk_rows(c + 3, rows_next);
+      const uint32_t msk = chunk_mask(c);
 
       // ---- S^T = K Q^T - mref; weights exp2
       f32x4 S[2][NHT];
@@ -808,6 +819,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     static_assert(kRing == 3, "the chunk loop is unrolled over 3 ring slots");
     issue(0, 0);
     issue(1, 1);
+    chunk_rows(2, rows_next);
     for (int c = 0; c < n_chunks; c += 3) {
       body(c, SlotTag<0>{});
       if (c + 1 < n_chunks) body(c + 1, SlotTag<1>{});
