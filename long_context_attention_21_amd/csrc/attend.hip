@@ -472,33 +472,45 @@ struct SlotTag {
   static constexpr int value = S;
 };
 
-template <int NHT, int NW, int MODE>  // MODE 0: CSA bf16 entries, 2: HCA
+// TOK query tokens per work-group (HCA only: they see the same entries and
+// nearly the same window, so one ring serves them all); NW / TOK waves per
+// token.
+template <int NHT, int NW, int MODE, int TOK = 1>  // MODE 0: CSA bf16 entries, 2: HCA
 __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
+  static_assert(MODE == 2 || TOK == 1, "CSA tokens have their own key sets");
+  constexpr int WPT = NW / TOK;  // waves per token
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kRing][32 * 256];
   // CSA: the token's idx row, padded with -1 up to a multiple of 32
   __shared__ __attribute__((aligned(16))) int32_t Is[MODE == 2 ? 4 : kMaxK];
-  __shared__ float2 Rt[32];    // (cos, sin) of the token's angle t * theta_f, f = 0..31
-  __shared__ float Rv[32];     // theta_f / 2pi (revolutions per position)
+  __shared__ float2 Rt[TOK][32];  // (cos, sin) of each token's angle t * theta_f, f = 0..31
+  __shared__ float Rv[32];        // theta_f / 2pi (revolutions per position)
   __shared__ int flag[2][NW];
   __shared__ int first_bad[NW];  // per wave: first idx position holding a missing key
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  const int64_t tok = blockIdx.x;  // b * n + q
-  const int b = (int)(tok / p.n);
-  const int qi = (int)(tok % p.n);
+  const int nq = (p.n + TOK - 1) / TOK;  // work-groups per batch row
+  const int b = (int)(blockIdx.x / nq);
+  const int q_first = (int)(blockIdx.x % nq) * TOK;
+  const int q_last = min(q_first + TOK, p.n) - 1;
+  const int tw = wave / WPT;  // this wave's token slot
+  const bool active = q_first + tw < p.n;
+  const int qi = min(q_first + tw, p.n - 1);
+  const int64_t tok = (int64_t)b * p.n + qi;
   const int64_t t = p.q_pos0 + qi;
+  const int64_t t0 = p.q_pos0 + q_first, t_last = p.q_pos0 + q_last;
   const float LOG2E = 1.4426950408889634f;
-  const int h0 = wave * NHT * 16;  // first head of this wave
+  const int h0 = (wave % WPT) * NHT * 16;  // first head of this wave
 
-  // ---- the token's rotation (angle formed in fp64) and the index row (CSA).
+  // ---- the tokens' rotations (angle formed in fp64) and the index row (CSA).
   // The ring needs no clearing: every chunk's loads rewrite all 32 rows (a
   // missing key's row reads as zeros).
-  if (tid < 32 && p.rope) {
+  if (tid < 32 * TOK && p.rope) {
+    const int ts = tid >> 5, f = tid & 31;
     float cs, sn;
-    rope_cs((double)t, p.rev[tid], cs, sn);
-    Rt[tid] = make_float2(cs, sn);
-    Rv[tid] = (float)p.rev[tid];
+    rope_cs((double)(p.q_pos0 + min(q_first + ts, p.n - 1)), p.rev[f], cs, sn);
+    Rt[ts][f] = make_float2(cs, sn);
+    if (ts == 0) Rv[f] = (float)p.rev[f];
   }
   const int kpad = (p.k + 31) & ~31;  // <= kMaxK (a multiple of 32)
   if (MODE == 0) {
@@ -537,7 +549,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
         if (p.rope && ks >= 2) {
 #pragma unroll
           for (int pp = 0; pp < 4; ++pp) {
-            const float2 r = Rt[(ks - 2) * 16 + 4 * g + pp];
+            const float2 r = Rt[tw][(ks - 2) * 16 + 4 * g + pp];
             const float a0 = x[2 * pp], a1 = x[2 * pp + 1];
             x[2 * pp] = a0 * r.x - a1 * r.y;
             x[2 * pp + 1] = a0 * r.y + a1 * r.x;
@@ -552,20 +564,24 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     }
   }
 
-  // ---- key sequence: entry chunks, then window chunks
-  int n_ent;
+  // ---- key sequence of the work-group: entry chunks, then window chunks
+  // (with several tokens: the entries of the last one and the union of the
+  // windows; each wave masks what its own token does not see)
+  int n_ent, n_ent_tok;
   if (MODE == 2) {
-    const int64_t nv = (t + 1) / p.m;
+    const int64_t nv = (t_last + 1) / p.m, nt = (t + 1) / p.m;
     n_ent = (int)(nv < p.N ? nv : p.N);
+    n_ent_tok = (int)(nt < p.N ? nt : p.N);
   } else {
-    n_ent = p.k;
+    n_ent = n_ent_tok = p.k;
   }
   n_ent = __builtin_amdgcn_readfirstlane(n_ent);  // uniform: keep the loop control scalar
+  n_ent_tok = __builtin_amdgcn_readfirstlane(n_ent_tok);
   const int n_ent_chunks = (n_ent + 31) >> 5;
-  // chunks before n_full hold 32 present keys each (no mask to form)
+  // chunks before n_full hold 32 keys present for this wave's token (no mask to form)
   int n_full;
   if (MODE == 2) {
-    n_full = n_ent >> 5;
+    n_full = n_ent_tok >> 5;
   } else {
     int fb = first_bad[0];
 #pragma unroll
@@ -573,15 +589,21 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     n_full = __builtin_amdgcn_readfirstlane(fb) >> 5;
   }
   int64_t j0 = 0;
-  int n_wk = 0;
+  int n_wk = 0, wlo = 0, whi = -1;
   if (p.n_win > 0) {
-    j0 = t - p.n_win + 1;
+    j0 = t0 - p.n_win + 1;
     if (j0 < 0) j0 = 0;
-    n_wk = (int)(t - j0 + 1);
+    n_wk = (int)(t_last - j0 + 1);
+    // this token's window keys j in [max(0, t - n_win + 1), t], as offsets from j0
+    const int64_t jl = t - p.n_win + 1;
+    wlo = (int)((jl < 0 ? 0 : jl) - j0);
+    whi = (int)(t - j0);
   }
   n_wk = __builtin_amdgcn_readfirstlane(n_wk);
+  wlo = __builtin_amdgcn_readfirstlane(wlo);
+  whi = __builtin_amdgcn_readfirstlane(whi);
   const int n_chunks = n_ent_chunks + ((n_wk + 31) >> 5);
-  const int dt0 = __builtin_amdgcn_readfirstlane((int)(t - j0));  // t - j of window key 0
+  const int dt0 = __builtin_amdgcn_readfirstlane((int)(t0 - j0));  // t0 - j of window key 0
 
   auto uniform_ptr = [](const void* ptr) {
     const uint64_t v = (uint64_t)ptr;
@@ -648,10 +670,11 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     bool v = false;
     if (c < n_ent_chunks) {
       const int e = c * 32 + kk;
-      if (MODE == 2) v = e < n_ent;
+      if (MODE == 2) v = e < n_ent_tok;
       else v = Is[e] >= 0;  // e < kpad; the padding is -1
     } else if (c < n_chunks) {
-      v = (c - n_ent_chunks) * 32 + kk < n_wk;
+      const int wj = (c - n_ent_chunks) * 32 + kk;
+      v = wj >= wlo && wj <= whi;
     }
     return (uint32_t)__builtin_amdgcn_ballot_w64(v && lane < 32);
   };
@@ -671,7 +694,9 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   // visible and ends all reads of chunk c-1, whose slot is refilled right
   // after.  A single wave orders its own LDS accesses.
   auto arrive = [&]() {
-    if constexpr (NW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    static_assert(QPW == 8 || QPW == 4 || QPW == 2, "loads per wave and chunk");
+    if constexpr (QPW == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if constexpr (QPW == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     if constexpr (NW > 1) __syncthreads();
   };
@@ -691,8 +716,8 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
         float rv = d * Rv[f];
         rv = rv - __builtin_floorf(rv);
         const float sd = __builtin_amdgcn_sinf(rv), cd = __builtin_amdgcn_cosf(rv);
-        const float2 rt = Rt[f];
-        const float cs = rt.x * cd + rt.y * sd, sn = rt.y * cd - rt.x * sd;  // angle t - d
+        const float2 rt = Rt[0][f];
+        const float cs = rt.x * cd + rt.y * sd, sn = rt.y * cd - rt.x * sd;  // angle t0 - d
         const float a0 = bf16lo(w[e]), a1 = bf16hi(w[e]);
         w[e] = pack_bf16(a0 * cs - a1 * sn, a0 * sn + a1 * cs);
       }
@@ -890,14 +915,14 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     const int h = h0 + ht * 16 + l16;
     const float L = Lacc[ht][0];
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    if (h >= p.H) continue;
+    if (h >= p.H || !active) continue;
     uint16_t* orow = p.out + (tok * p.H + h) * 128;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       float o0 = O[dt][ht][0] * inv, o1 = O[dt][ht][1] * inv;
       float o2 = O[dt][ht][2] * inv, o3 = O[dt][ht][3] * inv;
       if (p.rope && dt >= 4) {
-        const float2 r0c = Rt[8 * (dt - 4) + 2 * g], r1c = Rt[8 * (dt - 4) + 2 * g + 1];
+        const float2 r0c = Rt[tw][8 * (dt - 4) + 2 * g], r1c = Rt[tw][8 * (dt - 4) + 2 * g + 1];
         const float r0 = o0 * r0c.x + o1 * r0c.y, r1 = o1 * r0c.x - o0 * r0c.y;
         const float r2 = o2 * r1c.x + o3 * r1c.y, r3 = o3 * r1c.x - o2 * r1c.y;
         o0 = r0; o1 = r1; o2 = r2; o3 = r3;
@@ -913,13 +938,29 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
 template <int MODE>
 static hipError_t launch_ring(const AttendParams& p, hipStream_t stream) {
   const int nht = (p.H + 15) / 16;
-  dim3 grid((unsigned)((int64_t)p.B * p.n));
+  const int64_t bn = (int64_t)p.B * p.n;
+  // HCA: two tokens per work-group share the ring when every token sees at
+  // least 512 entries (the pair's one extra window chunk is then a small
+  // price for halving the row loads) and enough work-groups remain to fill
+  // the chip
+  int64_t ent0 = p.m > 0 ? (p.q_pos0 + 1) / p.m : 0;
+  if (ent0 > p.N) ent0 = p.N;
+  const bool pair = MODE == 2 && nht > 2 && bn >= 4096 && ent0 >= 512;
+  dim3 grid((unsigned)(pair ? (int64_t)p.B * ((p.n + 1) / 2) : bn));
   // up to 32 heads: one wave; more: two waves of up to 32 heads each
   switch (nht) {
     case 1: hipLaunchKernelGGL((attend_ring_kernel<1, 1, MODE>), grid, dim3(64), 0, stream, p); break;
     case 2: hipLaunchKernelGGL((attend_ring_kernel<2, 1, MODE>), grid, dim3(64), 0, stream, p); break;
     case 3:
-    case 4: hipLaunchKernelGGL((attend_ring_kernel<2, 2, MODE>), grid, dim3(128), 0, stream, p); break;
+    case 4:
+      if constexpr (MODE == 2) {
+        if (pair) {
+          hipLaunchKernelGGL((attend_ring_kernel<2, 4, MODE, 2>), grid, dim3(256), 0, stream, p);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((attend_ring_kernel<2, 2, MODE>), grid, dim3(128), 0, stream, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -154,7 +154,7 @@ def test_index_topk_matches_oracle(orc, B, n, N, H_I, k, q_pos0, fmt, extra):
 # ----------------------------------------------------------------- attention --
 
 def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True, q_scale=1.0,
-                 efmt="bf16", kv_scale=None, sink_shift=0.0):
+                 efmt="bf16", kv_scale=None, sink_shift=0.0, check_rows=None):
     rng = np.random.default_rng(seed)
     T = q_pos0 + n
     kv_scale = kv_scale or 1 / np.sqrt(128)
@@ -189,11 +189,13 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
                            sink=dev(sk) if sink else None)
     torch.cuda.synchronize()
     got = host_bits(out)
+    if check_rows is not None:
+        rows = np.asarray(check_rows, np.int32)
     for b in range(B):
         ref = orc.attend_rows(q[b], q_pos0, ents[b]["entries_f64"], m, rows, mode,
-                              idx=None if idx is None else idx[b], win=kv[b] if n_win else None,
+                              idx=None if idx is None else idx[b][rows], win=kv[b] if n_win else None,
                               win_pos0=0, n_win=n_win, sink=sk)
-        assert_close(got[b], ref, "batch %d" % b)
+        assert_close(got[b][rows], ref, "batch %d" % b)
     return got
 
 
@@ -221,6 +223,21 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
 def test_attend_matches_oracle(orc, case):
     print("attend case %s" % case, flush=True)
     _attend_case(orc, 11, **case)
+
+
+def test_hca_two_token_work_groups(orc):
+    """HCA with at least 4096 query rows, more than 32 heads and at least
+    512 entries visible to every row runs two tokens per work-group: one key
+    ring for both, the union of their windows, each token masking what it
+    does not see.  An odd row count leaves the last work-group a single
+    token.  The first and last rows, the rows around entry-block boundaries
+    and a random sample are checked against the oracle."""
+    n, m = 2049, 8
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(n - 40, n), np.arange(m - 3, 4 * m + 3),
+                                     rng.choice(n, 60, replace=False)]))
+    print("hca two-token work-groups", flush=True)
+    _attend_case(orc, 12, B=2, n=n, H=40, q_pos0=4200, m=m, mode="hca", check_rows=rows)
 
 
 def test_attend_deterministic_and_batch_invariant(orc):
