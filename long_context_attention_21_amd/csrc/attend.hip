@@ -514,36 +514,68 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   }
   const int kpad = (p.k + 31) & ~31;  // <= kMaxK (a multiple of 32)
   if (MODE == 0) {
+    // every load is issued before the first is used (addresses clamped into
+    // the row; positions past k become -1)
     const int32_t* irow = p.idx + tok * p.k;
-    int fb = kpad;
-    for (int i = 4 * tid; i < kpad; i += 256 * NW) {
-      u32x4 v;
-      if ((p.k & 3) == 0 && i < p.k) {
-        v = *(const u32x4*)&irow[i];
-      } else {
+    constexpr int kIt = kMaxK / (256 * NW);
+    u32x4 v[kIt];
+    if (p.k > 0 && (p.k & 3) == 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = i + e < p.k ? (uint32_t)irow[i + e] : 0xffffffffu;
+      for (int it = 0; it < kIt; ++it) {
+        const int i = 4 * tid + it * 256 * NW;
+        const u32x4 x = *(const u32x4*)&irow[min(i, p.k - 4)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[it][e] = i < p.k ? x[e] : 0xffffffffu;
       }
-      *(u32x4*)&Is[i] = v;
+    } else if (p.k > 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((int)v[e] < 0 && i + e < fb) fb = i + e;
+      for (int it = 0; it < kIt; ++it) {
+        const int i = 4 * tid + it * 256 * NW;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = (uint32_t)irow[min(i + e, p.k - 1)];
+          v[it][e] = i + e < p.k ? x : 0xffffffffu;
+        }
+      }
+    }
+    int fb = kpad;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int i = 4 * tid + it * 256 * NW;
+      if (i < kpad) {
+        *(u32x4*)&Is[i] = v[it];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((int)v[it][e] < 0 && i + e < fb) fb = i + e;
+      }
     }
     for (int off = 32; off >= 1; off >>= 1) fb = min(fb, __shfl_xor(fb, off));
     if (lane == 0) first_bad[wave] = fb;
   }
   __syncthreads();
 
-  // ---- Q^T operand: lane l holds head h0 + ht*16 + l16, dims ks*32 + 8g .. +7
+  // ---- Q^T operand: lane l holds head h0 + ht*16 + l16, dims ks*32 + 8g .. +7.
+  // Every load is issued before the first is used (one memory round trip):
+  // lanes past the last head read head H-1 and use zeros.
   bf16x8 Q[NHT][4];
+  u32x4 qraw[NHT][4];
+  float skv[NHT];  // the heads' sink logits (0 past the last head)
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int hc = min(h0 + ht * 16 + l16, p.H - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qraw[ht][ks] = *(const u32x4*)(p.q + ((tok * p.H + hc) * 128 + ks * 32 + 8 * g));
+    skv[ht] = p.sink ? p.sink[hc] : 0.0f;
+  }
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
     const int h = h0 + ht * 16 + l16;
+    if (h >= p.H) skv[ht] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       float x[8];
       if (h < p.H) {
-        const u32x4 v = *(const u32x4*)(p.q + ((tok * p.H + h) * 128 + ks * 32 + 8 * g));
+        const u32x4 v = qraw[ht][ks];
 #pragma unroll
         for (int e = 0; e < 4; ++e) { x[2 * e] = bf16lo(v[e]); x[2 * e + 1] = bf16hi(v[e]); }
         if (p.rope && ks >= 2) {
@@ -741,10 +773,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   // and all scores, after which every weight is <= 1 and the pass reruns.
   float mref[NHT];
 #pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    const int h = h0 + ht * 16 + l16;
-    mref[ht] = p.sink ? (h < p.H ? p.sink[h] : 0.0f) * LOG2E : 0.0f;
-  }
+  for (int ht = 0; ht < NHT; ++ht) mref[ht] = p.sink ? skv[ht] * LOG2E : 0.0f;
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
@@ -756,8 +785,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     f32x4 Cneg[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-      const int h = h0 + ht * 16 + l16;
-      const float l0 = p.sink ? __builtin_amdgcn_exp2f((h < p.H ? p.sink[h] : 0.0f) * LOG2E - mref[ht]) : 0.0f;
+      const float l0 = p.sink ? __builtin_amdgcn_exp2f(skv[ht] * LOG2E - mref[ht]) : 0.0f;
       Lacc[ht] = f32x4{l0, l0, l0, l0};
       Cneg[ht] = f32x4{-mref[ht], -mref[ht], -mref[ht], -mref[ht]};
 #pragma unroll
@@ -861,10 +889,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   auto run_max = [&]() {
     float m[NHT];
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      const int h = h0 + ht * 16 + l16;
-      m[ht] = p.sink ? (h < p.H ? p.sink[h] : 0.0f) * LOG2E : -__builtin_inff();
-    }
+    for (int ht = 0; ht < NHT; ++ht) m[ht] = p.sink ? skv[ht] * LOG2E : -__builtin_inff();
     __syncthreads();  // every wave is done with the ring
     issue(0, 0);
     issue(1, 1);
