@@ -60,9 +60,21 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   const float LOG2E = 1.4426950408889634f;
   const float NEG_INF = -__builtin_inff();
 
-  // ---- Q^T operand: lane l holds head ht*16+l16, dims ks*32 + 8g .. +7
+  // ---- Q^T operand: lane l holds head ht*16+l16, dims ks*32 + 8g .. +7.
+  // Every load is issued before the first is used (one memory round trip):
+  // lanes past the last head read head H-1 and use zeros.
   bf16x8 Q[NHT][4];
+  float skv[NHT];  // the heads' sink logits (0 past the last head)
   {
+    u32x4 qraw[NHT][4];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int hc = min(ht * 16 + l16, p.H - 1);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qraw[ht][ks] = *(const u32x4*)(p.q + ((tok * p.H + hc) * 128 + ks * 32 + 8 * g));
+      skv[ht] = p.sink ? p.sink[hc] : 0.0f;
+      if (ht * 16 + l16 >= p.H) skv[ht] = 0.0f;
+    }
     float qc[8], qs[8];
     if (p.rope) {
 #pragma unroll
@@ -78,7 +90,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
       for (int ks = 0; ks < 4; ++ks) {
         float x[8];
         if (h < p.H) {
-          const u32x4 v = *(const u32x4*)(p.q + ((tok * p.H + h) * 128 + ks * 32 + 8 * g));
+          const u32x4 v = qraw[ht][ks];
 #pragma unroll
           for (int e = 0; e < 4; ++e) { x[2 * e] = bf16lo(v[e]); x[2 * e + 1] = bf16hi(v[e]); }
           if (p.rope && ks >= 2) {
@@ -108,10 +120,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   float mref[NHT];
   f32x4 O[8][NHT], Lacc[NHT];
 #pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    const int h = ht * 16 + l16;
-    mref[ht] = p.sink ? (h < p.H ? p.sink[h] : 0.0f) * LOG2E : -1e30f;
-  }
+  for (int ht = 0; ht < NHT; ++ht) mref[ht] = p.sink ? skv[ht] * LOG2E : -1e30f;
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
@@ -286,10 +295,8 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   for (;;) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-      const int h = ht * 16 + l16;
       // the sink weight belongs to one part only
-      const float l0 =
-          (p.sink && part == 0) ? __builtin_amdgcn_exp2f((h < p.H ? p.sink[h] : 0.0f) * LOG2E - mref[ht]) : 0.0f;
+      const float l0 = (p.sink && part == 0) ? __builtin_amdgcn_exp2f(skv[ht] * LOG2E - mref[ht]) : 0.0f;
       Lacc[ht] = f32x4{l0, l0, l0, l0};
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) O[dt][ht] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
