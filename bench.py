@@ -78,7 +78,51 @@ def parse():
     ap.add_argument("--print-sha", action="store_true", help="print the kernel source hashes and exit")
     ap.add_argument("--append-probe", action="store_true",
                     help="only time the decode cache write path (csa_cache_append), 64 sequences at 1M")
+    ap.add_argument("--proj-probe", action="store_true",
+                    help="only time the projections around the path (csa_project_in with the indexer "
+                         "query, csa_project_out) at the prefill chunk shape")
     return ap.parse_args()
+
+
+def proj_probe(steps=20):
+    """The projections around the attention path for one prefill chunk of
+    8192 tokens: hidden 4096 -> 64 query heads of 128, the shared KV row
+    (128), the indexer key stream (64), a rank-32 indexer latent, 8 indexer
+    head weights and 2 compression logits in one GEMM, then the MXFP4
+    indexer query (8 heads of 64); out: the grouped output projection
+    (8 groups of 8 heads) back to 4096.  Random-init bf16 weights."""
+    import torch
+    import long_context_attention_21_amd as L
+    M, d, H, H_I, r, G = 8192, 4096, 64, 8, 32, 8
+    widths = (H * 128, 128, 64, r, H_I, 2)
+    g = torch.Generator(device="cuda").manual_seed(6)
+    x = torch.randn((M, d), generator=g, device="cuda").to(torch.bfloat16)
+    w_in = (torch.randn((sum(widths), d), generator=g, device="cuda") * d ** -0.5).to(torch.bfloat16)
+    w_up = (torch.randn((H_I * 64, r), generator=g, device="cuda") * r ** -0.5).to(torch.bfloat16)
+    KG = H // G * 128
+    o = torch.randn((M, H, 128), generator=g, device="cuda").to(torch.bfloat16)
+    w_o = (torch.randn((d, KG), generator=g, device="cuda") * KG ** -0.5).to(torch.bfloat16)
+    outs = L.csa_project_in(x, w_in, widths, w_up=w_up, n_qidx=H_I * 64)
+    y = L.csa_project_out(o, w_o, G)
+    calls = {"csa_project_in": (lambda: L.csa_project_in(x, w_in, widths, w_up=w_up, n_qidx=H_I * 64, out=outs),
+                                2.0 * M * sum(widths) * d + 2.0 * M * H_I * 64 * r),
+             "csa_project_out": (lambda: L.csa_project_out(o, w_o, G, out=y), 2.0 * M * d * KG)}
+    res = {}
+    for name, (fn, flops) in calls.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = flops / (ms / 1e3) / 1e12
+        res[name] = {"ms": round(ms, 4), "flops": flops, "achieved": round(tf, 1), "peak": PEAK["bf16"],
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK["bf16"], 4)}
+    print(json.dumps({"proj_probe": res, "tokens": M, "hidden": d, "calls": steps}), flush=True)
 
 
 def copy_probe():
@@ -532,6 +576,9 @@ def main():
         return
     if args.append_probe:
         append_probe()
+        return
+    if args.proj_probe:
+        proj_probe()
         return
     wl = {1: CsaLayer, 2: HcaLayer, 3: CsaLayer, 4: DecodeLayer, 5: PairLayer}[args.config](args.config)
     nk = len(wl.kernels)

@@ -253,6 +253,67 @@ int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D,
                const void* win_kv, int64_t win_pos0, int win_len, int n_win,
                const float* sink, int rope_dims, float rope_base, void* out, void* stream);
 
+/*
+ * Projections around the attention path (the step either side of it).
+ * Wiki summary, Proposed method item 1: CSA pairs a shared-KV multi-query
+ * attention with a grouped output projection, and its Lightning Indexer is
+ * made cheap by a low-rank factorisation and FP4 ("deepseek V4 技术论文" 1.1);
+ * Post-training item 3: the indexer's QK path is MXFP4.  The pages give no
+ * formula; the readings taken are
+ *   - every projection is linear, no bias, weights in the [out, in] layout,
+ *     bf16 operands, fp32 accumulation;
+ *   - the indexer query is q_I = lat . W_up^T with lat the bf16 indexer
+ *     latent: an fp32 fma chain over the rank in ascending order, then
+ *     MXFP4 per 32 outputs (OCP MX v1.0 rule: scale 2^(floor(log2 amax) - 2),
+ *     e2m1 nearest-even, saturating);
+ *   - the compression logits z (the per-token slot-logit offsets that
+ *     csa_compress takes) are one more linear map of the hidden state;
+ *   - the grouped output projection splits the H heads into G groups of
+ *     consecutive heads and maps group j's (H/G)*D values onto output
+ *     columns [j*d/G, (j+1)*d/G) with its own block of weights (nothing
+ *     mixes the groups).
+ *
+ * csa_project_in -- x [M, d] bf16 (the hidden state of M tokens) times the
+ * stacked weights w_in [n_q + n_kv + n_ik + n_lat + n_w + n_z, d] bf16 (W_q,
+ * W_kv, W_ik, W_lat, W_w, W_z in that order) in one GEMM:
+ *   q_out   [M, n_q]  bf16   (the query rows, pre-RoPE: [B, n, H, 128])
+ *   kv_out  [M, n_kv] bf16   (the shared KV rows, pre-RoPE)
+ *   ik_out  [M, n_ik] bf16   (the indexer key stream)
+ *   lat_out [M, n_lat] bf16  (the indexer latent)
+ *   w_out   [M, n_w]  fp32   (the indexer head weights)
+ *   z_out   [M, n_z]  fp32   (the compression logits, n_z = 2 for
+ *                             csa_compress's z)
+ * and, when n_qidx > 0, the indexer query from lat_out and w_up
+ * [n_qidx, n_lat] bf16: qidx_out [M, n_qidx/2] MXFP4 codes and
+ * qidx_scale_out [M, n_qidx/32] e8m0 scales (the layout csa_index_topk
+ * takes).  A width of 0 drops that output (its pointer may be NULL).
+ * Outputs are written with row stride equal to their width.
+ * Requirements: d a multiple of 32; n_lat in {16, 32, 64} when n_qidx > 0;
+ * n_qidx a multiple of 32 with n_qidx * n_lat <= 32768; x and w_in below
+ * 2 GiB; x, w_in, w_up, lat_out and qidx_out 16-byte aligned.  Device
+ * pointers, caller-owned; asynchronous on `stream`; nothing is launched on
+ * error.
+ *
+ * csa_project_qidx -- the indexer-query step alone: lat [M, r] bf16,
+ * w_up [n_qidx, r] bf16 -> qidx_out, qidx_scale_out as above, and, when
+ * q_f32_out is non-NULL, the fp32 values that were encoded [M, n_qidx].
+ *
+ * csa_project_out -- grouped output projection: o [M, H*D] bf16 (attention
+ * output rows, head-major), w_o [d, (H/G)*D] bf16 with group j's block in
+ * rows [j*d/G, (j+1)*d/G) -> y_out [M, d] bf16.  (H/G)*D a multiple of 32,
+ * d a multiple of G, o below 4 GiB, o and w_o 16-byte aligned.
+ */
+int csa_project_in(const void* x, int M, int d, const void* w_in, int n_q, int n_kv, int n_ik,
+                   int n_lat, int n_w, int n_z, const void* w_up, int n_qidx, void* q_out,
+                   void* kv_out, void* ik_out, void* lat_out, float* w_out, float* z_out,
+                   uint8_t* qidx_out, uint8_t* qidx_scale_out, void* stream);
+
+int csa_project_qidx(const void* lat, int M, int r, const void* w_up, int n_qidx,
+                     uint8_t* qidx_out, uint8_t* qidx_scale_out, float* q_f32_out, void* stream);
+
+int csa_project_out(const void* o, int M, int H, int D, int G, const void* w_o, int d,
+                    void* y_out, void* stream);
+
 /* Thread-local description of the last error (empty string if none). */
 const char* csa_last_error(void);
 /* Library version: major*10000 + minor*100 + patch. */

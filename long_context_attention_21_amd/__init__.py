@@ -6,7 +6,9 @@ stream; every step of the computation runs in the HIP kernels of
 ``libcsa_mi355x.so``.  Output tensors are allocated with torch when the
 caller does not pass them.
 
-Names follow the C ABI: csa_compress, csa_index_topk, csa_attend, hca_attend.
+Names follow the C ABI: csa_compress, csa_cache_append, csa_index_topk,
+csa_attend, hca_attend, and the projections around the path
+(csa_project_in, csa_project_qidx, csa_project_out).
 """
 from __future__ import annotations
 
@@ -14,7 +16,8 @@ import torch
 
 from ._lib import (FMT_BF16, FMT_FP8_ROPE_BF16, FMT_MXFP4, CsaError, check, lib)
 
-__all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend", "version",
+__all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend",
+           "csa_project_in", "csa_project_qidx", "csa_project_out", "version",
            "CsaError",
            "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16"]
 
@@ -167,4 +170,57 @@ def hca_attend(q, entries, q_pos0=0, m=128, win_kv=None, win_pos0=0, n_win=128, 
         _ptr(q), B, n, int(q_pos0), H, D, _ptr(entries), N, m, _ptr(win_kv), int(win_pos0), win_len,
         int(n_win) if win_kv is not None else 0, _ptr(sink), rope_dims, float(rope_base), _ptr(out),
         _stream(stream)))
+    return out
+
+
+def csa_project_in(x, w_in, widths, w_up=None, n_qidx=0, out=None, stream=None):
+    """Input projections (csa_project_in).  x [..., d] bf16; w_in
+    [sum(widths), d] bf16 = W_q, W_kv, W_ik, W_lat, W_w, W_z stacked; widths =
+    (n_q, n_kv, n_ik, n_lat, n_w, n_z); w_up [n_qidx, n_lat] bf16.  Returns a
+    dict of q, kv, ik, lat (bf16 [M, n_*]), w and z (fp32 [M, n_w], [M, n_z])
+    and, when n_qidx > 0, qidx (uint8 [M, n_qidx/2]) and qidx_scale (uint8
+    [M, n_qidx/32]); M = x.numel() / d.  Widths of 0 give no tensor."""
+    d = x.shape[-1]
+    M = x.numel() // d
+    n_q, n_kv, n_ik, n_lat, n_w, n_z = widths
+    dev = x.device
+    out = dict(out or {})
+    for name, n, dt in (("q", n_q, torch.bfloat16), ("kv", n_kv, torch.bfloat16), ("ik", n_ik, torch.bfloat16),
+                        ("lat", n_lat, torch.bfloat16), ("w", n_w, torch.float32), ("z", n_z, torch.float32)):
+        if n and name not in out:
+            out[name] = torch.empty((M, n), dtype=dt, device=dev)
+    if n_qidx:
+        out.setdefault("qidx", torch.empty((M, n_qidx // 2), dtype=torch.uint8, device=dev))
+        out.setdefault("qidx_scale", torch.empty((M, n_qidx // 32), dtype=torch.uint8, device=dev))
+    check(lib().csa_project_in(_ptr(x), M, d, _ptr(w_in), n_q, n_kv, n_ik, n_lat, n_w, n_z, _ptr(w_up), n_qidx,
+                               _ptr(out.get("q")), _ptr(out.get("kv")), _ptr(out.get("ik")), _ptr(out.get("lat")),
+                               _ptr(out.get("w")), _ptr(out.get("z")), _ptr(out.get("qidx")),
+                               _ptr(out.get("qidx_scale")),
+                               _stream(stream)))
+    return out
+
+
+def csa_project_qidx(lat, w_up, with_f32=False, stream=None):
+    """The indexer-query step (csa_project_qidx): lat [M, r] bf16, w_up
+    [n_qidx, r] bf16 -> (codes uint8 [M, n_qidx/2], scales uint8
+    [M, n_qidx/32], fp32 values [M, n_qidx] or None)."""
+    M, r = lat.shape
+    n_qidx = w_up.shape[0]
+    codes = torch.empty((M, n_qidx // 2), dtype=torch.uint8, device=lat.device)
+    scales = torch.empty((M, n_qidx // 32), dtype=torch.uint8, device=lat.device)
+    qf = torch.empty((M, n_qidx), dtype=torch.float32, device=lat.device) if with_f32 else None
+    check(lib().csa_project_qidx(_ptr(lat), M, r, _ptr(w_up), n_qidx, _ptr(codes), _ptr(scales), _ptr(qf),
+                                 _stream(stream)))
+    return codes, scales, qf
+
+
+def csa_project_out(o, w_o, G, out=None, stream=None):
+    """Grouped output projection (csa_project_out): o [..., H, D] bf16,
+    w_o [d, (H/G)*D] bf16 -> y [M, d] bf16 (M = o.numel() / (H*D))."""
+    H, D = o.shape[-2], o.shape[-1]
+    M = o.numel() // (H * D)
+    d = w_o.shape[0]
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=o.device)
+    check(lib().csa_project_out(_ptr(o), M, H, D, G, _ptr(w_o), d, _ptr(out), _stream(stream)))
     return out

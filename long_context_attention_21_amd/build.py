@@ -32,6 +32,8 @@ SOURCES = {
     # the score MFMA result feeds VALU code directly: keep it in VGPRs
     "index_topk.hip": DEVICE + ["-ffp-contract=off", "-fno-honor-nans", "-mno-amdgpu-ieee",
                                 "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # GEMM accumulators in VGPRs; the indexer-query chain is explicit fmas
+    "proj.hip": DEVICE + ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "abi.cpp": ["-ffp-contract=off"],
 }
 

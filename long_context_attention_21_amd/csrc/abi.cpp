@@ -342,4 +342,133 @@ int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const 
                        stream, "hca_attend");
 }
 
+// ---------------------------------------------------------------- projections
+
+namespace {
+
+int qidx_check(const void* lat, int ld_lat, int r, const void* w_up, int n_qidx, const uint8_t* codes,
+               const uint8_t* scales, const float* q_f32, const char* who) {
+  REQUIRE(r == 16 || r == 32 || r == 64, "%s: rank r=%d must be 16, 32 or 64", who, r);
+  REQUIRE(n_qidx > 0 && n_qidx % 32 == 0 && n_qidx * r <= 32768,
+          "%s: n_qidx=%d must be a positive multiple of 32 with n_qidx * r <= 32768", who, n_qidx);
+  REQUIRE(w_up && codes && scales, "%s: w_up, codes and scales must be non-NULL", who);
+  REQUIRE(aligned16(w_up) && aligned16(codes) && aligned16(q_f32),
+          "%s: w_up, codes and q_f32 must be 16-byte aligned", who);
+  REQUIRE(lat != nullptr && aligned16(lat) && ld_lat % 8 == 0,
+          "%s: the latent must be non-NULL with 16-byte aligned rows", who);
+  return CSA_OK;
+}
+
+int qidx_launch(const void* lat, int ld_lat, int M, int r, const void* w_up, int n_qidx, uint8_t* codes,
+                uint8_t* scales, float* q_f32, void* stream, const char* who) {
+  csa::QidxParams q{};
+  q.lat = (const uint16_t*)lat;
+  q.w_up = (const uint16_t*)w_up;
+  q.M = M;
+  q.r = r;
+  q.nq = n_qidx;
+  q.ld_lat = ld_lat;
+  q.codes = codes;
+  q.scales = scales;
+  q.q_f32 = q_f32;
+  return hip_status(csa::launch_qidx_mxfp4(q, (hipStream_t)stream), who);
+}
+
+}  // namespace
+
+int csa_project_qidx(const void* lat, int M, int r, const void* w_up, int n_qidx, uint8_t* qidx_out,
+                     uint8_t* qidx_scale_out, float* q_f32_out, void* stream) {
+  REQUIRE(M >= 0, "csa_project_qidx: M=%d must be >= 0", M);
+  if (qidx_check(lat, r, r, w_up, n_qidx, qidx_out, qidx_scale_out, q_f32_out, "csa_project_qidx") != CSA_OK)
+    return CSA_INVALID_ARG;
+  if (M == 0) return ok();
+  return qidx_launch(lat, r, M, r, w_up, n_qidx, qidx_out, qidx_scale_out, q_f32_out, stream, "csa_project_qidx");
+}
+
+int csa_project_in(const void* x, int M, int d, const void* w_in, int n_q, int n_kv, int n_ik, int n_lat,
+                   int n_w, int n_z, const void* w_up, int n_qidx, void* q_out, void* kv_out, void* ik_out,
+                   void* lat_out, float* w_out, float* z_out, uint8_t* qidx_out, uint8_t* qidx_scale_out,
+                   void* stream) {
+  REQUIRE(M >= 0, "csa_project_in: M=%d must be >= 0", M);
+  REQUIRE(d > 0 && d % 32 == 0, "csa_project_in: d=%d must be a positive multiple of 32", d);
+  REQUIRE(n_q >= 0 && n_kv >= 0 && n_ik >= 0 && n_lat >= 0 && n_w >= 0 && n_z >= 0,
+          "csa_project_in: output widths must be >= 0");
+  const int64_t N64 = (int64_t)n_q + n_kv + n_ik + n_lat + n_w + n_z;
+  REQUIRE(N64 < (1 << 24), "csa_project_in: total output width %lld too large", (long long)N64);
+  const int N = (int)N64;
+  REQUIRE(N > 0, "csa_project_in: no output");
+  REQUIRE(x && w_in, "csa_project_in: x and w_in must be non-NULL");
+  REQUIRE(aligned16(x) && aligned16(w_in), "csa_project_in: x and w_in must be 16-byte aligned");
+  REQUIRE((int64_t)M * d * 2 < (1ll << 31) && (int64_t)N * d * 2 < (1ll << 31),
+          "csa_project_in: x and w_in must each be below 2 GiB");
+  const int widths[6] = {n_q, n_kv, n_ik, n_lat, n_w, n_z};
+  void* ptrs[6] = {q_out, kv_out, ik_out, lat_out, w_out, z_out};
+  const char* names[6] = {"q_out", "kv_out", "ik_out", "lat_out", "w_out", "z_out"};
+  static_assert(csa::kGemmOuts >= 6, "one GEMM output per projection");
+  csa::GemmParams g{};
+  int c0 = 0;
+  for (int i = 0; i < 6; ++i) {
+    if (widths[i] == 0) continue;
+    REQUIRE(ptrs[i] != nullptr, "csa_project_in: %s is NULL but its width is %d", names[i], widths[i]);
+    csa::GemmOut& o = g.out[g.nout++];
+    o.ptr = ptrs[i];
+    o.n0 = c0;
+    o.n1 = c0 + widths[i];
+    o.ld = widths[i];
+    o.f32 = i >= 4;
+    c0 += widths[i];
+  }
+  if (n_qidx > 0) {
+    REQUIRE(n_lat > 0, "csa_project_in: the indexer query needs the latent (n_lat > 0)");
+    if (qidx_check(lat_out, n_lat, n_lat, w_up, n_qidx, qidx_out, qidx_scale_out, nullptr,
+                   "csa_project_in (indexer query)") != CSA_OK)
+      return CSA_INVALID_ARG;
+  }
+  if (M == 0) return ok();
+  g.A = (const uint16_t*)x;
+  g.B = (const uint16_t*)w_in;
+  g.M = M;
+  g.N = N;
+  g.K = d;
+  g.lda = d;
+  g.ldb = d;
+  g.a_bytes = (uint32_t)((int64_t)M * d * 2);
+  g.b_bytes = (uint32_t)((int64_t)N * d * 2);
+  int st = hip_status(csa::launch_gemm_tn(g, 1, (hipStream_t)stream), "csa_project_in (GEMM)");
+  if (st != CSA_OK || n_qidx == 0) return st;
+  return qidx_launch(lat_out, n_lat, M, n_lat, w_up, n_qidx, qidx_out, qidx_scale_out, nullptr, stream,
+                     "csa_project_in (indexer query)");
+}
+
+int csa_project_out(const void* o, int M, int H, int D, int G, const void* w_o, int d, void* y_out,
+                    void* stream) {
+  REQUIRE(M >= 0, "csa_project_out: M=%d must be >= 0", M);
+  REQUIRE(H > 0 && D > 0 && G > 0 && H % G == 0, "csa_project_out: H=%d must be a positive multiple of G=%d", H, G);
+  const int KG = H / G * D;
+  REQUIRE(KG % 32 == 0, "csa_project_out: (H/G)*D=%d must be a multiple of 32", KG);
+  REQUIRE(d > 0 && d % G == 0, "csa_project_out: d=%d must be a positive multiple of G=%d", d, G);
+  REQUIRE(o && w_o && y_out, "csa_project_out: o, w_o and y_out must be non-NULL");
+  REQUIRE(aligned16(o) && aligned16(w_o), "csa_project_out: o and w_o must be 16-byte aligned");
+  REQUIRE((int64_t)M * H * D * 2 < (1ll << 32) - 4096, "csa_project_out: o must be below 4 GiB");
+  if (M == 0) return ok();
+  const int dg = d / G;
+  csa::GemmParams g{};
+  g.A = (const uint16_t*)o;
+  g.B = (const uint16_t*)w_o;
+  g.M = M;
+  g.N = dg;
+  g.K = KG;
+  g.lda = H * D;
+  g.ldb = KG;
+  g.a_zoff = KG;
+  g.b_zoff = (int64_t)dg * KG;
+  g.a_bytes = (uint32_t)((int64_t)M * H * D * 2);
+  g.a_zbytes = (uint32_t)KG * 2u;
+  g.b_bytes = (uint32_t)((int64_t)dg * KG * 2);
+  g.c_zcol = dg;
+  g.nout = 1;
+  g.out[0] = csa::GemmOut{y_out, 0, d, d, 0};
+  return hip_status(csa::launch_gemm_tn(g, G, (hipStream_t)stream), "csa_project_out");
+}
+
 }  // extern "C"

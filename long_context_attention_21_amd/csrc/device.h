@@ -131,4 +131,30 @@ __device__ __forceinline__ float sum_over_groups(float x) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Buffer descriptor words (base, stride 0, byte extent, 32-bit data format):
+// reads past the extent return zeros.
+__device__ __forceinline__ u32x4 dma_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, (uint32_t)bytes, 0x00020000u};
+}
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes at `voff` land at
+// LDS address lds + 16 l.  Issued from inline asm so that the compiler does
+// not track it: otherwise it makes every LDS read wait for all outstanding
+// loads (vmcnt(0)), including the prefetch of the chunks ahead, which
+// serialises the ring.  The caller waits with s_waitcnt vmcnt and a barrier
+// before it reads the slot.  M0 carries the LDS address; the leading
+// s_nop 4 covers an M0 or descriptor write just before the load.
+__device__ __forceinline__ void dma_b128(const u32x4& r, uint32_t lds, uint32_t voff) {
+  u32x4 rs;  // wave-uniform: make that explicit so it is taken from SGPRs
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rs[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)r[i]);
+  asm volatile(
+      "s_nop 4\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "{m0}"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rs)
+      : "memory");
+}
+
 }  // namespace csa

@@ -94,4 +94,36 @@ hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream);
 size_t index_topk_workspace(int B, int n, int64_t q_pos0, int N, int m, int k);
 hipError_t index_topk_fallbacks(unsigned long long* count, bool reset);
 
+// bf16 GEMM C = A . B^T (A [M, K] rows lda apart, B [N, K] rows ldb apart,
+// fp32 accumulation; K a multiple of 32).  Output column c (plus z * c_zcol
+// for group z) goes to the destination whose range [n0, n1) holds it.
+constexpr int kGemmOuts = 6;
+struct GemmOut {
+  void* ptr;
+  int n0, n1, ld, f32;  // column range, leading dimension (elements), fp32 (1) or bf16 (0)
+};
+struct GemmParams {
+  const uint16_t* A;
+  const uint16_t* B;
+  int M, N, K, lda, ldb;
+  int64_t a_zoff, b_zoff;  // elements added to A and B per group z
+  uint32_t a_bytes, b_bytes, a_zbytes;  // extents from the (group-0) bases; a_zoff * 2
+  int c_zcol;
+  int nout;
+  GemmOut out[kGemmOuts];
+};
+hipError_t launch_gemm_tn(const GemmParams& p, int groups, hipStream_t stream);
+
+// Low-rank indexer query: q = lat . W_up^T (fp32 fma chain over the rank r,
+// ascending), MXFP4-encoded per 32 outputs.
+struct QidxParams {
+  const uint16_t* lat;   // [M, r] bf16, rows ld_lat apart
+  const uint16_t* w_up;  // [nq, r] bf16
+  int M, r, nq, ld_lat;
+  uint8_t* codes;        // [M, nq / 2]
+  uint8_t* scales;       // [M, nq / 32]
+  float* q_f32;          // [M, nq] or null
+};
+hipError_t launch_qidx_mxfp4(const QidxParams& p, hipStream_t stream);
+
 }  // namespace csa

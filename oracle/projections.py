@@ -21,6 +21,9 @@ Everything else is a reading, stated where it is used:
 * P2  the indexer query is low rank: q_I = lat . W_up^T with lat the bf16
       latent (rank r) and W_up [H_I*64, r]; the fp32 value of q_I is then
       MXFP4-encoded per 32-element block with the O4 rule.
+* P4  the compression logits z (the per-token slot-logit offsets the
+      compressor adds to its learned bias) are one more linear map of the
+      hidden state, kept in fp32 like w_I.
 * P3  the grouped output projection splits the H heads into G groups of
       consecutive heads; group j's head outputs (H/G x 128 values) are
       projected by its own [d/G, (H/G)*128] block onto output columns
@@ -52,15 +55,15 @@ def _bf16(y64):
     return bf16_from_f32(y64.astype(np.float32))
 
 
-def project_in(x, w_q, w_kv, w_ik, w_lat, w_w, w_up):
-    """The input projections of one layer (P1, P2).
+def project_in(x, w_q, w_kv, w_ik, w_lat, w_w, w_up, w_z=None):
+    """The input projections of one layer (P1, P2, P4).
 
     x [M, d] bf16 bits; w_q [H*128, d], w_kv [128, d], w_ik [64, d],
     w_lat [r, d], w_w [H_I, d], w_up [H_I*64, r], all bf16 bits.
     Returns dict: q [M, H*128] bf16, kv [M, 128] bf16, ik [M, 64] bf16,
     lat [M, r] bf16, w_I [M, H_I] fp32, q_I codes [M, H_I*32] uint8 and
     q_I scales [M, H_I*2] uint8 (MXFP4), and q_I_f32 [M, H_I*64] (the fp32
-    values that were encoded)."""
+    values that were encoded); with w_z [n_z, d], also z [M, n_z] fp32."""
     out = {
         "q": _bf16(linear_f64(x, w_q)),
         "kv": _bf16(linear_f64(x, w_kv)),
@@ -68,6 +71,8 @@ def project_in(x, w_q, w_kv, w_ik, w_lat, w_w, w_up):
         "lat": _bf16(linear_f64(x, w_lat)),
         "w_I": linear_f64(x, w_w).astype(np.float32),
     }
+    if w_z is not None:
+        out["z"] = linear_f64(x, w_z).astype(np.float32)
     qf = linear_f64(out["lat"], w_up).astype(np.float32)
     codes, scales = mxfp4_encode(qf)
     out["q_I_f32"] = qf

@@ -243,3 +243,63 @@ def test_attend_rejects_small_workspace(L):
     assert _attend(L, **kw, ws=FAKE, ws_bytes=need - 16) == _lib.CSA_WORKSPACE_TOO_SMALL
     assert _attend(L, **kw, ws=None, ws_bytes=need) == _lib.CSA_INVALID_ARG
     assert "ws must be" in _msg(L)
+
+
+def _proj_in(L, **kw):
+    a = dict(x=FAKE, M=5, d=256, w_in=FAKE2, n_q=512, n_kv=128, n_ik=64, n_lat=32, n_w=8, n_z=2, w_up=FAKE,
+             n_qidx=512, q_out=FAKE, kv_out=FAKE, ik_out=FAKE, lat_out=FAKE, w_out=FAKE, z_out=FAKE, qidx_out=FAKE,
+             qidx_scale_out=FAKE2, stream=None)
+    a.update(kw)
+    return L.csa_project_in(*a.values())
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(d=100), "d=100"),
+    (dict(n_q=0, n_kv=0, n_ik=0, n_lat=0, n_w=0, n_z=0, n_qidx=0), "no output"),
+    (dict(z_out=None), "z_out is NULL"),
+    (dict(n_q=1 << 30), "too large"),
+    (dict(kv_out=None), "kv_out is NULL"),
+    (dict(x=MIS), "aligned"),
+    (dict(n_lat=0), "needs the latent"),
+    (dict(n_lat=24), "rank r=24"),
+    (dict(n_qidx=48), "n_qidx=48"),
+    (dict(n_lat=64, n_qidx=1024), "n_qidx=1024"),   # W_up above 64 KB
+    (dict(qidx_scale_out=None), "non-NULL"),
+    (dict(M=-1), "M=-1"),
+    (dict(M=1 << 20, d=1024), "2 GiB"),
+])
+def test_project_in_rejects(L, kw, needle):
+    assert _proj_in(L, **kw) == _lib.CSA_INVALID_ARG
+    assert needle in _msg(L)
+
+
+def test_project_in_empty_is_ok(L):
+    assert _proj_in(L, M=0) == _lib.CSA_OK
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(r=8), "rank r=8"),
+    (dict(lat=MIS), "latent"),
+    (dict(q_f32_out=MIS), "aligned"),
+    (dict(w_up=None), "non-NULL"),
+])
+def test_project_qidx_rejects(L, kw, needle):
+    a = dict(lat=FAKE, M=3, r=32, w_up=FAKE2, n_qidx=512, qidx_out=FAKE, qidx_scale_out=FAKE, q_f32_out=None,
+             stream=None)
+    a.update(kw)
+    assert L.csa_project_qidx(*a.values()) == _lib.CSA_INVALID_ARG
+    assert needle in _msg(L)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(G=3), "multiple of G=3"),
+    (dict(D=100, H=1, G=1), "multiple of 32"),
+    (dict(d=102), "d=102"),
+    (dict(y_out=None), "non-NULL"),
+    (dict(o=MIS), "aligned"),
+])
+def test_project_out_rejects(L, kw, needle):
+    a = dict(o=FAKE, M=4, H=8, D=128, G=4, w_o=FAKE2, d=256, y_out=FAKE, stream=None)
+    a.update(kw)
+    assert L.csa_project_out(*a.values()) == _lib.CSA_INVALID_ARG
+    assert needle in _msg(L)

@@ -46,12 +46,13 @@ def test_identity_projection_returns_the_input():
     x = _bits(rng, (5, d))
     eye = oracle.bf16_from_f32(np.eye(d, dtype=np.float32))
     w_up = oracle.bf16_from_f32(np.zeros((2 * 64, 4), np.float32))   # H_I = 2, r = 4
-    r = P.project_in(x, eye, eye[:16], eye[:8], eye[:4], eye[:2], w_up)
+    r = P.project_in(x, eye, eye[:16], eye[:8], eye[:4], eye[:2], w_up, w_z=eye[5:7])
     assert np.array_equal(r["q"], x)
     assert np.array_equal(r["kv"], x[:, :16])
     assert np.array_equal(r["ik"], x[:, :8])
     assert np.array_equal(r["lat"], x[:, :4])
     assert np.array_equal(r["w_I"], oracle.bf16_to_f64(x[:, :2]).astype(np.float32))
+    assert np.array_equal(r["z"], oracle.bf16_to_f64(x[:, 5:7]).astype(np.float32))
     assert not r["q_I_f32"].any() and not r["q_I_codes"].any() and not r["q_I_scales"].any()
 
 
