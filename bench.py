@@ -43,7 +43,8 @@ TRAFFIC = {  # profiles/csa_prefill_128k_hbm_counters.txt
                           "bytes": 7.296e7},
 }
 KERNEL_SOURCE = {"csa_compress": "compress.hip", "hca_compress": "compress.hip", "csa_index_topk": "index_topk.hip",
-                 "csa_attend": "attend.hip", "hca_attend": "attend.hip"}
+                 "csa_attend": "attend.hip", "hca_attend": "attend.hip", "csa_project_in": "proj.hip",
+                 "csa_project_out": "proj.hip"}
 
 
 def source_sha(kernel):

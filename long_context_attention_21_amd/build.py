@@ -33,7 +33,7 @@ SOURCES = {
     "index_topk.hip": DEVICE + ["-ffp-contract=off", "-fno-honor-nans", "-mno-amdgpu-ieee",
                                 "-mllvm", "-amdgpu-mfma-vgpr-form"],
     # GEMM accumulators in VGPRs; the indexer-query chain is explicit fmas
-    "proj.hip": DEVICE + ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "proj.hip": DEVICE + ["-ffp-contract=off"],
     "abi.cpp": ["-ffp-contract=off"],
 }
 

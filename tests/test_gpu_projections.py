@@ -72,6 +72,7 @@ def _run_in(x, W, n_qidx=None):
     (300, 256, 4, 8, 32),     # ragged rows, 6 column tiles with a ragged last one, 8 K steps
     (129, 32, 2, 4, 16),      # one K step (less than the ring), one ragged row tile
     (1, 96, 1, 2, 64),        # a single row, 3 K steps
+    (1100, 256, 4, 8, 32),    # 256 x 256 tiles: ragged row and column tiles
 ])
 def test_project_in_matches_oracle(orc, M, d, H, H_I, r):
     from oracle import projections as P
@@ -125,6 +126,8 @@ def test_project_qidx_on_oracle_latent(orc, r):
     (130, 4, 1, 384),     # G = 1: a dense projection, 3 column tiles
     (65, 16, 16, 2048),   # one head per group, 128 columns per group
     (3, 8, 2, 512),
+    (1030, 16, 8, 2048),  # 256 x 256 tiles over 8 groups, ragged rows
+    (1500, 4, 1, 768),    # 256 x 256 tiles, dense, 3 column tiles
 ])
 def test_project_out_matches_oracle(M, H, G, d):
     from oracle import projections as P
