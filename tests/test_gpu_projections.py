@@ -193,3 +193,60 @@ def test_projections_full_size_sampled_rows(orc):
     os_ = o[rows]
     S = np.concatenate([_cond(os_[:, j * KG:(j + 1) * KG], w_o[j * dg:(j + 1) * dg]) for j in range(G)], axis=1)
     _check_bf16(y, ref, S, KG, "y")
+
+
+def test_csa_layer_forward_from_hidden_state(orc):
+    """One CSA attention layer from the hidden state: csa_project_in ->
+    csa_compress (kv, indexer keys, the projected compression logits z) ->
+    csa_index_topk (the projected MXFP4 indexer query and head weights) ->
+    csa_attend (window = the projected kv rows, sink) -> csa_project_out.
+    Each stage is checked against the oracle given the GPU's bytes of the
+    stage before: compression and the MXFP4 top-k bit-exactly, attention to
+    the output tolerance, the projections to the bounds above."""
+    from oracle import projections as P
+    from _helpers import assert_close, canon_idx, oracle_compress_store
+    rng = np.random.default_rng(21)
+    M, d, H, H_I, r, G, m, k = 512, 256, 8, 8, 32, 4, 4, 32
+    print("layer forward M=%d d=%d H=%d" % (M, d, H), flush=True)
+    x = _w(rng, (M, d), 1.0)
+    W = _layer_weights(rng, d, H, H_I, r)
+    beta = rng.standard_normal(2 * m).astype(np.float32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    KG = H // G * 128
+    w_o = _w(rng, (d, KG), KG ** -0.5)
+    out = _run_in(x, W)
+    q = out["q"].view(1, M, H, 128)
+    comp = L.csa_compress(out["kv"].view(1, M, 128), dev(beta), m, 1, ik=out["ik"].view(1, M, 64),
+                          z=out["z"].view(1, M, 2), kidx_fmt="mxfp4")
+    idx = L.csa_index_topk(out["qidx"].view(1, M, H_I, 32), out["w"].view(1, M, H_I), comp["kidx"], k, m,
+                           fmt="mxfp4", qidx_scale=out["qidx_scale"].view(1, M, H_I, 2),
+                           kidx_scale=comp["kidx_scale"])
+    o = L.csa_attend(q, comp["entries"], idx, m=m, win_kv=out["kv"].view(1, M, 128), sink=dev(sink))
+    y = L.csa_project_out(o, dev(w_o), G)
+    torch.cuda.synchronize()
+    # projections
+    for name, wname in (("q", "w_q"), ("kv", "w_kv"), ("ik", "w_ik")):
+        _check_bf16(host_bits(out[name]), P.linear_f64(x, W[wname]), _cond(x, W[wname]), d, name)
+    _check_f32(host(out["z"]), P.linear_f64(x, W["w_z"]), _cond(x, W["w_z"]), d, "z")
+    # compression of the projected rows
+    kv, ik, z = host_bits(out["kv"]), host_bits(out["ik"]), host(out["z"])
+    ref = oracle_compress_store(orc, kv, beta, m, 1, ik=ik, z=z, kidx_fmt="mxfp4")
+    assert np.array_equal(host_bits(comp["entries"])[0], ref["entries"])
+    assert np.array_equal(host(comp["kidx"])[0], ref["kidx"])
+    assert np.array_equal(host(comp["kidx_scale"])[0], ref["kidx_scale"])
+    # top-k from the projected MXFP4 query
+    qdec = orc.mxfp4_decode(host(out["qidx"]), host(out["qidx_scale"])).reshape(M, H_I, 64)
+    rows = np.arange(M, dtype=np.int32)
+    ref_idx = orc.index_topk_rows(qdec, host(out["w"]), ref["kidx_dec"], m, 0, rows, k)
+    got_idx = host(idx)[0]
+    assert np.array_equal(canon_idx(got_idx), ref_idx)
+    # attention
+    ref_o = orc.attend_rows(host_bits(out["q"]).reshape(M, H, 128), 0, ref["entries_f64"], m, rows, "csa",
+                            idx=ref_idx, win=kv, sink=sink)
+    assert_close(host_bits(o)[0], ref_o, "layer attention")
+    # output projection of the GPU's attention output
+    o_bits = host_bits(o).reshape(M, H * 128)
+    _, ref_y = P.project_out(o_bits, w_o, G)
+    dg = d // G
+    S = np.concatenate([_cond(o_bits[:, j * KG:(j + 1) * KG], w_o[j * dg:(j + 1) * dg]) for j in range(G)], axis=1)
+    _check_bf16(host_bits(y), ref_y, S, KG, "y")
