@@ -42,6 +42,8 @@ TRAFFIC = {  # profiles/csa_prefill_128k_hbm_counters.txt
     ("csa_compress", 3): {"sha256": "2fed75a38f059725fadc6fcd774c1ecff134c35a77219ff3ac6f1019203b2a06",
                           "bytes": 7.296e7},
 }
+TRAFFIC[("csa_project_in", "proj")] = {  # the GEMM (1.100e9) + the indexer-query kernel (9.7e6)
+    "sha256": "0d29565ac9e7d9abe38eca2dd0e454f5024f54683e75d81002409904ce29ee24", "bytes": 1.110e9}
 KERNEL_SOURCE = {"csa_compress": "compress.hip", "hca_compress": "compress.hip", "csa_index_topk": "index_topk.hip",
                  "csa_attend": "attend.hip", "hca_attend": "attend.hip", "csa_project_in": "proj.hip",
                  "csa_project_out": "proj.hip"}
@@ -85,7 +87,7 @@ def parse():
     return ap.parse_args()
 
 
-def proj_probe(steps=20):
+def proj_probe(steps=20, no_cpu=False):
     """The projections around the attention path for one prefill chunk of
     8192 tokens: hidden 4096 -> 64 query heads of 128, the shared KV row
     (128), the indexer key stream (64), a rank-32 indexer latent, 8 indexer
@@ -123,7 +125,54 @@ def proj_probe(steps=20):
         tf = flops / (ms / 1e3) / 1e12
         res[name] = {"ms": round(ms, 4), "flops": flops, "achieved": round(tf, 1), "peak": PEAK["bf16"],
                      "unit": "TFLOP/s", "frac": round(tf / PEAK["bf16"], 4)}
-    print(json.dumps({"proj_probe": res, "tokens": M, "hidden": d, "calls": steps}), flush=True)
+    ms_total = sum(r["ms"] for r in res.values())
+    dom = res["csa_project_in"]
+    cpu = None
+    if not no_cpu:
+        cpu = proj_cpu_baseline(d, H, H_I, r, G, widths)
+    print(json.dumps({
+        "metric": "projections around the attention path: tokens/s (input projections + indexer query + "
+                  "grouped output projection)",
+        "value": round(M / (ms_total / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "ms_per_step": round(ms_total, 4), "higher_is_better": True, "dtype": "bf16 (MFMA, fp32 accumulation)",
+        "data": "synthetic (seeded torch.randn, random-init weights)",
+        "config": {"workload": "projections of one 8192-token prefill chunk: hidden 4096, 64 query heads, "
+                               "rank-32 MXFP4 indexer query (8 heads), 8 output groups", "tokens": M, "hidden": d},
+        "roofline": {"kernel": "csa_project_in", "bound": "mfma", "achieved": dom["achieved"], "peak": dom["peak"],
+                     "unit": "TFLOP/s", "frac": dom["frac"], "traffic": traffic_bytes("csa_project_in", "proj")},
+        "kernels": res, "cpu_baseline": cpu}), flush=True)
+
+
+def proj_cpu_baseline(d, H, H_I, r, G, widths, rows=8192, chunks=4):
+    """The projection oracle (numpy fp64) on `chunks` chunks of `rows` tokens
+    with full-size weights, scaled to tokens/s."""
+    import oracle
+    from oracle import projections as P
+    rng = np.random.default_rng(0)
+
+    def w(shape, scale):
+        return oracle.bf16_from_f32((rng.standard_normal(shape) * scale).astype(np.float32))
+    Ws = [w((n, d), d ** -0.5) for n in widths]
+    w_up = w((H_I * 64, r), r ** -0.5)
+    KG = H // G * 128
+    w_o = w((d, KG), KG ** -0.5)
+    t = 0.0
+    for _ in range(chunks):
+        x = w((rows, d), 1.0)
+        o = w((rows, H * 128), 1.0)
+        t0 = time.time()
+        P.project_in(x, Ws[0], Ws[1], Ws[2], Ws[3], Ws[4], w_up, w_z=Ws[5])
+        P.project_out(o, w_o, G)
+        t += time.time() - t0
+    return {"value": round(chunks * rows / t, 1), "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
+            "sample": "%d chunks of %d tokens through the projection oracle (input projections, indexer query, "
+                      "grouped output projection) with full-size weights, %.1f s" % (chunks, rows, t)}
+
+
+def _cores():
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    return min(cores, int(omp)) if omp else cores
 
 
 def copy_probe():
@@ -138,7 +187,7 @@ def copy_probe():
                       "launches": 3}), flush=True)
 
 
-def append_probe(steps=1024):
+def append_probe(steps=1024, no_cpu=False):
     """The decode cache write path at config 4's shape: 64 sequences append
     one token per call at positions 1,048,576 .. +steps-1, into a CSA layer
     (m = 4 overlapped, FP8 + bf16-RoPE entries, MXFP4 indexer keys) and an
@@ -187,7 +236,42 @@ def append_probe(steps=1024):
         per_call = B * ((2 * 256 + (128 if with_ik else 0)) + (Lr * row_in + entry_out) / m)
         res[name] = {"us_per_call": round(us, 3), "tokens_per_s": round(B / us * 1e6, 1),
                      "algorithmic_bytes_per_call": int(per_call), "achieved_GBps": round(per_call / us * 1e-3, 2)}
-    print(json.dumps({"append_probe": res, "sequences": B, "calls": steps, "q_pos": P}), flush=True)
+    tot_us = sum(r["us_per_call"] for r in res.values())
+    tot_bytes = sum(r["algorithmic_bytes_per_call"] for r in res.values())
+    dom = max(res, key=lambda k: res[k]["us_per_call"])
+    print(json.dumps({
+        "metric": "decode cache write path: appended tokens/s (CSA + HCA layer per token)",
+        "value": round(B / tot_us * 1e6, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "ms_per_step": round(tot_us / 1e3, 5), "higher_is_better": True, "dtype": "fp32 pooling; fp8/bf16/mxfp4 storage",
+        "data": "synthetic (seeded torch.randn)",
+        "config": {"workload": "64 sequences append one token at positions 1048576.. into a CSA (m=4 overlapped, "
+                               "FP8 + bf16-RoPE entries, MXFP4 keys) and an HCA (m'=128, bf16) layer",
+                   "sequences": B, "q_pos": P},
+        "roofline": {"kernel": "compress_kernel (append, %s)" % dom, "bound": "hbm",
+                     "achieved": res[dom]["achieved_GBps"], "peak": PEAK["hbm"], "unit": "GB/s",
+                     "frac": round(res[dom]["achieved_GBps"] / PEAK["hbm"], 5), "traffic": None},
+        "append_probe": res, "algorithmic_bytes_per_step": tot_bytes,
+        "cpu_baseline": None if no_cpu else append_cpu_baseline()}), flush=True)
+
+
+def append_cpu_baseline(seqs=64, T=32768):
+    """The compression oracle with the storage encoders over `seqs`
+    sequences of T tokens for both layers, scaled to appended tokens/s."""
+    import oracle
+    rng = np.random.default_rng(0)
+    t0 = time.time()
+    for _ in range(seqs):
+        kv = oracle.bf16_from_f32((rng.standard_normal((T, 128)) * 0.1).astype(np.float32))
+        ik = oracle.bf16_from_f32((rng.standard_normal((T, 64)) * 0.1).astype(np.float32))
+        ent, kid = oracle.compress(kv, rng.standard_normal(8).astype(np.float32), 4, 1, ik=ik)
+        oracle.store_entries_fp8(ent)
+        oracle.mxfp4_encode(kid)
+        ent, _ = oracle.compress(kv, rng.standard_normal(128).astype(np.float32), 128, 0)
+        oracle.bf16_from_f32(ent)
+    t = time.time() - t0
+    return {"value": round(seqs * T / t, 1), "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
+            "sample": "%d sequences x %d tokens through the compression oracle and storage encoders, "
+                      "CSA and HCA layer, %.2f s" % (seqs, T, t)}
 
 
 # ---------------------------------------------------------------- workloads --
@@ -576,10 +660,10 @@ def main():
         copy_probe()
         return
     if args.append_probe:
-        append_probe()
+        append_probe(no_cpu=args.no_cpu)
         return
     if args.proj_probe:
-        proj_probe()
+        proj_probe(no_cpu=args.no_cpu)
         return
     wl = {1: CsaLayer, 2: HcaLayer, 3: CsaLayer, 4: DecodeLayer, 5: PairLayer}[args.config](args.config)
     nk = len(wl.kernels)
