@@ -52,6 +52,8 @@ def lib():
             "orc_store_entries_fp8_n": (None, [P, i64, i32, i32, P, P, P]),
             "orc_load_entries_fp8_n": (None, [P, P, P, i64, i32, i32, P]),
             "orc_mxfp4_encode_rows": (None, [P, i64, i32, P, P]),
+            "orc_store_entries_nvfp4_n": (None, [P, i64, P, P]),
+            "orc_load_entries_nvfp4_n": (None, [P, P, i64, P]),
             "orc_mxfp4_decode_rows": (None, [P, P, i64, i32, P]),
             "orc_compress": (i32, [P, P, P, P, P, P, P, i32, i64, i32, i32, i32, i32,
                                    i32, dbl, P, P]),
@@ -128,6 +130,28 @@ def mxfp4_decode(codes, scales):
     rows = codes.size // (n // 2)
     out = np.empty(codes.shape[:-1] + (n,), np.float32)
     lib().orc_mxfp4_decode_rows(_p(codes), _p(scales), rows, n, _p(out))
+    return out
+
+
+def store_entries_nvfp4(rows_f32):
+    """[n, 128] fp32 post-RoPE entries -> (records [n, 72] u8: e2m1 codes +
+    e4m3 block scales, scale [n] f32)."""
+    r = _c(rows_f32, np.float32)
+    assert r.shape[-1] == 128
+    n = r.size // 128
+    recs = np.empty(r.shape[:-1] + (72,), np.uint8)
+    sc = np.empty(r.shape[:-1], np.float32)
+    lib().orc_store_entries_nvfp4_n(_p(r), n, _p(recs), _p(sc))
+    return recs, sc
+
+
+def load_entries_nvfp4(recs, scale):
+    """NVFP4 records + scales -> fp64 rows [n, 128]."""
+    recs = _c(recs, np.uint8)
+    scale = _c(scale, np.float32)
+    n = recs.size // 72
+    out = np.empty(recs.shape[:-1] + (128,), np.float64)
+    lib().orc_load_entries_nvfp4_n(_p(recs), _p(scale), n, _p(out))
     return out
 
 

@@ -291,6 +291,65 @@ void orc_store_entry_fp8(const float* row, int D, int rope_dims,
     for (int d = nq; d < D; ++d) rope_out[d - nq] = orc_bf16_from_f32(row[d]);
 }
 
+/* NVFP4 entry storage, the V4.1 cache variant: the pages (the Russian
+ * summary of V4.1-Flash) store the compressed KV cache in NVFP4, quantised
+ * after RoPE, with the SWA window in FP8.  NVFP4 itself is NVIDIA's format:
+ * e2m1 elements in blocks of 16 with an e4m3 block scale, and an fp32
+ * second-level scale.  The reading taken for a cache written entry by entry:
+ * the second-level scale is per entry, s = amax(entry) / (6 * 448), so the
+ * block holding amax gets block scale 448; block j's scale is
+ * b_j = e4m3(amax_j / (6 s)) (RNE, saturating); an element is
+ * e2m1(x / (e4m3_value(b_j) * s)) (RNE on the e2m1 grid, saturating at 6),
+ * 0 where the block scale is 0.  Every step is one fp32 operation, rounded
+ * to nearest even, in that order.  Record: 64 bytes of codes (dim 2i in the
+ * low nibble of byte i, dim 2i+1 in the high nibble), then the 8 block
+ * scales; the fp32 scale is stored apart. */
+void orc_store_entry_nvfp4(const float* row, uint8_t* rec_out, float* scale_out)
+{
+    float amax = 0.0f;
+    for (int d = 0; d < 128; ++d) { float a = fabsf(row[d]); if (a > amax) amax = a; }
+    volatile float s = amax / 2688.0f;
+    *scale_out = s;
+    memset(rec_out, 0, 72);
+    if (s == 0.0f) return;
+    volatile float d6 = 6.0f * s;
+    for (int j = 0; j < 8; ++j) {
+        float bamax = 0.0f;
+        for (int i = 0; i < 16; ++i) { float a = fabsf(row[16 * j + i]); if (a > bamax) bamax = a; }
+        volatile float t = bamax / d6;
+        uint8_t b = orc_e4m3_from_f32(t);
+        rec_out[64 + j] = b;
+        volatile float sb = orc_e4m3_to_f32(b) * s;
+        if (sb == 0.0f) continue;
+        for (int i = 0; i < 16; ++i) {
+            int d = 16 * j + i;
+            volatile float q = row[d] / sb;
+            int idx = e2m1_round_index(fabs((double)q));
+            uint8_t c = (uint8_t)idx;
+            if (q < 0 && idx != 0) c |= 8;
+            rec_out[d >> 1] |= (uint8_t)((d & 1) ? (c << 4) : c);
+        }
+    }
+}
+
+void orc_store_entries_nvfp4_n(const float* rows, int64_t n, uint8_t* recs, float* scale)
+{
+    for (int64_t i = 0; i < n; ++i) orc_store_entry_nvfp4(rows + i * 128, recs + i * 72, scale + i);
+}
+
+/* NVFP4 records -> fp64 rows: e2m1 x e4m3 x s, exact in fp64. */
+void orc_load_entries_nvfp4_n(const uint8_t* recs, const float* scale, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const uint8_t* r = recs + i * 72;
+        for (int d = 0; d < 128; ++d) {
+            uint8_t c = (d & 1) ? (r[d >> 1] >> 4) : (r[d >> 1] & 15);
+            out[i * 128 + d] = (double)orc_e2m1_to_f32(c) * (double)orc_e4m3_to_f32(r[64 + d / 16]) *
+                               (double)scale[i];
+        }
+    }
+}
+
 /* ========================================================================== */
 /* Lightning indexer and top-k                                                */
 /* ========================================================================== */

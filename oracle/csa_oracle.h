@@ -118,6 +118,9 @@ void orc_mxfp4_encode_rows(const float* x, int64_t rows, int n_per_row,
                            uint8_t* codes, uint8_t* scales);
 void orc_mxfp4_decode_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                            int n_per_row, float* out);
+void orc_store_entry_nvfp4(const float* row, uint8_t* rec_out, float* scale_out);
+void orc_store_entries_nvfp4_n(const float* rows, int64_t n, uint8_t* recs, float* scale);
+void orc_load_entries_nvfp4_n(const uint8_t* recs, const float* scale, int64_t n, double* out);
 
 #ifdef __cplusplus
 }
