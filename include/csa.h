@@ -62,6 +62,8 @@ extern "C" {
 #define CSA_FMT_BF16 0          /* entries [.., 128] bf16 / indexer [.., 64] bf16 */
 #define CSA_FMT_MXFP4 1         /* indexer: codes [.., 32] u8 + scales [.., 2] u8 */
 #define CSA_FMT_FP8_ROPE_BF16 2 /* entries: e4m3 [.., 64] + bf16 [.., 64] + f32 scale [..] */
+#define CSA_FMT_NVFP4 3         /* entries: records [.., 72] u8 (64 B e2m1 codes of the 128
+                                   post-RoPE dims + 8 e4m3 scales of 16-dim blocks) + f32 scale [..] */
 
 /*
  * csa_compress -- token-level compressor (CSA: m = 4 with overlap; HCA:
@@ -94,8 +96,17 @@ extern "C" {
  *  entries_out       entry_fmt BF16: [B, N_new, 128] bf16.
  *                    entry_fmt FP8_ROPE_BF16: [B, N_new, 64] e4m3 codes of
  *                    x / scale, scale = amax(dims 0..63) / 448 (fp32).
+ *                    entry_fmt NVFP4 (the V4.1 variant of the Russian
+ *                    summary: the cache held in NVFP4, quantised after RoPE):
+ *                    [B, N_new, 72] u8 records.  Per entry s = amax / 2688
+ *                    (= amax / (6 * 448)); block j (dims 16j .. 16j+15) has
+ *                    the e4m3 scale b_j = e4m3(amax_j / (6 s)); dim d is the
+ *                    e2m1 code of x_d / (b_j s), 0 when b_j s = 0 (every step
+ *                    one fp32 operation, round to nearest even; e4m3 and
+ *                    e2m1 saturate).  Bytes 0..63: codes, dim 2i in the low
+ *                    nibble of byte i; bytes 64..71: b_0 .. b_7.
  *  entries_rope_out  FP8_ROPE_BF16 only: [B, N_new, 64] bf16 (dims 64..127)
- *  entry_scale_out   FP8_ROPE_BF16 only: [B, N_new] fp32
+ *  entry_scale_out   FP8_ROPE_BF16 and NVFP4: [B, N_new] fp32
  *  kidx_out          [B, N_new, 64] bf16, or [B, N_new, 32] MXFP4 codes
  *  kidx_scale_out    MXFP4 only: [B, N_new, 2] e8m0
  * Returns CSA_INVALID_ARG for a bad shape, format or missing prev rows.

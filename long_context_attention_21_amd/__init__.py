@@ -14,12 +14,12 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (FMT_BF16, FMT_FP8_ROPE_BF16, FMT_MXFP4, CsaError, check, lib)
+from ._lib import (FMT_BF16, FMT_FP8_ROPE_BF16, FMT_MXFP4, FMT_NVFP4, CsaError, check, lib)
 
 __all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend",
            "csa_project_in", "csa_project_qidx", "csa_project_out", "version",
            "CsaError",
-           "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16"]
+           "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16", "FMT_NVFP4"]
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
 
@@ -41,7 +41,7 @@ def _stream(stream):
 
 
 def _fmt(name):
-    return {"bf16": FMT_BF16, "mxfp4": FMT_MXFP4, "fp8": FMT_FP8_ROPE_BF16}[name]
+    return {"bf16": FMT_BF16, "mxfp4": FMT_MXFP4, "fp8": FMT_FP8_ROPE_BF16, "nvfp4": FMT_NVFP4}[name]
 
 
 def version():
@@ -52,6 +52,8 @@ def csa_compress(kv, beta, m, overlap, pos0=0, ik=None, z=None, prev_kv=None, pr
                  prev_z=None, rope_dims=64, rope_base=10000.0, entry_fmt="bf16", kidx_fmt="mxfp4",
                  out=None, stream=None):
     """kv [B, T, 128] bf16 -> dict(entries, entries_rope, entry_scale, kidx, kidx_scale).
+    entry_fmt "bf16", "fp8" (e4m3 + bf16 RoPE dims + scale) or "nvfp4"
+    (records [B, N, 72] u8 + scale).
     ``out`` may hold preallocated output tensors under the same keys (e.g.
     views into a larger cache)."""
     B, T, D = kv.shape
@@ -63,9 +65,10 @@ def csa_compress(kv, beta, m, overlap, pos0=0, ik=None, z=None, prev_kv=None, pr
         if ef == FMT_BF16:
             out["entries"] = torch.empty((B, n_new, D), dtype=torch.bfloat16, device=dev)
         else:
-            out["entries"] = torch.empty((B, n_new, 64), dtype=torch.uint8, device=dev)
+            out["entries"] = torch.empty((B, n_new, 72 if ef == FMT_NVFP4 else 64), dtype=torch.uint8, device=dev)
     if ef == FMT_FP8_ROPE_BF16:
         out.setdefault("entries_rope", torch.empty((B, n_new, 64), dtype=torch.bfloat16, device=dev))
+    if ef in (FMT_FP8_ROPE_BF16, FMT_NVFP4):
         out.setdefault("entry_scale", torch.empty((B, n_new), dtype=torch.float32, device=dev))
     if ik is not None:
         if kf == FMT_BF16:
@@ -134,13 +137,19 @@ def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=12
                entries_rope=None, entry_scale=None, rope_dims=64, rope_base=10000.0, N=None,
                out=None, ws=None, stream=None):
     """q [B, n, H, 128] bf16; entries [B, N, 128] bf16 (or e4m3 [B, N, 64] with
-    entries_rope/entry_scale); idx [B, n, k] int32; win_kv [B, W, 128] bf16.
+    entries_rope/entry_scale, or NVFP4 records [B, N, 72] u8 with entry_scale
+    only); idx [B, n, k] int32; win_kv [B, W, 128] bf16.
     ``ws``: workspace of csa_attend_workspace_bytes() bytes (allocated here
     when needed and not given)."""
     B, n, H, D = q.shape
     if N is None:
         N = entries.shape[1]
-    ef = FMT_BF16 if entries_rope is None else FMT_FP8_ROPE_BF16
+    if entries_rope is not None:
+        ef = FMT_FP8_ROPE_BF16
+    elif entry_scale is not None:
+        ef = FMT_NVFP4  # NVFP4 records [B, N, 72] u8 + entry_scale
+    else:
+        ef = FMT_BF16
     if out is None:
         out = torch.empty_like(q, dtype=torch.bfloat16)
     win_len = 0 if win_kv is None else win_kv.shape[1]

@@ -19,6 +19,7 @@ CSA_HIP_ERROR = -4
 FMT_BF16 = 0
 FMT_MXFP4 = 1
 FMT_FP8_ROPE_BF16 = 2
+FMT_NVFP4 = 3
 
 EXPORTS = ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_workspace_bytes",
            "csa_index_topk_fallbacks", "csa_attend", "csa_attend_workspace_bytes", "hca_attend", "csa_project_in",

@@ -74,11 +74,13 @@ int csa_compress(const void* kv, const void* ik, const float* z, const float* be
   if ((int64_t)B * n_new == 0) return ok();
   REQUIRE(kv != nullptr, "csa_compress: kv is NULL");
   REQUIRE(entries_out != nullptr, "csa_compress: entries_out is NULL");
-  REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16,
+  REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16 || entry_fmt == CSA_FMT_NVFP4,
           "csa_compress: entry_fmt=%d unsupported", entry_fmt);
   if (entry_fmt == CSA_FMT_FP8_ROPE_BF16)
     REQUIRE(entries_rope_out && entry_scale_out,
             "csa_compress: FP8 entries need entries_rope_out and entry_scale_out");
+  if (entry_fmt == CSA_FMT_NVFP4)
+    REQUIRE(entry_scale_out, "csa_compress: NVFP4 entries need entry_scale_out");
   if (ik) {
     REQUIRE(d_idx == 64, "csa_compress: d_idx=%d unsupported (must be 64)", d_idx);
     if (kidx_out) {
@@ -150,10 +152,12 @@ int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new,
     const int64_t i = (t + 1) / m - 1;
     REQUIRE(i < N_cap, "csa_cache_append: entry %lld does not fit the caches (N_cap=%d)", (long long)i, N_cap);
     REQUIRE(entries != nullptr, "csa_cache_append: entries is NULL");
-    REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16,
+    REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16 || entry_fmt == CSA_FMT_NVFP4,
             "csa_cache_append: entry_fmt=%d unsupported", entry_fmt);
     if (entry_fmt == CSA_FMT_FP8_ROPE_BF16)
       REQUIRE(entries_rope && entry_scale, "csa_cache_append: FP8 entries need entries_rope and entry_scale");
+    if (entry_fmt == CSA_FMT_NVFP4)
+      REQUIRE(entry_scale, "csa_cache_append: NVFP4 entries need entry_scale");
     if (ik_new) {
       REQUIRE(kidx != nullptr, "csa_cache_append: kidx is NULL");
       REQUIRE(kidx_fmt == CSA_FMT_BF16 || kidx_fmt == CSA_FMT_MXFP4, "csa_cache_append: kidx_fmt=%d unsupported",
@@ -269,12 +273,13 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   if ((int64_t)B * n == 0) return ok();
   REQUIRE(q != nullptr && out != nullptr, "%s: q and out must be non-NULL", name);
   REQUIRE(N == 0 || entries != nullptr, "%s: entries is NULL", name);
-  if (mode == 0 || mode == 1) {
+  if (mode == 0 || mode == 1 || mode == 3) {
     REQUIRE(k <= 2048, "%s: k=%d must be <= 2048", name, k);
     REQUIRE(k == 0 || idx != nullptr, "%s: idx is NULL", name);
     REQUIRE(aligned16(idx), "%s: idx must be 16-byte aligned", name);
   }
   if (mode == 1) REQUIRE(N == 0 || (entries_rope && entry_scale), "%s: FP8 entries need entries_rope and entry_scale", name);
+  if (mode == 3) REQUIRE(N == 0 || entry_scale, "%s: NVFP4 entries need entry_scale", name);
   if (n_win > 0) {
     REQUIRE(win_kv != nullptr, "%s: win_kv is NULL but n_win > 0", name);
     int64_t lo = q_pos0 - n_win + 1;
@@ -322,16 +327,18 @@ int csa_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const 
                const int32_t* idx, int k, const void* win_kv, int64_t win_pos0, int win_len,
                int n_win, const float* sink, int rope_dims, float rope_base, void* out, void* ws,
                size_t ws_bytes, void* stream) {
-  REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16,
+  REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16 || entry_fmt == CSA_FMT_NVFP4,
           "csa_attend: entry_fmt=%d unsupported", entry_fmt);
-  return attend_common(entry_fmt == CSA_FMT_BF16 ? 0 : 1, q, B, n, q_pos0, H, D, entries,
+  const int mode = entry_fmt == CSA_FMT_BF16 ? 0 : entry_fmt == CSA_FMT_FP8_ROPE_BF16 ? 1 : 3;
+  return attend_common(mode, q, B, n, q_pos0, H, D, entries,
                        entries_rope, entry_scale, N, m, idx, k, win_kv, win_pos0, win_len, n_win,
                        sink, rope_dims, rope_base, out, ws, ws_bytes, stream, "csa_attend");
 }
 
 size_t csa_attend_workspace_bytes(int B, int n, int k, int n_win, int entry_fmt) {
   if (B < 0 || n < 0 || k < 0 || n_win < 0) return 0;
-  return csa::attend_workspace(entry_fmt == CSA_FMT_FP8_ROPE_BF16 ? 1 : 0, B, n, k, n_win);
+  return csa::attend_workspace(entry_fmt == CSA_FMT_FP8_ROPE_BF16 ? 1 : entry_fmt == CSA_FMT_NVFP4 ? 3 : 0, B, n,
+                               k, n_win);
 }
 
 int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const void* entries,

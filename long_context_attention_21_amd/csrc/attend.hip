@@ -46,7 +46,7 @@ struct ChunkRegs {
 // SPLIT: work-group (token, part) takes chunks [part * cpp, (part+1) * cpp)
 // and leaves its unnormalised O, reference and row sums in the workspace for
 // attend_combine_kernel.
-template <int NHT, int MODE, bool SPLIT = false>  // MODE 0: CSA bf16 entries, 1: CSA fp8+bf16 entries, 2: HCA
+template <int NHT, int MODE, bool SPLIT = false>  // MODE 0: CSA bf16, 1: CSA fp8+bf16, 3: CSA NVFP4 entries; 2: HCA
 __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][32 * KP];
   __shared__ __attribute__((aligned(16))) int32_t Is[MODE == 2 ? 4 : kMaxK];  // the token's idx row
@@ -187,7 +187,12 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
       uniform_ptr(p.win ? p.win + (int64_t)bu * p.win_len * 128 : p.q), (short)0,
       p.win ? __builtin_amdgcn_readfirstlane(p.win_len * 256) : 0, 0x00020000);
   __amdgpu_buffer_rsrc_t rE, rR = rW, rS = rW;
-  if (MODE == 1) {
+  if (MODE == 3) {
+    rE = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t*)p.entries + (int64_t)bu * p.N * 72),
+                                           (short)0, __builtin_amdgcn_readfirstlane(p.N * 72), 0x00020000);
+    rS = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.entry_scale + (int64_t)bu * p.N), (short)0,
+                                           __builtin_amdgcn_readfirstlane(p.N * 4), 0x00020000);
+  } else if (MODE == 1) {
     rE = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t*)p.entries + (int64_t)bu * p.N * 64),
                                            (short)0, __builtin_amdgcn_readfirstlane(p.N * 64), 0x00020000);
     rR = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.entries_rope + (int64_t)bu * p.N * 64), (short)0,
@@ -215,7 +220,19 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
       if (c >= c_hi) row = -1;
       R.v[kt] = row >= 0;
       R.sc[kt] = 1.0f;
-      if (MODE == 1 && ent) {
+      if (MODE == 3 && ent) {
+        // the lane's dims ks*32 + 8g .. +7: 4 code bytes at 16 ks + 4 g; the
+        // 8 block scales ride in words 1 and 2 of the first slot until the
+        // chunk is dequantised
+        const int o = row >= 0 ? row * 72 : kOOB;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          R.r[kt][ks] = u32x4{__builtin_amdgcn_raw_buffer_load_b32(rE, o + 16 * ks + 4 * g, 0, 0), 0u, 0u, 0u};
+        const auto bs = __builtin_amdgcn_raw_buffer_load_b64(rE, o + 64, 0, 0);
+        R.r[kt][0][1] = bs[0];
+        R.r[kt][0][2] = bs[1];
+        R.sc[kt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, row >= 0 ? row * 4 : kOOB, 0, 0));
+      } else if (MODE == 1 && ent) {
         const int oc = row >= 0 ? row * 64 + 8 * g : kOOB;
         const int orr = row >= 0 ? row * 128 + 16 * g : kOOB;
 #pragma unroll
@@ -237,6 +254,22 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   // post-process a loaded chunk: fp8 dequantisation, window-row rotation
   auto finish = [&](int c, ChunkRegs& R) {
     if (c >= c_hi) return;
+    if (MODE == 3 && c < n_ent_chunks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint32_t blo = R.r[kt][0][1], bhi = R.r[kt][0][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int blk = 2 * ks + (g >> 1);  // 16-dim block of dims ks*32 + 8g .. +7
+          const uint32_t bcode = ((blk < 4 ? blo : bhi) >> (8 * (blk & 3))) & 255u;
+          const float sb = e4m3_to_f32(bcode) * R.sc[kt];
+          const uint32_t w = R.r[kt][ks][0];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            R.r[kt][ks][e] = pack_bf16(e2m1_to_f32((w >> (8 * e)) & 15u) * sb, e2m1_to_f32((w >> (8 * e + 4)) & 15u) * sb);
+        }
+      }
+    }
     if (MODE == 1 && c < n_ent_chunks) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -1016,7 +1049,7 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p) {
 template <int MODE>
 static hipError_t launch_mode(const AttendParams& p, hipStream_t stream) {
   const int nht = (p.H + 15) / 16;
-  const bool split = MODE == 1 && p.ws != nullptr && p.parts > 1;
+  const bool split = (MODE == 1 || MODE == 3) && p.ws != nullptr && p.parts > 1;
   dim3 grid((unsigned)((int64_t)p.B * p.n * (split ? p.parts : 1))), block(64);
   if (split) {
     switch (nht) {
@@ -1039,10 +1072,10 @@ static hipError_t launch_mode(const AttendParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// FP8 entries with few query rows: one work-group per token would leave most
+// FP8 or NVFP4 entries with few query rows: one work-group per token would leave most
 // CUs idle, so each token's chunks are split over several work-groups.
 static int attend_parts(int mode, int B, int n, int k, int n_win) {
-  if (mode != 1 || (int64_t)B * n > 512) return 1;
+  if ((mode != 1 && mode != 3) || (int64_t)B * n > 512) return 1;
   const int chunks = (k + 31) / 32 + (n_win + 31) / 32;
   if (chunks < 2 * kAttendChunksPerPart) return 1;
   return (chunks + kAttendChunksPerPart - 1) / kAttendChunksPerPart;
@@ -1061,6 +1094,7 @@ hipError_t launch_attend(const AttendParams& p_in, int mode, hipStream_t stream)
   switch (mode) {
     case 0: return launch_ring<0>(p, stream);
     case 1: return launch_mode<1>(p, stream);
+    case 3: return launch_mode<3>(p, stream);
     case 2: return launch_ring<2>(p, stream);
   }
   return hipErrorInvalidValue;

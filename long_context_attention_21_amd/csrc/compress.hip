@@ -4,7 +4,8 @@
 // Intelligence" wiki summary, Proposed method item 1 (every m tokens become
 // one entry by a weighted average; adjacent blocks overlap for CSA);
 // "deepseek V4 技术论文" 1.1 (C^b overlaps C^a).  Storage formats: wiki
-// summary, Training infrastructure item 5 (RoPE dims BF16, other dims FP8)
+// summary, Training infrastructure item 5 (RoPE dims BF16, other dims FP8);
+// the V4.1 variant of the Russian summary stores post-RoPE entries in NVFP4
 // and Post-training item 3 (MXFP4 indexer QK path).
 //
 // Design: HBM-bound strided pooling.  One wave per output entry; lane l owns
@@ -180,6 +181,27 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
   const int64_t orow = p.append ? (int64_t)b * p.N_cap + i : (int64_t)b * p.n_new + e;
   if (p.entry_fmt == 0) {
     ((uint32_t*)p.entries_out)[orow * 64 + lane] = pack_bf16(a0, a1);
+  } else if (p.entry_fmt == 3) {
+    // NVFP4 (post-RoPE, all 128 dims): s = amax / (6 * 448) per entry; block
+    // j = dims 16j .. 16j+15 (lanes 8j .. 8j+7) gets the e4m3 scale of
+    // amax_j / (6 s); codes are e2m1(x / (b_j s)); one fp32 operation per
+    // step, rounded to nearest even.  Record: 64 code bytes, 8 scale bytes.
+    float amax = fmaxf(fabsf(a0), fabsf(a1));
+    float bamax = amax;
+    for (int off = 4; off >= 1; off >>= 1) bamax = fmaxf(bamax, __shfl_xor(bamax, off));
+    amax = bamax;
+    for (int off = 32; off >= 8; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float scale = __fdiv_rn(amax, 2688.0f);
+    uint32_t code = 0, bcode = 0;
+    if (scale != 0.0f) {
+      bcode = f32_to_e4m3(__fdiv_rn(bamax, __fmul_rn(6.0f, scale)));
+      const float sb = __fmul_rn(e4m3_to_f32(bcode), scale);
+      if (sb != 0.0f) code = f32_to_e2m1(__fdiv_rn(a0, sb)) | (f32_to_e2m1(__fdiv_rn(a1, sb)) << 4);
+    }
+    uint8_t* rec = (uint8_t*)p.entries_out + orow * 72;
+    rec[lane] = (uint8_t)code;
+    if ((lane & 7) == 0) rec[64 + (lane >> 3)] = (uint8_t)bcode;
+    if (lane == 0) p.entry_scale_out[orow] = scale;
   } else {
     // dims 0..63 (lanes 0..31) -> e4m3 with scale amax/448; dims 64..127 -> bf16
     float amax = (lane < 32) ? fmaxf(fabsf(a0), fabsf(a1)) : 0.0f;

@@ -97,6 +97,9 @@ def oracle_compress_store(orc, kv, beta, m, overlap, ik=None, z=None, pos0=0, pr
     if entry_fmt == "bf16":
         res["entries"] = orc.bf16_from_f32(ent)
         res["entries_f64"] = orc.bf16_to_f64(res["entries"])
+    elif entry_fmt == "nvfp4":
+        res["entries"], res["entry_scale"] = orc.store_entries_nvfp4(ent)
+        res["entries_f64"] = orc.load_entries_nvfp4(res["entries"], res["entry_scale"])
     else:
         c, r, s = orc.store_entries_fp8(ent)
         res["entries"], res["entries_rope"], res["entry_scale"] = c, r, s

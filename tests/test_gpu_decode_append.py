@@ -27,6 +27,9 @@ def _empty_caches(B, N_cap, efmt, kfmt, with_ik):
     c = {}
     if efmt == "bf16":
         c["entries"] = torch.zeros((B, N_cap, 128), dtype=torch.bfloat16, device=cu)
+    elif efmt == "nvfp4":
+        c["entries"] = torch.zeros((B, N_cap, 72), dtype=torch.uint8, device=cu)
+        c["entry_scale"] = torch.zeros((B, N_cap), dtype=torch.float32, device=cu)
     else:
         c["entries"] = torch.zeros((B, N_cap, 64), dtype=torch.uint8, device=cu)
         c["entries_rope"] = torch.zeros((B, N_cap, 64), dtype=torch.bfloat16, device=cu)
@@ -69,6 +72,7 @@ def _window_start(t):
     (4, 1, True, False, "mxfp4", "fp8"),     # CSA decode caches (FP8 + bf16 RoPE dims, MXFP4 keys)
     (4, 1, True, True, "bf16", "bf16"),      # with slot-logit offsets z
     (128, 0, False, False, "mxfp4", "bf16"),  # HCA: the block is the whole ring
+    (4, 1, True, False, "mxfp4", "nvfp4"),   # the V4.1 variant: NVFP4 entries
 ])
 def test_cache_append_matches_whole_sequence(orc, m, overlap, with_ik, with_z, kfmt, efmt):
     print("append case m=%d overlap=%d ik=%s z=%s kfmt=%s efmt=%s" % (m, overlap, with_ik, with_z, kfmt, efmt),
@@ -88,6 +92,9 @@ def test_cache_append_matches_whole_sequence(orc, m, overlap, with_ik, with_z, k
                                     z=None if z is None else z[b], kidx_fmt=kfmt, entry_fmt=efmt)
         if efmt == "bf16":
             assert np.array_equal(host_bits(caches["entries"])[b, :n_full], ref["entries"])
+        elif efmt == "nvfp4":
+            assert np.array_equal(host(caches["entries"])[b, :n_full], ref["entries"])
+            assert np.array_equal(host(caches["entry_scale"])[b, :n_full], ref["entry_scale"])
         else:
             assert np.array_equal(host(caches["entries"])[b, :n_full], ref["entries"])
             assert np.array_equal(host_bits(caches["entries_rope"])[b, :n_full], ref["entries_rope"])
@@ -98,7 +105,9 @@ def test_cache_append_matches_whole_sequence(orc, m, overlap, with_ik, with_z, k
         elif with_ik:
             assert np.array_equal(host_bits(caches["kidx"])[b, :n_full], ref["kidx"])
         # rows past the last complete block are untouched
-        assert not host_bits(caches["entries"] if efmt == "bf16" else caches["entries_rope"])[b, n_full:].any()
+        rest = {"bf16": lambda: host_bits(caches["entries"]), "fp8": lambda: host_bits(caches["entries_rope"]),
+                "nvfp4": lambda: host(caches["entries"])}[efmt]()
+        assert not rest[b, n_full:].any()
     # the ring holds the raw window of the last position, contiguous from s0
     t = T - 1
     j0, s0 = _window_start(t)

@@ -27,6 +27,8 @@ def _bf16(rng, shape, scale):
     (4, 1, True, "mxfp4", "fp8"),
     (128, 0, False, None, "bf16"),
     (8, 0, True, "mxfp4", "fp8"),
+    (4, 1, True, "mxfp4", "nvfp4"),
+    (128, 0, False, None, "nvfp4"),
 ])
 def test_compress_matches_oracle(orc, m, overlap, with_z, kfmt, efmt):
     rng = np.random.default_rng(100 + m)
@@ -46,6 +48,9 @@ def test_compress_matches_oracle(orc, m, overlap, with_z, kfmt, efmt):
                                     entry_fmt=efmt)
         if efmt == "bf16":
             assert np.array_equal(host_bits(out["entries"])[b], ref["entries"])
+        elif efmt == "nvfp4":
+            assert np.array_equal(host(out["entries"])[b], ref["entries"])
+            assert np.array_equal(host(out["entry_scale"])[b], ref["entry_scale"])
         else:
             assert np.array_equal(host(out["entries"])[b], ref["entries"])
             assert np.array_equal(host_bits(out["entries_rope"])[b], ref["entries_rope"])
@@ -182,6 +187,8 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
         if efmt == "fp8":
             kw = dict(entries_rope=dev(np.stack([e["entries_rope"] for e in ents])),
                       entry_scale=dev(np.stack([e["entry_scale"] for e in ents])))
+        elif efmt == "nvfp4":
+            kw = dict(entry_scale=dev(np.stack([e["entry_scale"] for e in ents])))
         out = L.csa_attend(dev(q), e_dev, dev(idx), q_pos0=q_pos0, m=m, win_kv=win, win_pos0=0,
                            n_win=n_win, sink=dev(sk) if sink else None, **kw)
     else:
@@ -219,6 +226,11 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
     dict(B=1, n=3, H=16, q_pos0=2200, m=4, mode="csa", k=500, efmt="fp8", kv_scale=1.0, sink_shift=-60.0,
          q_scale=24.0),
     dict(B=2, n=1, H=64, q_pos0=60, m=4, mode="csa", k=512, efmt="fp8", kv_scale=1.0),  # parts without keys
+    # NVFP4 entries (the V4.1 cache variant): many rows, then the split decode
+    dict(B=2, n=50, H=64, q_pos0=400, m=4, mode="csa", k=96, efmt="nvfp4", kv_scale=1.0),
+    dict(B=3, n=2, H=64, q_pos0=2200, m=4, mode="csa", k=512, efmt="nvfp4", kv_scale=1.0),
+    dict(B=1, n=3, H=16, q_pos0=2200, m=4, mode="csa", k=500, efmt="nvfp4", kv_scale=1.0, sink_shift=-60.0,
+         q_scale=24.0),
 ])
 def test_attend_matches_oracle(orc, case):
     print("attend case %s" % case, flush=True)
