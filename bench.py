@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--print-sha", action="store_true", help="print the kernel source hashes and exit")
     ap.add_argument("--append-probe", action="store_true",
                     help="only time the decode cache write path (csa_cache_append), 64 sequences at 1M")
+    ap.add_argument("--entry-fmt", default="fp8", choices=["fp8", "nvfp4"],
+                    help="config 4 only: the decode cache's entry format (fp8: e4m3 + bf16 RoPE dims; nvfp4: "
+                         "the V4.1 variant, post-RoPE NVFP4)")
     ap.add_argument("--proj-probe", action="store_true",
                     help="only time the projections around the path (csa_project_in with the indexer "
                          "query, csa_project_out) at the prefill chunk shape")
@@ -433,8 +436,9 @@ def encode_cache(L, entries_bf16, keys_bf16, entry_fmt, out):
 
 class DecodeLayer:
     """Config 4: single-token CSA decode, 64 sequences at t = 1,048,576 over
-    262,144 FP8 + bf16 entries and MXFP4 indexer keys each (caches given):
-    csa_index_topk -> csa_attend."""
+    262,144 FP8 + bf16 entries (or NVFP4 entries, the V4.1 variant) and MXFP4
+    indexer keys each (caches given): csa_index_topk -> csa_attend."""
+    entry_fmt = "fp8"
 
     def __init__(self, cfg_id):
         import torch
@@ -447,8 +451,9 @@ class DecodeLayer:
         self.B, self.N, self.H, self.k = B, N, H, c["k"]
         self.n = B  # query tokens per step
         cu = "cuda"
-        self.codes = torch.empty((B, N, 64), dtype=torch.uint8, device=cu)
-        self.rope = torch.empty((B, N, 64), dtype=torch.bfloat16, device=cu)
+        efmt = self.entry_fmt
+        self.codes = torch.empty((B, N, 72 if efmt == "nvfp4" else 64), dtype=torch.uint8, device=cu)
+        self.rope = torch.empty((B, N, 64), dtype=torch.bfloat16, device=cu) if efmt == "fp8" else None
         self.scale = torch.empty((B, N), dtype=torch.float32, device=cu)
         self.kc = torch.empty((B, N, 32), dtype=torch.uint8, device=cu)
         self.ks = torch.empty((B, N, 2), dtype=torch.uint8, device=cu)
@@ -460,9 +465,11 @@ class DecodeLayer:
             from long_context_attention_21_amd.synth import to_bf16_bits
             e16 = dev_bf16(to_bf16_bits(ent)[None])
             k16 = dev_bf16(to_bf16_bits(ik)[None])
-            encode_cache(L, e16, k16, "fp8", {"entries": self.codes[b:b + 1], "entries_rope": self.rope[b:b + 1],
-                                              "entry_scale": self.scale[b:b + 1], "kidx": self.kc[b:b + 1],
-                                              "kidx_scale": self.ks[b:b + 1]})
+            outs = {"entries": self.codes[b:b + 1], "entry_scale": self.scale[b:b + 1], "kidx": self.kc[b:b + 1],
+                    "kidx_scale": self.ks[b:b + 1]}
+            if efmt == "fp8":
+                outs["entries_rope"] = self.rope[b:b + 1]
+            encode_cache(L, e16, k16, efmt, outs)
             self.swa[b] = dev_bf16(swa)
         q, q_I, w_I, sink = c["tail"]()
         log("decode caches generated and stored in %.1f s" % (time.time() - t0))
@@ -471,10 +478,12 @@ class DecodeLayer:
         self.out = torch.empty((B, 1, H, 128), dtype=torch.bfloat16, device=cu)
         self.kernels = ["csa_index_topk", "csa_attend"]
         keys = B * (min(self.k, N) + c["n_win"])
-        # bytes: the indexer scans every key (34 B); attention gathers k entries (196 B) + window (256 B)
+        # bytes: the indexer scans every key (34 B); attention gathers k entries (196 B FP8 + bf16,
+        # 76 B NVFP4) + window (256 B)
+        eb = 76 if efmt == "nvfp4" else 196
         self.work = {
             "csa_index_topk": ("hbm", B * N * 34),
-            "csa_attend": ("hbm", B * (min(self.k, N) * 196 + c["n_win"] * 256 + 2 * H * 256 + 4 * self.k)),
+            "csa_attend": ("hbm", B * (min(self.k, N) * eb + c["n_win"] * 256 + 2 * H * 256 + 4 * self.k)),
         }
         self.keys = keys
 
@@ -486,7 +495,7 @@ class DecodeLayer:
         if ev: ev[1].record()
         L.csa_attend(self.q, self.codes, self.idx, q_pos0=c["q_pos0"], m=4, win_kv=self.swa,
                      win_pos0=c["win_pos0"], sink=self.sink, entries_rope=self.rope, entry_scale=self.scale,
-                     out=self.out)
+                     out=self.out)  # entries_rope None: NVFP4 records
         if ev: ev[2].record()
 
     cpu_desc = ("%d sequences (all): oracle top-k over 262144 entries + attention for each query "
@@ -505,8 +514,12 @@ class DecodeLayer:
         t_rows = 0.0
         for b in range(nb):
             kdec = orc.mxfp4_decode(self.kc[b].cpu().numpy(), self.ks[b].cpu().numpy())
-            E = orc.load_entries_fp8(self.codes[b].cpu().numpy(), self.rope[b].view(torch_int16()).cpu().numpy()
-                                     .view(np.uint16), self.scale[b].cpu().numpy())
+            if self.rope is None:
+                E = orc.load_entries_nvfp4(self.codes[b].cpu().numpy(), self.scale[b].cpu().numpy())
+            else:
+                E = orc.load_entries_fp8(self.codes[b].cpu().numpy(),
+                                         self.rope[b].view(torch_int16()).cpu().numpy().view(np.uint16),
+                                         self.scale[b].cpu().numpy())
             swa = self.swa[b].view(torch_int16()).cpu().numpy().view(np.uint16)
             qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(qI[b]).astype(np.float32))
             t1 = time.time()
@@ -665,6 +678,10 @@ def main():
     if args.proj_probe:
         proj_probe(no_cpu=args.no_cpu)
         return
+    if args.entry_fmt != "fp8":
+        if args.config != 4:
+            sys.exit("--entry-fmt applies to config 4 only")
+        DecodeLayer.entry_fmt = args.entry_fmt
     wl = {1: CsaLayer, 2: HcaLayer, 3: CsaLayer, 4: DecodeLayer, 5: PairLayer}[args.config](args.config)
     nk = len(wl.kernels)
     log("warmup %d steps" % args.warmup)
@@ -722,15 +739,20 @@ def main():
                          "attention for those rows (%.1f s) plus whole-sequence compression "
                          "(%.1f s) charged pro rata" % (rows, t_rows, t_comp)}
 
-    cfg = {"workload": WORKLOAD[args.config], "global_batch": getattr(wl, "B", 1), "seq_len": wl.n,
+    wname = WORKLOAD[args.config]
+    dname = {1: "bf16", 2: "bf16", 3: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)",
+             4: "fp8 e4m3 + bf16 entries, bf16 MFMA (attention) + mxfp4 (indexer MFMA)",
+             5: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)"}[args.config]
+    if args.entry_fmt == "nvfp4":
+        wname = wname.replace("262144 FP8+bf16 entries", "262144 NVFP4 entries (post-RoPE, the V4.1 variant)")
+        dname = dname.replace("fp8 e4m3 + bf16 entries", "nvfp4 entries")
+    cfg = {"workload": wname, "global_batch": getattr(wl, "B", 1), "seq_len": wl.n,
            "heads": wl.H, "head_dim": 128}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {1: "bf16", 2: "bf16", 3: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)",
-                  4: "fp8 e4m3 + bf16 entries, bf16 MFMA (attention) + mxfp4 (indexer MFMA)",
-                  5: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)"}[args.config],
+        "dtype": dname,
         "data": "synthetic (seeded, numpy default_rng)", "config": cfg,
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
     }

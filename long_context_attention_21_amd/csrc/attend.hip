@@ -263,10 +263,18 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
           const int blk = 2 * ks + (g >> 1);  // 16-dim block of dims ks*32 + 8g .. +7
           const uint32_t bcode = ((blk < 4 ? blo : bhi) >> (8 * (blk & 3))) & 255u;
           const float sb = e4m3_to_f32(bcode) * R.sc[kt];
+          // the hardware conversion with scale 1 gives the two e2m1 values of
+          // byte e exactly (low nibble first); the block and entry scale
+          // follow in fp32
           const uint32_t w = R.r[kt][ks][0];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            R.r[kt][ks][e] = pack_bf16(e2m1_to_f32((w >> (8 * e)) & 15u) * sb, e2m1_to_f32((w >> (8 * e + 4)) & 15u) * sb);
+          const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+          const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+          const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+          const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+          R.r[kt][ks][0] = pack_bf16(v0[0] * sb, v0[1] * sb);
+          R.r[kt][ks][1] = pack_bf16(v1[0] * sb, v1[1] * sb);
+          R.r[kt][ks][2] = pack_bf16(v2[0] * sb, v2[1] * sb);
+          R.r[kt][ks][3] = pack_bf16(v3[0] * sb, v3[1] * sb);
         }
       }
     }

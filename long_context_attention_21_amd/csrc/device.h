@@ -23,6 +23,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -80,14 +81,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 
 // e2m1 code of v (v already divided by the block scale): nearest with ties
 // to the even code, saturating at 6.  Grid 0, .5, 1, 1.5, 2, 3, 4, 6.
-// e2m1 code (sign in bit 3) -> fp32: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6
-// built from the fields (exponent bias 1, one mantissa bit)
-__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
-  const uint32_t mag = c & 7u;
-  uint32_t bits = mag >= 2u ? (((mag >> 1) + 126u) << 23) | ((mag & 1u) << 22) : (mag ? 0x3f000000u : 0u);
-  return __builtin_bit_cast(float, bits | ((c & 8u) << 28));
-}
-
 __device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
   float a = fabsf(v);
   uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
