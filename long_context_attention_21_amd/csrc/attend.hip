@@ -283,12 +283,18 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+          // the hardware conversion with scale 1 gives two e4m3 values exactly
+          // (bytes 0-1, or 2-3 with the word select); the entry scale follows
           const uint32_t w0 = R.r[kt][ks][0], w1 = R.r[kt][ks][1];
           const float sc = R.sc[kt];
-          R.r[kt][ks][0] = pack_bf16(e4m3_to_f32(w0 & 255u) * sc, e4m3_to_f32((w0 >> 8) & 255u) * sc);
-          R.r[kt][ks][1] = pack_bf16(e4m3_to_f32((w0 >> 16) & 255u) * sc, e4m3_to_f32(w0 >> 24) * sc);
-          R.r[kt][ks][2] = pack_bf16(e4m3_to_f32(w1 & 255u) * sc, e4m3_to_f32((w1 >> 8) & 255u) * sc);
-          R.r[kt][ks][3] = pack_bf16(e4m3_to_f32((w1 >> 16) & 255u) * sc, e4m3_to_f32(w1 >> 24) * sc);
+          const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, false);
+          const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, true);
+          const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, false);
+          const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, true);
+          R.r[kt][ks][0] = pack_bf16(v0[0] * sc, v0[1] * sc);
+          R.r[kt][ks][1] = pack_bf16(v1[0] * sc, v1[1] * sc);
+          R.r[kt][ks][2] = pack_bf16(v2[0] * sc, v2[1] * sc);
+          R.r[kt][ks][3] = pack_bf16(v3[0] * sc, v3[1] * sc);
         }
     }
     if (c >= n_ent_chunks && p.rope) {
