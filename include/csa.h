@@ -300,7 +300,7 @@ int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D,
  * takes).  A width of 0 drops that output (its pointer may be NULL).
  * Outputs are written with row stride equal to their width.
  * Requirements: d a multiple of 32; n_lat in {16, 32, 64} when n_qidx > 0;
- * n_qidx a multiple of 32 with n_qidx * n_lat <= 32768; x and w_in below
+ * n_qidx a positive multiple of 32 (at most 2^20); x and w_in below
  * 2 GiB; x, w_in, w_up, lat_out and qidx_out 16-byte aligned.  Device
  * pointers, caller-owned; asynchronous on `stream`; nothing is launched on
  * error.

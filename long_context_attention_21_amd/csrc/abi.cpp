@@ -356,8 +356,8 @@ namespace {
 int qidx_check(const void* lat, int ld_lat, int r, const void* w_up, int n_qidx, const uint8_t* codes,
                const uint8_t* scales, const float* q_f32, const char* who) {
   REQUIRE(r == 16 || r == 32 || r == 64, "%s: rank r=%d must be 16, 32 or 64", who, r);
-  REQUIRE(n_qidx > 0 && n_qidx % 32 == 0 && n_qidx * r <= 32768,
-          "%s: n_qidx=%d must be a positive multiple of 32 with n_qidx * r <= 32768", who, n_qidx);
+  REQUIRE(n_qidx > 0 && n_qidx % 32 == 0 && n_qidx <= (1 << 20),
+          "%s: n_qidx=%d must be a positive multiple of 32, at most 2^20", who, n_qidx);
   REQUIRE(w_up && codes && scales, "%s: w_up, codes and scales must be non-NULL", who);
   REQUIRE(aligned16(w_up) && aligned16(codes) && aligned16(q_f32),
           "%s: w_up, codes and q_f32 must be 16-byte aligned", who);
@@ -404,6 +404,7 @@ int csa_project_in(const void* x, int M, int d, const void* w_in, int n_q, int n
   REQUIRE(N64 < (1 << 24), "csa_project_in: total output width %lld too large", (long long)N64);
   const int N = (int)N64;
   REQUIRE(N > 0, "csa_project_in: no output");
+  REQUIRE(n_qidx >= 0, "csa_project_in: n_qidx=%d must be >= 0", n_qidx);
   REQUIRE(x && w_in, "csa_project_in: x and w_in must be non-NULL");
   REQUIRE(aligned16(x) && aligned16(w_in), "csa_project_in: x and w_in must be 16-byte aligned");
   REQUIRE((int64_t)M * d * 2 < (1ll << 31) && (int64_t)N * d * 2 < (1ll << 31),

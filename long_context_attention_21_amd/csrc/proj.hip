@@ -74,6 +74,9 @@ __global__ __launch_bounds__(64 * NWM * NWN) void gemm_tn_kernel(GemmParams p, i
   // extent and read as zeros
   const u32x4 rA = dma_rsrc(uniform_ptr(p.A + (int64_t)z * p.a_zoff), p.a_bytes - (uint32_t)z * p.a_zbytes);
   const u32x4 rB = dma_rsrc(uniform_ptr(p.B + (int64_t)z * p.b_zoff), p.b_bytes);
+  // 32-bit byte offsets: below the extent for every row inside M (N); rows
+  // of a ragged last tile may wrap, which only loads values that are
+  // never stored
   const uint32_t lda2 = (uint32_t)p.lda * 2u, ldb2 = (uint32_t)p.ldb * 2u;
   const int nk = p.K >> 5;
 

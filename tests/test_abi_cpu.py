@@ -263,7 +263,7 @@ def _proj_in(L, **kw):
     (dict(n_lat=0), "needs the latent"),
     (dict(n_lat=24), "rank r=24"),
     (dict(n_qidx=48), "n_qidx=48"),
-    (dict(n_lat=64, n_qidx=1024), "n_qidx=1024"),   # W_up above 64 KB
+    (dict(n_qidx=-32), "n_qidx=-32"),
     (dict(qidx_scale_out=None), "non-NULL"),
     (dict(M=-1), "M=-1"),
     (dict(M=1 << 20, d=1024), "2 GiB"),
