@@ -62,8 +62,9 @@ def lib():
             "orc_topk": (None, [P, i32, i32, P]),
             "orc_index_topk_rows": (None, [P, P, P, i32, i32, i32, i32, i64, P, i32, i32,
                                            i32, P]),
-            "orc_attend_rows": (i32, [P, i32, i32, i64, P, i32, i32, P, i32, i32, P, i64,
+            "orc_attend_rows": (i32, [P, i32, i32, i64, P, i32, i32, P, i32, i32, P, P, i64,
                                       i32, i32, P, i32, dbl, P, i32, P]),
+            "orc_store_window_fp8_n": (None, [P, i64, i64, i32, dbl, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -130,6 +131,27 @@ def mxfp4_decode(codes, scales):
     rows = codes.size // (n // 2)
     out = np.empty(codes.shape[:-1] + (n,), np.float32)
     lib().orc_mxfp4_decode_rows(_p(codes), _p(scales), rows, n, _p(out))
+    return out
+
+
+def store_window_fp8(win_bits, pos0, rope_dims=64, rope_base=10000.0):
+    """Raw window rows [n, 128] bf16 bits of positions pos0.. -> the FP8
+    window cache (codes [n, 128] e4m3 of the rotated rows, scale [n] f32)."""
+    w = _c(win_bits, np.uint16)
+    n = w.size // 128
+    codes = np.empty(w.shape[:-1] + (128,), np.uint8)
+    sc = np.empty(w.shape[:-1], np.float32)
+    lib().orc_store_window_fp8_n(_p(w), n, int(pos0), rope_dims, float(rope_base), _p(codes), _p(sc))
+    return codes, sc
+
+
+def load_window_fp8(codes, scale):
+    """FP8 window cache -> fp64 rows [n, 128] (code x scale, exact)."""
+    codes = _c(codes, np.uint8)
+    scale = _c(scale, np.float32)
+    n = codes.size // 128
+    out = np.empty(codes.shape[:-1] + (128,), np.float64)
+    lib().orc_load_entries_fp8_n(_p(codes), None, _p(scale), n, 128, 0, _p(out))
     return out
 
 
@@ -245,11 +267,12 @@ def index_topk_rows(q_dec, w, k_dec, m, q_pos0, rows, k, relu=True):
 # ---- attention --------------------------------------------------------------
 
 def attend_rows(q, q_pos0, entries_f64, m, rows, mode, idx=None, win=None, win_pos0=0,
-                n_win=128, sink=None, rope_dims=64, rope_base=10000.0):
+                n_win=128, sink=None, rope_dims=64, rope_base=10000.0, win_post=None):
     """q [n, H, D] bf16 bits; entries_f64 [N, D] decoded post-RoPE entries;
     mode 'csa' (keys = idx rows) or 'hca' (keys = all visible entries);
-    win [win_len, D] bf16 bits pre-RoPE starting at win_pos0.  Returns
-    out [len(rows), H, D] fp64."""
+    win [win_len, D] bf16 bits pre-RoPE starting at win_pos0, or win_post
+    [win_len, D] fp64 rows already rotated (a decoded FP8 window cache).
+    Returns out [len(rows), H, D] fp64."""
     q = _c(q, np.uint16)
     n, H, D = q.shape
     ent = _c(entries_f64, np.float64)
@@ -262,13 +285,15 @@ def attend_rows(q, q_pos0, entries_f64, m, rows, mode, idx=None, win=None, win_p
     if mode == "csa":
         assert idx is not None and idx.shape[0] == rows.size
     win = _c(win, np.uint16)
-    win_len = 0 if win is None else win.shape[0]
-    if win is None:
+    win_post = _c(win_post, np.float64)
+    src = win if win_post is None else win_post
+    win_len = 0 if src is None else src.shape[0]
+    if src is None:
         n_win = 0
     sink = _c(sink, np.float32)
     out = np.empty((rows.size, H, D), np.float64)
     r = lib().orc_attend_rows(_p(q), H, D, int(q_pos0), _p(ent), N, m, _p(idx), k,
-                              0 if mode == "csa" else 1, _p(win), int(win_pos0), win_len,
+                              0 if mode == "csa" else 1, _p(win), _p(win_post), int(win_pos0), win_len,
                               int(n_win), _p(sink), rope_dims, float(rope_base), _p(rows),
                               rows.size, _p(out))
     if r != 0:

@@ -350,6 +350,24 @@ void orc_load_entries_nvfp4_n(const uint8_t* recs, const float* scale, int64_t n
     }
 }
 
+/* The FP8 sliding-window cache of the V4.1 variant (the Russian summary:
+ * the SWA KV cache is held in FP8): each raw window row of position j is
+ * rotated at j (fp64, as the entries are), rounded to fp32, and stored as
+ * e4m3 codes of all 128 dims with the scale amax / 448 (the FP8 entry rule
+ * without bf16 RoPE dims). */
+void orc_store_window_fp8_n(const uint16_t* win, int64_t n, int64_t pos0, int rope_dims,
+                            double rope_base, uint8_t* codes, float* scale)
+{
+    double v[128];
+    float r[128];
+    for (int64_t i = 0; i < n; ++i) {
+        for (int d = 0; d < 128; ++d) v[d] = orc_bf16_to_f32(win[i * 128 + d]);
+        if (rope_dims > 0) orc_rope(v, 128, rope_dims, rope_base, (double)(pos0 + i));
+        for (int d = 0; d < 128; ++d) r[d] = (float)v[d];
+        orc_store_entry_fp8(r, 128, 0, codes + i * 128, NULL, scale + i);
+    }
+}
+
 /* ========================================================================== */
 /* Lightning indexer and top-k                                                */
 /* ========================================================================== */
@@ -488,7 +506,7 @@ void orc_attend_row(const uint16_t* q, int64_t t, int H, int D,
 int orc_attend_rows(const uint16_t* q, int H, int D, int64_t q_pos0,
                     const double* entries, int N, int m,
                     const int32_t* idx, int k, int mode,
-                    const uint16_t* win, int64_t win_pos0, int win_len, int n_win,
+                    const uint16_t* win, const double* win_post, int64_t win_pos0, int win_len, int n_win,
                     const float* sink, int rope_dims, double rope_base,
                     const int32_t* rows, int nrows, double* out)
 {
@@ -522,8 +540,12 @@ int orc_attend_rows(const uint16_t* q, int H, int D, int64_t q_pos0,
                     int64_t row = j - win_pos0;
                     if (row < 0 || row >= win_len) { bad = 1; continue; }
                     double* kr = keys + (size_t)nk * D;
-                    for (int d = 0; d < D; ++d) kr[d] = orc_bf16_to_f32(win[(size_t)row * D + d]);
-                    if (rope_dims > 0) orc_rope(kr, D, rope_dims, rope_base, (double)j);
+                    if (win_post) {  /* stored after RoPE (decoded FP8 window cache) */
+                        memcpy(kr, win_post + (size_t)row * D, sizeof(double) * D);
+                    } else {
+                        for (int d = 0; d < D; ++d) kr[d] = orc_bf16_to_f32(win[(size_t)row * D + d]);
+                        if (rope_dims > 0) orc_rope(kr, D, rope_dims, rope_base, (double)j);
+                    }
                     ++nk;
                 }
             }

@@ -100,7 +100,7 @@ void orc_attend_row(const uint16_t* q, int64_t t, int H, int D,
 int orc_attend_rows(const uint16_t* q, int H, int D, int64_t q_pos0,
                     const double* entries, int N, int m,
                     const int32_t* idx, int k, int mode,
-                    const uint16_t* win, int64_t win_pos0, int win_len, int n_win,
+                    const uint16_t* win, const double* win_post, int64_t win_pos0, int win_len, int n_win,
                     const float* sink, int rope_dims, double rope_base,
                     const int32_t* rows, int nrows, double* out);
 
@@ -119,6 +119,8 @@ void orc_mxfp4_encode_rows(const float* x, int64_t rows, int n_per_row,
 void orc_mxfp4_decode_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                            int n_per_row, float* out);
 void orc_store_entry_nvfp4(const float* row, uint8_t* rec_out, float* scale_out);
+void orc_store_window_fp8_n(const uint16_t* win, int64_t n, int64_t pos0, int rope_dims,
+                            double rope_base, uint8_t* codes, float* scale);
 void orc_store_entries_nvfp4_n(const float* rows, int64_t n, uint8_t* recs, float* scale);
 void orc_load_entries_nvfp4_n(const uint8_t* recs, const float* scale, int64_t n, double* out);
 

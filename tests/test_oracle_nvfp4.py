@@ -4,7 +4,9 @@ NVFP4, quantised after RoPE).  NVFP4 is e2m1 elements in blocks of 16 with
 an e4m3 block scale and an fp32 second-level scale (here per entry,
 amax / (6 * 448)).  Pinned against values built exactly on the grids, the
 rounding rule checked by brute force over the 8 e2m1 magnitudes, hand
-worked ties and saturation, power-of-two scaling and sign symmetry."""
+worked ties and saturation, power-of-two scaling and sign symmetry.  Also
+the FP8 sliding-window cache of the same variant (rows rotated at their
+position, then e4m3 over all 128 dims with scale amax / 448)."""
 import numpy as np
 import pytest
 
@@ -137,3 +139,52 @@ def test_error_bound(seed):
     ok = (q <= 6) & (sb > 0)
     err = np.abs(x - xh)
     assert np.all(err[ok] <= spacing[ok] / 2 * sb[ok] * (1 + 1e-6))
+
+
+# ---- the FP8 sliding-window cache of the V4.1 variant ----------------------
+
+def _raw_rows(rng, n, scale=0.5):
+    return oracle.bf16_from_f32((rng.standard_normal((n, 128)) * scale).astype(np.float32))
+
+
+def test_window_fp8_at_position_zero_is_plain_fp8():
+    """RoPE at position 0 is the identity, so row 0 is the FP8 entry rule
+    over all 128 dims (scale amax / 448)."""
+    rng = np.random.default_rng(10)
+    w = _raw_rows(rng, 3)
+    codes, sc = oracle.store_window_fp8(w, 0)
+    c0, _, s0 = oracle.store_entries_fp8(oracle.bf16_to_f64(w[:1]).astype(np.float32), rope_dims=0)
+    assert np.array_equal(codes[0], c0[0]) and sc[0] == s0[0]
+    assert sc[0] == np.float32(np.abs(oracle.bf16_to_f64(w[0])).max()) / np.float32(448.0)
+
+
+def test_window_fp8_is_the_rotated_row_within_fp8_error():
+    rng = np.random.default_rng(11)
+    pos0 = 1_000_000
+    w = _raw_rows(rng, 64)
+    codes, sc = oracle.store_window_fp8(w, pos0)
+    dec = oracle.load_window_fp8(codes, sc)
+    for i in range(64):
+        rot = oracle.bf16_to_f64(w[i]).copy()
+        rot = oracle.rope(rot, pos0 + i)
+        assert np.all(np.abs(dec[i] - rot) <= 2.0 ** -4 * np.abs(rot) + float(sc[i]) * 2.0 ** -9)
+        # the rotation keeps each (2f, 2f+1) pair's length: dims 0..63 are not rotated
+        assert np.allclose(np.hypot(rot[64::2], rot[65::2]),
+                           np.hypot(*oracle.bf16_to_f64(w[i])[64:].reshape(32, 2).T), rtol=1e-12)
+
+
+def test_attention_over_a_rotated_window_equals_the_raw_window():
+    """The post-RoPE window input (used for the FP8 cache) and the raw one
+    give the same attention when the post-RoPE rows are the exact rotations."""
+    rng = np.random.default_rng(12)
+    H, n, pos0 = 8, 6, 300
+    q = oracle.bf16_from_f32((rng.standard_normal((n, H, 128)) * 0.3).astype(np.float32))
+    win = _raw_rows(rng, pos0 + n, 0.3)
+    post = np.stack([oracle.rope(oracle.bf16_to_f64(win[j]).copy(), j) for j in range(pos0 + n)])
+    ent = rng.standard_normal((75, 128))
+    rows = np.arange(n, dtype=np.int32)
+    idx = np.sort(rng.choice(75, size=(n, 20)), axis=1).astype(np.int32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    a = oracle.attend_rows(q, pos0, ent, 4, rows, "csa", idx=idx, win=win, sink=sink)
+    b = oracle.attend_rows(q, pos0, ent, 4, rows, "csa", idx=idx, win_post=post, sink=sink)
+    assert np.array_equal(a, b)
