@@ -64,6 +64,8 @@ extern "C" {
 #define CSA_FMT_FP8_ROPE_BF16 2 /* entries: e4m3 [.., 64] + bf16 [.., 64] + f32 scale [..] */
 #define CSA_FMT_NVFP4 3         /* entries: records [.., 72] u8 (64 B e2m1 codes of the 128
                                    post-RoPE dims + 8 e4m3 scales of 16-dim blocks) + f32 scale [..] */
+#define CSA_FMT_FP8 4           /* window cache: e4m3 [.., 128] of post-RoPE rows + f32 scale [..]
+                                   (amax / 448 over the 128 dims) */
 
 /*
  * csa_compress -- token-level compressor (CSA: m = 4 with overlap; HCA:
@@ -140,6 +142,13 @@ int csa_compress(const void* kv, const void* ik, const float* z, const float* be
  *            max(0, t-W+1) - s0.
  *  ik_ring   [B, W, 64] bf16 (slot j % W), with ik_new, else NULL
  *  z_ring    [B, W, 2] fp32 (slot j % W), with z_new, else NULL
+ *  win8_ring [B, 2W, 128] e4m3, or NULL: the FP8 sliding-window cache of
+ *            the V4.1 variant (the Russian summary: SWA cache in FP8).  Row
+ *            t, rotated at t (fp64, as the entries), rounded to fp32 and
+ *            coded over all 128 dims with scale amax / 448, goes to slots
+ *            t % W and t % W + W like kv_ring, so csa_attend can read it as
+ *            an FP8 window (win_fmt = CSA_FMT_FP8) in the same way
+ *  win8_scale [B, 2W] fp32, with win8_ring
  *  W         ring length in rows, >= L (2m with overlap, else m); 128 holds
  *            the sliding window
  *  beta, m, overlap, rope_dims, rope_base: as csa_compress
@@ -153,7 +162,8 @@ int csa_compress(const void* kv, const void* ik, const float* z, const float* be
  * an entry index >= N_cap.
  */
 int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new, int B, int64_t t,
-                     void* kv_ring, void* ik_ring, float* z_ring, int W, const float* beta, int m,
+                     void* kv_ring, void* ik_ring, float* z_ring, void* win8_ring, float* win8_scale,
+                     int W, const float* beta, int m,
                      int overlap, int rope_dims, float rope_base, void* entries, void* entries_rope,
                      float* entry_scale, int entry_fmt, void* kidx, uint8_t* kidx_scale, int kidx_fmt,
                      int N_cap, void* stream);
@@ -222,16 +232,23 @@ int csa_index_topk_fallbacks(uint64_t* count, int reset);
  *
  *  q            [B, n, H, 128] bf16 pre-RoPE; 1 <= H <= 64
  *  entries      BF16: [B, N, 128] bf16 post-RoPE.  FP8_ROPE_BF16:
- *               [B, N, 64] e4m3 codes (value = code * entry_scale)
+ *               [B, N, 64] e4m3 codes (value = code * entry_scale).
+ *               NVFP4: [B, N, 72] records as csa_compress writes them
  *  entries_rope FP8_ROPE_BF16: [B, N, 64] bf16 (dims 64..127); else NULL
- *  entry_scale  FP8_ROPE_BF16: [B, N] fp32; else NULL
+ *  entry_scale  FP8_ROPE_BF16 and NVFP4: [B, N] fp32; else NULL
  *  idx          [B, n, k] int32 entry indices (-1 = unused slot), 16-byte
  *               aligned, k <= 2048; every index must be < N (not checked on
  *               the device)
- *  win_kv       [B, win_len, 128] bf16 pre-RoPE raw rows at positions
- *               win_pos0 .. win_pos0+win_len-1; must cover
- *               [max(0, q_pos0-n_win+1), q_pos0+n-1] when n_win > 0
+ *  win_kv       win_fmt BF16: [B, win_len, 128] bf16 pre-RoPE raw rows at
+ *               positions win_pos0 .. win_pos0+win_len-1; must cover
+ *               [max(0, q_pos0-n_win+1), q_pos0+n-1] when n_win > 0.
+ *               win_fmt FP8 (the V4.1 variant's FP8 sliding-window cache,
+ *               FP8 or NVFP4 entries only): [B, win_len, 128] e4m3 codes of
+ *               the rows rotated at their positions, value = code *
+ *               win_scale (csa_cache_append writes such a ring)
  *  n_win        0 (no window) .. 128
+ *  win_fmt      CSA_FMT_BF16 or CSA_FMT_FP8
+ *  win_scale    FP8 window: [B, win_len] fp32; else NULL
  *  sink         [H] fp32 or NULL (no sink)
  *  out          [B, n, H, 128] bf16
  *  ws, ws_bytes device scratch of at least csa_attend_workspace_bytes()
@@ -247,9 +264,9 @@ int csa_index_topk_fallbacks(uint64_t* count, int reset);
 int csa_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D,
                const void* entries, const void* entries_rope, const float* entry_scale,
                int entry_fmt, int N, int m, const int32_t* idx, int k,
-               const void* win_kv, int64_t win_pos0, int win_len, int n_win,
-               const float* sink, int rope_dims, float rope_base, void* out, void* ws,
-               size_t ws_bytes, void* stream);
+               const void* win_kv, int64_t win_pos0, int win_len, int n_win, int win_fmt,
+               const float* win_scale, const float* sink, int rope_dims, float rope_base,
+               void* out, void* ws, size_t ws_bytes, void* stream);
 
 size_t csa_attend_workspace_bytes(int B, int n, int k, int n_win, int entry_fmt);
 

@@ -14,12 +14,12 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (FMT_BF16, FMT_FP8_ROPE_BF16, FMT_MXFP4, FMT_NVFP4, CsaError, check, lib)
+from ._lib import (FMT_BF16, FMT_FP8, FMT_FP8_ROPE_BF16, FMT_MXFP4, FMT_NVFP4, CsaError, check, lib)
 
 __all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend",
            "csa_project_in", "csa_project_qidx", "csa_project_out", "version",
            "CsaError",
-           "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16", "FMT_NVFP4"]
+           "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16", "FMT_NVFP4", "FMT_FP8"]
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
 
@@ -87,17 +87,20 @@ def csa_compress(kv, beta, m, overlap, pos0=0, ik=None, z=None, prev_kv=None, pr
 
 def csa_cache_append(kv_new, beta, m, overlap, t, kv_ring, caches, ik_new=None, ik_ring=None,
                      z_new=None, z_ring=None, rope_dims=64, rope_base=10000.0, entry_fmt="bf16",
-                     kidx_fmt="mxfp4", stream=None):
+                     kidx_fmt="mxfp4", win8_ring=None, win8_scale=None, stream=None):
     """Decode write path: kv_new [B, 128] (ik_new [B, 64], z_new [B, 2]) of
     position t into the rings kv_ring [B, 2W, 128] (ik_ring [B, W, 64],
     z_ring [B, W, 2]); the block it completes, if any, into ``caches``
-    (entries [B, N_cap, ...], entries_rope, entry_scale, kidx, kidx_scale)."""
+    (entries [B, N_cap, ...], entries_rope, entry_scale, kidx, kidx_scale).
+    win8_ring [B, 2W, 128] u8 + win8_scale [B, 2W] f32: optional FP8 window
+    cache (rows rotated at their positions), slots as kv_ring."""
     B = kv_new.shape[0]
     W = kv_ring.shape[1] // 2
     ents = caches.get("entries")
     N_cap = 0 if ents is None else ents.shape[1]
     check(lib().csa_cache_append(
-        _ptr(kv_new), _ptr(ik_new), _ptr(z_new), B, int(t), _ptr(kv_ring), _ptr(ik_ring), _ptr(z_ring), W,
+        _ptr(kv_new), _ptr(ik_new), _ptr(z_new), B, int(t), _ptr(kv_ring), _ptr(ik_ring), _ptr(z_ring),
+        _ptr(win8_ring), _ptr(win8_scale), W,
         _ptr(beta), m, int(overlap), rope_dims, float(rope_base), _ptr(ents), _ptr(caches.get("entries_rope")),
         _ptr(caches.get("entry_scale")), _fmt(entry_fmt), _ptr(caches.get("kidx")), _ptr(caches.get("kidx_scale")),
         _fmt(kidx_fmt), N_cap, _stream(stream)))
@@ -135,10 +138,11 @@ def csa_index_topk_fallbacks(reset=False):
 
 def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=128, sink=None,
                entries_rope=None, entry_scale=None, rope_dims=64, rope_base=10000.0, N=None,
-               out=None, ws=None, stream=None):
+               out=None, ws=None, win_scale=None, stream=None):
     """q [B, n, H, 128] bf16; entries [B, N, 128] bf16 (or e4m3 [B, N, 64] with
     entries_rope/entry_scale, or NVFP4 records [B, N, 72] u8 with entry_scale
-    only); idx [B, n, k] int32; win_kv [B, W, 128] bf16.
+    only); idx [B, n, k] int32; win_kv [B, W, 128] bf16 raw rows, or with
+    win_scale an FP8 window cache (e4m3 [B, W, 128] of rotated rows).
     ``ws``: workspace of csa_attend_workspace_bytes() bytes (allocated here
     when needed and not given)."""
     B, n, H, D = q.shape
@@ -159,7 +163,8 @@ def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=12
         ws = torch.empty((need,), dtype=torch.uint8, device=q.device)
     check(lib().csa_attend(
         _ptr(q), B, n, int(q_pos0), H, D, _ptr(entries), _ptr(entries_rope), _ptr(entry_scale), ef,
-        N, m, _ptr(idx), idx.shape[2], _ptr(win_kv), int(win_pos0), win_len, nw, _ptr(sink), rope_dims,
+        N, m, _ptr(idx), idx.shape[2], _ptr(win_kv), int(win_pos0), win_len, nw,
+        FMT_BF16 if win_scale is None else FMT_FP8, _ptr(win_scale), _ptr(sink), rope_dims,
         float(rope_base), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
     return out

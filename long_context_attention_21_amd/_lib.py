@@ -20,6 +20,7 @@ FMT_BF16 = 0
 FMT_MXFP4 = 1
 FMT_FP8_ROPE_BF16 = 2
 FMT_NVFP4 = 3
+FMT_FP8 = 4
 
 EXPORTS = ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_workspace_bytes",
            "csa_index_topk_fallbacks", "csa_attend", "csa_attend_workspace_bytes", "hca_attend", "csa_project_in",
@@ -46,15 +47,15 @@ def lib():
     P, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
     L.csa_compress.argtypes = [P, P, P, P, P, P, P, i32, i32, i64, i32, i32, i32, i32, i32, f32,
                                P, P, P, i32, P, P, i32, P]
-    L.csa_cache_append.argtypes = [P, P, P, i32, i64, P, P, P, i32, P, i32, i32, i32, f32, P, P, P, i32, P, P,
-                                   i32, i32, P]
+    L.csa_cache_append.argtypes = [P, P, P, i32, i64, P, P, P, P, P, i32, P, i32, i32, i32, f32, P, P, P, i32,
+                                   P, P, i32, i32, P]
     L.csa_index_topk.argtypes = [P, P, P, P, P, i32, i32, i32, i64, i32, i32, i32, i32, i32, P, P,
                                  sz, P]
     L.csa_index_topk_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.csa_index_topk_workspace_bytes.restype = sz
     L.csa_index_topk_fallbacks.argtypes = [P, i32]
     L.csa_attend.argtypes = [P, i32, i32, i64, i32, i32, P, P, P, i32, i32, i32, P, i32, P, i64, i32,
-                             i32, P, i32, f32, P, P, sz, P]
+                             i32, i32, P, P, i32, f32, P, P, sz, P]
     L.csa_attend_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.csa_attend_workspace_bytes.restype = sz
     L.hca_attend.argtypes = [P, i32, i32, i64, i32, i32, P, i32, i32, P, i64, i32, i32, P, i32, f32,

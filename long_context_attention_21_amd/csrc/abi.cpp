@@ -128,7 +128,8 @@ int csa_compress(const void* kv, const void* ik, const float* z, const float* be
 }
 
 int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new, int B, int64_t t,
-                     void* kv_ring, void* ik_ring, float* z_ring, int W, const float* beta, int m,
+                     void* kv_ring, void* ik_ring, float* z_ring, void* win8_ring, float* win8_scale,
+                     int W, const float* beta, int m,
                      int overlap, int rope_dims, float rope_base, void* entries, void* entries_rope,
                      float* entry_scale, int entry_fmt, void* kidx, uint8_t* kidx_scale, int kidx_fmt,
                      int N_cap, void* stream) {
@@ -147,6 +148,7 @@ int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new,
   REQUIRE(kv_new && kv_ring && beta, "csa_cache_append: kv_new, kv_ring and beta must be non-NULL");
   REQUIRE((ik_new == nullptr) == (ik_ring == nullptr), "csa_cache_append: ik_new and ik_ring go together");
   REQUIRE((z_new == nullptr) == (z_ring == nullptr), "csa_cache_append: z_new and z_ring go together");
+  REQUIRE((win8_ring == nullptr) == (win8_scale == nullptr), "csa_cache_append: win8_ring and win8_scale go together");
   const bool complete = (t + 1) % m == 0;
   if (complete) {
     const int64_t i = (t + 1) / m - 1;
@@ -167,7 +169,8 @@ int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new,
   }
   REQUIRE(((uintptr_t)kv_new & 3u) == 0 && ((uintptr_t)ik_new & 3u) == 0 && ((uintptr_t)kv_ring & 3u) == 0 &&
               ((uintptr_t)ik_ring & 3u) == 0 && ((uintptr_t)entries & 3u) == 0 &&
-              ((uintptr_t)entries_rope & 3u) == 0 && ((uintptr_t)kidx & 3u) == 0,
+              ((uintptr_t)entries_rope & 3u) == 0 && ((uintptr_t)kidx & 3u) == 0 &&
+              ((uintptr_t)win8_ring & 3u) == 0,
           "csa_cache_append: tensor pointers must be 4-byte aligned");
 
   csa::CompressParams p{};
@@ -178,6 +181,8 @@ int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new,
   p.kv_ring = (uint32_t*)kv_ring;
   p.ik_ring = (uint32_t*)ik_ring;
   p.z_ring = z_ring;
+  p.win8_ring = (uint8_t*)win8_ring;
+  p.win8_scale = win8_scale;
   p.W = W;
   p.N_cap = N_cap;
   p.t = t;
@@ -255,7 +260,8 @@ int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* wid
 static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, int H, int D,
                          const void* entries, const void* entries_rope, const float* entry_scale,
                          int N, int m, const int32_t* idx, int k, const void* win_kv,
-                         int64_t win_pos0, int win_len, int n_win, const float* sink,
+                         int64_t win_pos0, int win_len, int n_win, int win_fmt, const float* win_scale,
+                         const float* sink,
                          int rope_dims, float rope_base, void* out, void* ws, size_t ws_bytes,
                          void* stream, const char* name) {
   REQUIRE(B >= 0 && n >= 0 && N >= 0 && k >= 0, "%s: B, n, N and k must be >= 0", name);
@@ -267,6 +273,9 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   REQUIRE(rope_dims == 0 || (std::isfinite(rope_base) && rope_base > 1.0f),
           "%s: rope_base must be finite and > 1", name);
   REQUIRE(n_win >= 0, "%s: n_win=%d must be >= 0", name, n_win);
+  REQUIRE(win_fmt == CSA_FMT_BF16 || win_fmt == CSA_FMT_FP8, "%s: win_fmt=%d unsupported", name, win_fmt);
+  REQUIRE(win_fmt == CSA_FMT_BF16 || mode == 1 || mode == 3,
+          "%s: an FP8 window needs FP8 or NVFP4 entries (the decode cache layout)", name);
   // row sources are addressed with 32-bit byte offsets inside the kernel
   REQUIRE((int64_t)N * 256 < 0x7fff0000LL && (int64_t)win_len * 256 < 0x7fff0000LL,
           "%s: N=%d or win_len=%d too large (at most 8388351 rows)", name, N, win_len);
@@ -282,6 +291,7 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   if (mode == 3) REQUIRE(N == 0 || entry_scale, "%s: NVFP4 entries need entry_scale", name);
   if (n_win > 0) {
     REQUIRE(win_kv != nullptr, "%s: win_kv is NULL but n_win > 0", name);
+    REQUIRE(win_fmt == CSA_FMT_BF16 || win_scale != nullptr, "%s: an FP8 window needs win_scale", name);
     int64_t lo = q_pos0 - n_win + 1;
     if (lo < 0) lo = 0;
     const int64_t hi = q_pos0 + n - 1;
@@ -310,6 +320,8 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   p.idx = idx;
   p.k = (mode == 2) ? 0 : k;
   p.win = (const uint16_t*)win_kv;
+  p.win_fp8 = win_fmt == CSA_FMT_FP8 ? 1 : 0;
+  p.win_scale = win_scale;
   p.win_pos0 = win_pos0;
   p.win_len = win_len;
   p.n_win = n_win;
@@ -325,14 +337,14 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
 int csa_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const void* entries,
                const void* entries_rope, const float* entry_scale, int entry_fmt, int N, int m,
                const int32_t* idx, int k, const void* win_kv, int64_t win_pos0, int win_len,
-               int n_win, const float* sink, int rope_dims, float rope_base, void* out, void* ws,
-               size_t ws_bytes, void* stream) {
+               int n_win, int win_fmt, const float* win_scale, const float* sink, int rope_dims,
+               float rope_base, void* out, void* ws, size_t ws_bytes, void* stream) {
   REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16 || entry_fmt == CSA_FMT_NVFP4,
           "csa_attend: entry_fmt=%d unsupported", entry_fmt);
   const int mode = entry_fmt == CSA_FMT_BF16 ? 0 : entry_fmt == CSA_FMT_FP8_ROPE_BF16 ? 1 : 3;
   return attend_common(mode, q, B, n, q_pos0, H, D, entries,
                        entries_rope, entry_scale, N, m, idx, k, win_kv, win_pos0, win_len, n_win,
-                       sink, rope_dims, rope_base, out, ws, ws_bytes, stream, "csa_attend");
+                       win_fmt, win_scale, sink, rope_dims, rope_base, out, ws, ws_bytes, stream, "csa_attend");
 }
 
 size_t csa_attend_workspace_bytes(int B, int n, int k, int n_win, int entry_fmt) {
@@ -345,8 +357,8 @@ int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const 
                int N, int m, const void* win_kv, int64_t win_pos0, int win_len, int n_win,
                const float* sink, int rope_dims, float rope_base, void* out, void* stream) {
   return attend_common(2, q, B, n, q_pos0, H, D, entries, nullptr, nullptr, N, m, nullptr, 0,
-                       win_kv, win_pos0, win_len, n_win, sink, rope_dims, rope_base, out, nullptr, 0,
-                       stream, "hca_attend");
+                       win_kv, win_pos0, win_len, n_win, CSA_FMT_BF16, nullptr, sink, rope_dims, rope_base,
+                       out, nullptr, 0, stream, "hca_attend");
 }
 
 // ---------------------------------------------------------------- projections

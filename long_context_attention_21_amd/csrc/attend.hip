@@ -183,9 +183,14 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   };
   constexpr int kOOB = 0x7fff0000;  // past every row source (the host bounds them below this)
   const int bu = __builtin_amdgcn_readfirstlane(b);
+  const int wrow = p.win_fp8 ? 128 : 256;  // bytes per window row
   __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(p.win ? p.win + (int64_t)bu * p.win_len * 128 : p.q), (short)0,
-      p.win ? __builtin_amdgcn_readfirstlane(p.win_len * 256) : 0, 0x00020000);
+      uniform_ptr(p.win ? (const uint8_t*)p.win + (int64_t)bu * p.win_len * wrow : (const uint8_t*)p.q), (short)0,
+      p.win ? __builtin_amdgcn_readfirstlane(p.win_len * wrow) : 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t rWS = rW;
+  if (p.win_fp8)
+    rWS = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p.win_scale + (int64_t)bu * p.win_len), (short)0,
+                                            __builtin_amdgcn_readfirstlane(p.win_len * 4), 0x00020000);
   __amdgpu_buffer_rsrc_t rE, rR = rW, rS = rW;
   if (MODE == 3) {
     rE = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t*)p.entries + (int64_t)bu * p.N * 72),
@@ -243,6 +248,15 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
 #pragma unroll
         for (int ks = 2; ks < 4; ++ks) R.r[kt][ks] = __builtin_amdgcn_raw_buffer_load_b128(rR, orr + (ks - 2) * 64, 0, 0);
         R.sc[kt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, row >= 0 ? row * 4 : kOOB, 0, 0));
+      } else if (!ent && p.win_fp8) {
+        // FP8 window row (post-RoPE): 8 code bytes of the lane's dims per slice
+        const int off = row >= 0 ? row * 128 + 8 * g : kOOB;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const auto cw = __builtin_amdgcn_raw_buffer_load_b64(rW, off + ks * 32, 0, 0);
+          R.r[kt][ks] = u32x4{cw[0], cw[1], 0u, 0u};
+        }
+        R.sc[kt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rWS, row >= 0 ? row * 4 : kOOB, 0, 0));
       } else {
         const int off = row >= 0 ? row * 256 + 16 * g : kOOB;
 #pragma unroll
@@ -297,7 +311,24 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
           R.r[kt][ks][3] = pack_bf16(v3[0] * sc, v3[1] * sc);
         }
     }
-    if (c >= n_ent_chunks && p.rope) {
+    if (c >= n_ent_chunks && p.win_fp8) {
+      // FP8 window rows: all four slices, already rotated
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const uint32_t w0 = R.r[kt][ks][0], w1 = R.r[kt][ks][1];
+          const float sc = R.sc[kt];
+          const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, false);
+          const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, 1.0f, true);
+          const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, false);
+          const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, 1.0f, true);
+          R.r[kt][ks][0] = pack_bf16(v0[0] * sc, v0[1] * sc);
+          R.r[kt][ks][1] = pack_bf16(v1[0] * sc, v1[1] * sc);
+          R.r[kt][ks][2] = pack_bf16(v2[0] * sc, v2[1] * sc);
+          R.r[kt][ks][3] = pack_bf16(v3[0] * sc, v3[1] * sc);
+        }
+    } else if (c >= n_ent_chunks && p.rope) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         if (!R.v[kt]) continue;

@@ -52,6 +52,34 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
       p.kv_ring[((int64_t)b * 2 * p.W + s + p.W) * 64 + lane] = x;
       if (p.ik_new && lane < 32) p.ik_ring[((int64_t)b * p.W + s) * 32 + lane] = p.ik_new[(int64_t)b * 32 + lane];
       if (p.z_new && lane < 2) p.z_ring[((int64_t)b * p.W + s) * 2 + lane] = p.z_new[(int64_t)b * 2 + lane];
+      if (p.win8_ring) {
+        // FP8 window cache: the row rotated at t (fp64, as the entries), then
+        // e4m3 over all 128 dims with scale amax / 448
+        float v0 = bf16lo(x), v1 = bf16hi(x);
+        if (p.rope_dims == 64 && lane >= 32) {
+          const double phi = (double)p.t * p.theta[lane - 32];
+          const double c = cos(phi), sn = sin(phi);
+          const double x0 = v0, x1 = v1;
+          v0 = (float)(x0 * c - x1 * sn);
+          v1 = (float)(x0 * sn + x1 * c);
+        }
+        float amax = fmaxf(fabsf(v0), fabsf(v1));
+        for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        const float scale = __fdiv_rn(amax, 448.0f);
+        uint32_t c0 = 0, c1 = 0;
+        if (scale != 0.0f) {
+          c0 = f32_to_e4m3(__fdiv_rn(v0, scale));
+          c1 = f32_to_e4m3(__fdiv_rn(v1, scale));
+        }
+        const uint16_t cc = (uint16_t)(c0 | (c1 << 8));
+        uint16_t* w8 = (uint16_t*)p.win8_ring;
+        w8[((int64_t)b * 2 * p.W + s) * 64 + lane] = cc;
+        w8[((int64_t)b * 2 * p.W + s + p.W) * 64 + lane] = cc;
+        if (lane == 0) {
+          p.win8_scale[(int64_t)b * 2 * p.W + s] = scale;
+          p.win8_scale[(int64_t)b * 2 * p.W + s + p.W] = scale;
+        }
+      }
     }
     // t is the same for every wave: a call that completes no block ends here
     // on the whole work-group, before any barrier

@@ -36,6 +36,8 @@ struct CompressParams {
   uint32_t* kv_ring;       // [B, 2W, 128] bf16
   uint32_t* ik_ring;       // [B, W, 64] bf16 or null
   float* z_ring;           // [B, W, 2] or null
+  uint8_t* win8_ring;      // [B, 2W, 128] e4m3 post-RoPE window cache or null (slots as kv_ring)
+  float* win8_scale;       // [B, 2W] with win8_ring
   int W, N_cap;
   int64_t t;
   __device__ uint8_t* kidx_out_u8() const { return (uint8_t*)kidx_out; }
@@ -53,7 +55,9 @@ struct AttendParams {
   int N, m;
   const int32_t* idx;  // CSA: [B, n, k]
   int k;
-  const uint16_t* win;  // [B, win_len, 128]
+  const uint16_t* win;  // [B, win_len, 128] bf16 pre-RoPE, or e4m3 post-RoPE when win_fp8
+  const float* win_scale;  // win_fp8: [B, win_len]
+  int win_fp8;
   int64_t win_pos0;
   int win_len, n_win;
   const float* sink;  // [H] or null
@@ -73,7 +77,8 @@ constexpr int kAttendPartFloats = 64 * 128 + 2 * 64;
 constexpr int kAttendChunksPerPart = 8;
 size_t attend_workspace(int mode, int B, int n, int k, int n_win);
 
-// mode: 0 = CSA with bf16 entries, 1 = CSA with fp8+bf16 entries, 2 = HCA
+// mode: 0 = CSA with bf16 entries, 1 = CSA with fp8+bf16 entries, 2 = HCA,
+// 3 = CSA with NVFP4 entries
 hipError_t launch_attend(const AttendParams& p, int mode, hipStream_t stream);
 
 struct IndexParams {

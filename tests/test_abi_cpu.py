@@ -138,8 +138,8 @@ def test_index_rejects_small_or_misaligned_workspace(L):
 def _attend(L, **kw):
     a = dict(q=FAKE, B=1, n=8, q_pos0=200, H=64, D=128, entries=FAKE, entries_rope=None,
              entry_scale=None, entry_fmt=0, N=50, m=4, idx=FAKE, k=16, win_kv=FAKE,
-             win_pos0=73, win_len=200, n_win=128, sink=None, rope_dims=64, rope_base=10000.0,
-             out=FAKE2, ws=None, ws_bytes=0, stream=None)
+             win_pos0=73, win_len=200, n_win=128, win_fmt=0, win_scale=None, sink=None, rope_dims=64,
+             rope_base=10000.0, out=FAKE2, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.csa_attend(*a.values())
 
@@ -161,6 +161,9 @@ def _attend(L, **kw):
     (dict(win_len=134), "does not cover"),       # needs up to 207
     (dict(q=MIS), "aligned"),
     (dict(q_pos0=-5), "q_pos0"),
+    (dict(win_fmt=3), "win_fmt=3"),
+    (dict(win_fmt=4, win_scale=FAKE), "FP8 or NVFP4 entries"),
+    (dict(win_fmt=4, entry_fmt=2, entries_rope=FAKE, entry_scale=FAKE), "win_scale"),
 ])
 def test_attend_rejects(L, kw, needle):
     assert _attend(L, **kw) == _lib.CSA_INVALID_ARG
@@ -199,7 +202,7 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
 
 def _append(L, **kw):
     a = dict(kv_new=FAKE, ik_new=None, z_new=None, B=2, t=3, kv_ring=FAKE2, ik_ring=None, z_ring=None,
-             W=128, beta=FAKE, m=4, overlap=1, rope_dims=64, rope_base=10000.0, entries=FAKE,
+             win8_ring=None, win8_scale=None, W=128, beta=FAKE, m=4, overlap=1, rope_dims=64, rope_base=10000.0, entries=FAKE,
              entries_rope=None, entry_scale=None, entry_fmt=0, kidx=None, kidx_scale=None, kidx_fmt=1,
              N_cap=8, stream=None)
     a.update(kw)
@@ -215,6 +218,7 @@ def _append(L, **kw):
     (dict(t=-1), "t must be"),
     (dict(entry_fmt=1), "entry_fmt=1"),
     (dict(kv_ring=MIS + 2), "aligned"),
+    (dict(win8_ring=FAKE), "win8_ring and win8_scale"),
 ])
 def test_cache_append_rejects(L, kw, needle):
     assert _append(L, **kw) == _lib.CSA_INVALID_ARG

@@ -43,9 +43,9 @@ def _empty_caches(B, N_cap, efmt, kfmt, with_ik):
     return c
 
 
-def _append_all(kv, ik, z, beta, m, overlap, efmt, kfmt, N_cap):
+def _append_all(kv, ik, z, beta, m, overlap, efmt, kfmt, N_cap, win8=None):
     """Append every token of kv [B, T, 128] (ik, z) in order; returns the
-    rings and caches."""
+    rings and caches.  win8: optional (ring, scale) FP8 window cache."""
     B, T, _ = kv.shape
     kv_d, beta_d = dev(kv), dev(beta)
     ik_d = dev(ik) if ik is not None else None
@@ -58,7 +58,8 @@ def _append_all(kv, ik, z, beta, m, overlap, efmt, kfmt, N_cap):
         L.csa_cache_append(kv_d[:, t].contiguous(), beta_d, m, overlap, t, ring, caches,
                            ik_new=None if ik_d is None else ik_d[:, t].contiguous(), ik_ring=ik_ring,
                            z_new=None if z_d is None else z_d[:, t].contiguous(), z_ring=z_ring,
-                           entry_fmt=efmt, kidx_fmt=kfmt)
+                           entry_fmt=efmt, kidx_fmt=kfmt, win8_ring=None if win8 is None else win8[0],
+                           win8_scale=None if win8 is None else win8[1])
     torch.cuda.synchronize()
     return ring, ik_ring, z_ring, caches
 
@@ -142,3 +143,45 @@ def test_decode_step_reads_window_from_ring(orc):
         ref = orc.attend_rows(q[b], t, ref_ent["entries_f64"], m, np.zeros(1, np.int32), "hca", win=kv[b],
                               win_pos0=0, sink=sink)
         assert_close(host_bits(out)[b], ref, "hca decode through the ring (sequence %d)" % b)
+
+
+def test_v41_decode_nvfp4_entries_fp8_window(orc):
+    """The V4.1 cache layout: NVFP4 entries and the FP8 sliding-window cache
+    written token by token by csa_cache_append.  The FP8 ring rows equal the
+    oracle's FP8 window rows bit for bit; a CSA decode step over the caches
+    (window read from the FP8 ring) matches the oracle given the same bytes."""
+    rng = np.random.default_rng(41)
+    B, H, m, k = 2, 32, 4, 40
+    T = 2 * W + 45
+    kv = _bf16(rng, (B, T, 128), 1 / np.sqrt(128))
+    ik = _bf16(rng, (B, T, 64), 0.3)
+    beta = rng.standard_normal(2 * m).astype(np.float32)
+    q = _bf16(rng, (B, 1, H, 128), 1 / np.sqrt(128))
+    sink = rng.standard_normal(H).astype(np.float32)
+    print("v4.1 decode B=%d T=%d" % (B, T), flush=True)
+    ring8 = torch.zeros((B, 2 * W, 128), dtype=torch.uint8, device="cuda")
+    sc8 = torch.zeros((B, 2 * W), dtype=torch.float32, device="cuda")
+    N_cap = T // m + 1
+    ring, _, _, caches = _append_all(kv, ik, None, beta, m, 1, "nvfp4", "mxfp4", N_cap, win8=(ring8, sc8))
+    t = T - 1
+    j0, s0 = _window_start(t)
+    codes8, scale8 = host(ring8), host(sc8)
+    for b in range(B):
+        ref_c, ref_s = orc.store_window_fp8(kv[b, j0:t + 1], j0)
+        assert np.array_equal(codes8[b, s0:s0 + (t - j0 + 1)], ref_c)
+        assert np.array_equal(scale8[b, s0:s0 + (t - j0 + 1)], ref_s)
+    n_ent = (t + 1) // m
+    idx = np.full((B, 1, k), -1, np.int32)
+    for b in range(B):
+        idx[b, 0] = np.sort(rng.choice(n_ent, size=k, replace=False))
+    out = L.csa_attend(dev(q), caches["entries"], dev(idx), q_pos0=t, m=m, win_kv=ring8, win_pos0=j0 - s0,
+                       sink=dev(sink), entry_scale=caches["entry_scale"], win_scale=sc8)
+    torch.cuda.synchronize()
+    ents = host(caches["entries"])
+    escale = host(caches["entry_scale"])
+    for b in range(B):
+        ref_e = orc.load_entries_nvfp4(ents[b, :n_ent], escale[b, :n_ent])
+        post = orc.load_window_fp8(codes8[b], scale8[b])
+        ref = orc.attend_rows(q[b], t, ref_e, m, np.zeros(1, np.int32), "csa", idx=idx[b], win_post=post,
+                              win_pos0=j0 - s0, sink=sink)
+        assert_close(host_bits(out)[b], ref, "v4.1 decode (sequence %d)" % b)

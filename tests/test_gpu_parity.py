@@ -159,7 +159,7 @@ def test_index_topk_matches_oracle(orc, B, n, N, H_I, k, q_pos0, fmt, extra):
 # ----------------------------------------------------------------- attention --
 
 def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True, q_scale=1.0,
-                 efmt="bf16", kv_scale=None, sink_shift=0.0, check_rows=None):
+                 efmt="bf16", kv_scale=None, sink_shift=0.0, check_rows=None, wfmt="bf16"):
     rng = np.random.default_rng(seed)
     T = q_pos0 + n
     kv_scale = kv_scale or 1 / np.sqrt(128)
@@ -182,6 +182,10 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
                     idx[b, r, :c] = np.sort(rng.choice(nv, size=c, replace=False))
     e_dev = dev(np.stack([e["entries"] for e in ents]))
     win = dev(kv) if n_win > 0 else None
+    win8 = None
+    if wfmt == "fp8":  # the FP8 window cache of the whole sequence, from the oracle
+        win8 = [orc.store_window_fp8(kv[b], 0) for b in range(B)]
+        win = dev(np.stack([w[0] for w in win8]))
     if mode == "csa":
         kw = {}
         if efmt == "fp8":
@@ -189,6 +193,8 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
                       entry_scale=dev(np.stack([e["entry_scale"] for e in ents])))
         elif efmt == "nvfp4":
             kw = dict(entry_scale=dev(np.stack([e["entry_scale"] for e in ents])))
+        if win8 is not None:
+            kw["win_scale"] = dev(np.stack([w[1] for w in win8]))
         out = L.csa_attend(dev(q), e_dev, dev(idx), q_pos0=q_pos0, m=m, win_kv=win, win_pos0=0,
                            n_win=n_win, sink=dev(sk) if sink else None, **kw)
     else:
@@ -199,9 +205,12 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
     if check_rows is not None:
         rows = np.asarray(check_rows, np.int32)
     for b in range(B):
+        wkw = dict(win=kv[b] if n_win else None)
+        if win8 is not None:
+            wkw = dict(win_post=orc.load_window_fp8(*win8[b]))
         ref = orc.attend_rows(q[b], q_pos0, ents[b]["entries_f64"], m, rows, mode,
-                              idx=None if idx is None else idx[b][rows], win=kv[b] if n_win else None,
-                              win_pos0=0, n_win=n_win, sink=sk)
+                              idx=None if idx is None else idx[b][rows], win_pos0=0, n_win=n_win, sink=sk,
+                              **wkw)
         assert_close(got[b][rows], ref, "batch %d" % b)
     return got
 
@@ -231,6 +240,10 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
     dict(B=3, n=2, H=64, q_pos0=2200, m=4, mode="csa", k=512, efmt="nvfp4", kv_scale=1.0),
     dict(B=1, n=3, H=16, q_pos0=2200, m=4, mode="csa", k=500, efmt="nvfp4", kv_scale=1.0, sink_shift=-60.0,
          q_scale=24.0),
+    # the FP8 window cache (V4.1): with NVFP4 and FP8 entries, many rows and the split decode
+    dict(B=2, n=50, H=64, q_pos0=400, m=4, mode="csa", k=96, efmt="nvfp4", kv_scale=1.0, wfmt="fp8"),
+    dict(B=3, n=2, H=64, q_pos0=2200, m=4, mode="csa", k=512, efmt="nvfp4", kv_scale=1.0, wfmt="fp8"),
+    dict(B=2, n=1, H=40, q_pos0=2200, m=4, mode="csa", k=512, efmt="fp8", kv_scale=1.0, wfmt="fp8"),
 ])
 def test_attend_matches_oracle(orc, case):
     print("attend case %s" % case, flush=True)
