@@ -472,6 +472,9 @@ class DecodeLayer:
             encode_cache(L, e16, k16, efmt, outs)
             self.swa[b] = dev_bf16(swa)
         q, q_I, w_I, sink = c["tail"]()
+        self.win8 = self.win8_scale = None
+        if efmt == "nvfp4":
+            self.make_fp8_window(c)
         log("decode caches generated and stored in %.1f s" % (time.time() - t0))
         self.q, self.qI, self.w, self.sink = dev_bf16(q), dev_bf16(q_I), dev(w_I), dev(sink)
         self.idx = torch.empty((B, 1, self.k), dtype=torch.int32, device=cu)
@@ -479,13 +482,34 @@ class DecodeLayer:
         self.kernels = ["csa_index_topk", "csa_attend"]
         keys = B * (min(self.k, N) + c["n_win"])
         # bytes: the indexer scans every key (34 B); attention gathers k entries (196 B FP8 + bf16,
-        # 76 B NVFP4) + window (256 B)
-        eb = 76 if efmt == "nvfp4" else 196
+        # 76 B NVFP4) + window (256 B bf16, 132 B FP8)
+        eb, wb = (76, 132) if efmt == "nvfp4" else (196, 256)
         self.work = {
             "csa_index_topk": ("hbm", B * N * 34),
-            "csa_attend": ("hbm", B * (min(self.k, N) * eb + c["n_win"] * 256 + 2 * H * 256 + 4 * self.k)),
+            "csa_attend": ("hbm", B * (min(self.k, N) * eb + c["n_win"] * wb + 2 * H * 256 + 4 * self.k)),
         }
         self.keys = keys
+
+    def make_fp8_window(self, c):
+        """The V4.1 layout's FP8 sliding-window cache: the raw window rows
+        appended in order by csa_cache_append into its FP8 ring (an HCA-style
+        m = 128 block completes once, into a scratch cache freed after)."""
+        import torch
+        L, B, W = self.L, self.B, 128
+        cu = "cuda"
+        ring = torch.zeros((B, 2 * W, 128), dtype=torch.bfloat16, device=cu)
+        self.win8 = torch.zeros((B, 2 * W, 128), dtype=torch.uint8, device=cu)
+        self.win8_scale = torch.zeros((B, 2 * W), dtype=torch.float32, device=cu)
+        beta = torch.zeros(128, dtype=torch.float32, device=cu)
+        j0 = c["win_pos0"]
+        n_cap = (j0 + c["n_win"]) // 128 + 1
+        scratch = {"entries": torch.empty((B, n_cap, 128), dtype=torch.bfloat16, device=cu)}
+        for r in range(c["n_win"]):
+            L.csa_cache_append(self.swa[:, r].contiguous(), beta, 128, 0, j0 + r, ring, scratch,
+                               win8_ring=self.win8, win8_scale=self.win8_scale)
+        torch.cuda.synchronize()
+        del scratch
+        self.win8_pos0 = j0 - (j0 % W)  # ring row s holds position win8_pos0 + s for the window rows
 
     def step(self, ev=None):
         L, c = self.L, self.c
@@ -493,9 +517,14 @@ class DecodeLayer:
         L.csa_index_topk(self.qI, self.w, self.kc, self.k, 4, q_pos0=c["q_pos0"], fmt="mxfp4",
                          kidx_scale=self.ks, idx_out=self.idx)
         if ev: ev[1].record()
-        L.csa_attend(self.q, self.codes, self.idx, q_pos0=c["q_pos0"], m=4, win_kv=self.swa,
-                     win_pos0=c["win_pos0"], sink=self.sink, entries_rope=self.rope, entry_scale=self.scale,
-                     out=self.out)  # entries_rope None: NVFP4 records
+        if self.win8 is None:
+            L.csa_attend(self.q, self.codes, self.idx, q_pos0=c["q_pos0"], m=4, win_kv=self.swa,
+                         win_pos0=c["win_pos0"], sink=self.sink, entries_rope=self.rope, entry_scale=self.scale,
+                         out=self.out)
+        else:  # V4.1 layout: NVFP4 entries, FP8 window ring
+            L.csa_attend(self.q, self.codes, self.idx, q_pos0=c["q_pos0"], m=4, win_kv=self.win8,
+                         win_pos0=self.win8_pos0, sink=self.sink, entry_scale=self.scale, win_scale=self.win8_scale,
+                         out=self.out)
         if ev: ev[2].record()
 
     cpu_desc = ("%d sequences (all): oracle top-k over 262144 entries + attention for each query "
@@ -521,12 +550,15 @@ class DecodeLayer:
                                          self.rope[b].view(torch_int16()).cpu().numpy().view(np.uint16),
                                          self.scale[b].cpu().numpy())
             swa = self.swa[b].view(torch_int16()).cpu().numpy().view(np.uint16)
+            wkw = dict(win=swa, win_pos0=c["win_pos0"])
+            if self.win8 is not None:
+                wkw = dict(win_post=orc.load_window_fp8(self.win8[b].cpu().numpy(), self.win8_scale[b].cpu().numpy()),
+                           win_pos0=self.win8_pos0)
             qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(qI[b]).astype(np.float32))
             t1 = time.time()
             rows = np.zeros(1, np.int32)
             idx = orc.index_topk_rows(orc.mxfp4_decode(qc, qs), w[b], kdec, 4, c["q_pos0"], rows, self.k)
-            orc.attend_rows(q[b], c["q_pos0"], E, 4, rows, "csa", idx=idx, win=swa, win_pos0=c["win_pos0"],
-                            sink=sink)
+            orc.attend_rows(q[b], c["q_pos0"], E, 4, rows, "csa", idx=idx, sink=sink, **wkw)
             t_rows += time.time() - t1
         return nb / t_rows, nb, time.time() - t0 - t_rows, t_rows
 
@@ -744,7 +776,8 @@ def main():
              4: "fp8 e4m3 + bf16 entries, bf16 MFMA (attention) + mxfp4 (indexer MFMA)",
              5: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)"}[args.config]
     if args.entry_fmt == "nvfp4":
-        wname = wname.replace("262144 FP8+bf16 entries", "262144 NVFP4 entries (post-RoPE, the V4.1 variant)")
+        wname = wname.replace("262144 FP8+bf16 entries", "262144 NVFP4 entries + an FP8 window cache "
+                                                         "(post-RoPE, the V4.1 variant)")
         dname = dname.replace("fp8 e4m3 + bf16 entries", "nvfp4 entries")
     cfg = {"workload": wname, "global_batch": getattr(wl, "B", 1), "seq_len": wl.n,
            "heads": wl.H, "head_dim": 128}
