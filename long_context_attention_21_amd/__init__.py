@@ -154,6 +154,11 @@ def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=12
         ef = FMT_NVFP4  # NVFP4 records [B, N, 72] u8 + entry_scale
     else:
         ef = FMT_BF16
+    want = {FMT_BF16: D, FMT_FP8_ROPE_BF16: 64, FMT_NVFP4: 72}[ef]
+    if entries.shape[-1] != want:
+        raise ValueError("csa_attend: entries of the %s format have %d values per row, got %d"
+                         % ({FMT_BF16: "bf16", FMT_FP8_ROPE_BF16: "fp8", FMT_NVFP4: "nvfp4"}[ef], want,
+                            entries.shape[-1]))
     if out is None:
         out = torch.empty_like(q, dtype=torch.bfloat16)
     win_len = 0 if win_kv is None else win_kv.shape[1]

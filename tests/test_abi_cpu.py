@@ -307,3 +307,14 @@ def test_project_out_rejects(L, kw, needle):
     a.update(kw)
     assert L.csa_project_out(*a.values()) == _lib.CSA_INVALID_ARG
     assert needle in _msg(L)
+
+
+def test_binding_checks_the_entry_row_width():
+    """FP8 entries passed without entries_rope would read as NVFP4 records:
+    the binding refuses rows of the wrong width before calling the library."""
+    torch = pytest.importorskip("torch")
+    import long_context_attention_21_amd as Lb
+    q = torch.zeros((1, 1, 8, 128), dtype=torch.bfloat16)
+    ent = torch.zeros((1, 16, 64), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="nvfp4"):
+        Lb.csa_attend(q, ent, torch.zeros((1, 1, 4), dtype=torch.int32), entry_scale=torch.zeros((1, 16)))
