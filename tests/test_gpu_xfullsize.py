@@ -107,6 +107,41 @@ def test_config4_decode_full(orc):
 
 
 @pytest.mark.timeout(600)
+def test_config4_decode_full_v41_layout(orc):
+    """Config 4 in the V4.1 layout the benchmark times with --entry-fmt
+    nvfp4: NVFP4 entries stored by csa_compress and the FP8 window ring
+    written by csa_cache_append; sampled sequences against the oracle, the
+    stored window bytes against the oracle's FP8 window rule."""
+    import bench
+    bench.DecodeLayer.entry_fmt = "nvfp4"
+    try:
+        wl = bench.DecodeLayer(4)
+    finally:
+        bench.DecodeLayer.entry_fmt = "fp8"
+    wl.step()
+    torch.cuda.synchronize()
+    c = wl.c
+    t = c["q_pos0"]
+    q = _bits(wl.q)
+    sink = wl.sink.cpu().numpy()
+    got_idx = wl.idx.cpu().numpy()
+    got_out = _bits(wl.out)
+    j0 = c["win_pos0"]
+    s0 = j0 - wl.win8_pos0
+    for b in (0, 37, wl.B - 1):
+        codes8, sc8 = wl.win8[b].cpu().numpy(), wl.win8_scale[b].cpu().numpy()
+        ref_c, ref_s = orc.store_window_fp8(_bits(wl.swa[b]), j0)
+        assert np.array_equal(codes8[s0:s0 + c["n_win"]], ref_c)
+        assert np.array_equal(sc8[s0:s0 + c["n_win"]], ref_s)
+        E = orc.load_entries_nvfp4(wl.codes[b].cpu().numpy(), wl.scale[b].cpu().numpy())
+        rows = np.zeros(1, np.int32)
+        idx = got_idx[b]  # the top-k itself is checked bit-exactly in the FP8 layout test
+        ref = orc.attend_rows(q[b], t, E, 4, rows, "csa", idx=idx, win_post=orc.load_window_fp8(codes8, sc8),
+                              win_pos0=wl.win8_pos0, sink=sink)
+        assert_close(got_out[b], ref, "config 4 V4.1 layout csa_attend (sequence %d)" % b)
+
+
+@pytest.mark.timeout(600)
 def test_config5_pair_full(orc):
     import bench
     wl = bench.PairLayer(5)
