@@ -66,6 +66,8 @@ extern "C" {
                                    post-RoPE dims + 8 e4m3 scales of 16-dim blocks) + f32 scale [..] */
 #define CSA_FMT_FP8 4           /* window cache: e4m3 [.., 128] of post-RoPE rows + f32 scale [..]
                                    (amax / 448 over the 128 dims) */
+#define CSA_FMT_BF16_ROPED 5    /* window: bf16 [.., 128] rows already rotated at their positions
+                                   (csa_rope_rows) */
 
 /*
  * csa_compress -- token-level compressor (CSA: m = 4 with overlap; HCA:
@@ -247,7 +249,8 @@ int csa_index_topk_fallbacks(uint64_t* count, int reset);
  *               the rows rotated at their positions, value = code *
  *               win_scale (csa_cache_append writes such a ring)
  *  n_win        0 (no window) .. 128
- *  win_fmt      CSA_FMT_BF16 or CSA_FMT_FP8
+ *  win_fmt      CSA_FMT_BF16 (raw rows), CSA_FMT_BF16_ROPED (rows rotated at
+ *               their positions by csa_rope_rows) or CSA_FMT_FP8
  *  win_scale    FP8 window: [B, win_len] fp32; else NULL
  *  sink         [H] fp32 or NULL (no sink)
  *  out          [B, n, H, 128] bf16
@@ -278,8 +281,22 @@ size_t csa_attend_workspace_bytes(int B, int n, int k, int n_win, int entry_fmt)
  */
 int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D,
                const void* entries, int N, int m,
-               const void* win_kv, int64_t win_pos0, int win_len, int n_win,
+               const void* win_kv, int64_t win_pos0, int win_len, int n_win, int win_fmt,
                const float* sink, int rope_dims, float rope_base, void* out, void* stream);
+
+/*
+ * csa_rope_rows -- the window rows rotated once (wiki summary item 1:
+ * partial RoPE on the last 64 dims).  out[b, i] = kv[b, i] with each pair
+ * (64 + 2f, 65 + 2f) rotated by (pos0 + i) * rope_base^(-2f/64) in fp64,
+ * rounded to fp32 and then to bf16 (the same rotation as the entries).
+ * Attention that reads such rows as its window (win_fmt =
+ * CSA_FMT_BF16_ROPED) does not rotate them per query token.
+ *  kv, out  [B, T, 128] bf16, 4-byte aligned device pointers; out may be kv
+ *  rope_dims  must be 64
+ * Asynchronous on `stream`; nothing is launched on error.
+ */
+int csa_rope_rows(const void* kv, int B, int T, int64_t pos0, int rope_dims, float rope_base, void* out,
+                  void* stream);
 
 /*
  * Projections around the attention path (the step either side of it).

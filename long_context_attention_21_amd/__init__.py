@@ -14,10 +14,11 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (FMT_BF16, FMT_FP8, FMT_FP8_ROPE_BF16, FMT_MXFP4, FMT_NVFP4, CsaError, check, lib)
+from ._lib import (FMT_BF16, FMT_BF16_ROPED, FMT_FP8, FMT_FP8_ROPE_BF16, FMT_MXFP4, FMT_NVFP4, CsaError, check,
+                   lib)
 
 __all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend",
-           "csa_project_in", "csa_project_qidx", "csa_project_out", "version",
+           "csa_project_in", "csa_project_qidx", "csa_project_out", "csa_rope_rows", "version",
            "CsaError",
            "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16", "FMT_NVFP4", "FMT_FP8"]
 
@@ -138,11 +139,12 @@ def csa_index_topk_fallbacks(reset=False):
 
 def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=128, sink=None,
                entries_rope=None, entry_scale=None, rope_dims=64, rope_base=10000.0, N=None,
-               out=None, ws=None, win_scale=None, stream=None):
+               out=None, ws=None, win_scale=None, win_roped=False, stream=None):
     """q [B, n, H, 128] bf16; entries [B, N, 128] bf16 (or e4m3 [B, N, 64] with
     entries_rope/entry_scale, or NVFP4 records [B, N, 72] u8 with entry_scale
     only); idx [B, n, k] int32; win_kv [B, W, 128] bf16 raw rows, or with
-    win_scale an FP8 window cache (e4m3 [B, W, 128] of rotated rows).
+    win_scale an FP8 window cache (e4m3 [B, W, 128] of rotated rows), or
+    with win_roped rows rotated by csa_rope_rows.
     ``ws``: workspace of csa_attend_workspace_bytes() bytes (allocated here
     when needed and not given)."""
     B, n, H, D = q.shape
@@ -169,16 +171,18 @@ def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=12
     check(lib().csa_attend(
         _ptr(q), B, n, int(q_pos0), H, D, _ptr(entries), _ptr(entries_rope), _ptr(entry_scale), ef,
         N, m, _ptr(idx), idx.shape[2], _ptr(win_kv), int(win_pos0), win_len, nw,
-        FMT_BF16 if win_scale is None else FMT_FP8, _ptr(win_scale), _ptr(sink), rope_dims,
+        FMT_FP8 if win_scale is not None else (FMT_BF16_ROPED if win_roped else FMT_BF16), _ptr(win_scale),
+        _ptr(sink), rope_dims,
         float(rope_base), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
     return out
 
 
 def hca_attend(q, entries, q_pos0=0, m=128, win_kv=None, win_pos0=0, n_win=128, sink=None,
-               rope_dims=64, rope_base=10000.0, N=None, out=None, stream=None):
+               rope_dims=64, rope_base=10000.0, N=None, out=None, win_roped=False, stream=None):
     """q [B, n, H, 128] bf16; entries [B, N, 128] bf16: dense attention over
-    every visible entry + window + sink."""
+    every visible entry + window + sink.  win_roped: win_kv rows were rotated
+    by csa_rope_rows."""
     B, n, H, D = q.shape
     if N is None:
         N = entries.shape[1]
@@ -187,8 +191,8 @@ def hca_attend(q, entries, q_pos0=0, m=128, win_kv=None, win_pos0=0, n_win=128, 
     win_len = 0 if win_kv is None else win_kv.shape[1]
     check(lib().hca_attend(
         _ptr(q), B, n, int(q_pos0), H, D, _ptr(entries), N, m, _ptr(win_kv), int(win_pos0), win_len,
-        int(n_win) if win_kv is not None else 0, _ptr(sink), rope_dims, float(rope_base), _ptr(out),
-        _stream(stream)))
+        int(n_win) if win_kv is not None else 0, FMT_BF16_ROPED if win_roped else FMT_BF16, _ptr(sink),
+        rope_dims, float(rope_base), _ptr(out), _stream(stream)))
     return out
 
 
@@ -242,4 +246,14 @@ def csa_project_out(o, w_o, G, out=None, stream=None):
     if out is None:
         out = torch.empty((M, d), dtype=torch.bfloat16, device=o.device)
     check(lib().csa_project_out(_ptr(o), M, H, D, G, _ptr(w_o), d, _ptr(out), _stream(stream)))
+    return out
+
+
+def csa_rope_rows(kv, pos0=0, rope_dims=64, rope_base=10000.0, out=None, stream=None):
+    """kv [B, T, 128] bf16 raw rows of positions pos0.. -> the rows rotated
+    at their positions (csa_rope_rows), for win_roped windows."""
+    B, T, _ = kv.shape
+    if out is None:
+        out = torch.empty_like(kv)
+    check(lib().csa_rope_rows(_ptr(kv), B, T, int(pos0), rope_dims, float(rope_base), _ptr(out), _stream(stream)))
     return out

@@ -21,10 +21,11 @@ FMT_MXFP4 = 1
 FMT_FP8_ROPE_BF16 = 2
 FMT_NVFP4 = 3
 FMT_FP8 = 4
+FMT_BF16_ROPED = 5
 
 EXPORTS = ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_workspace_bytes",
            "csa_index_topk_fallbacks", "csa_attend", "csa_attend_workspace_bytes", "hca_attend", "csa_project_in",
-           "csa_project_qidx", "csa_project_out", "csa_last_error", "csa_version")
+           "csa_project_qidx", "csa_project_out", "csa_rope_rows", "csa_last_error", "csa_version")
 
 
 class CsaError(RuntimeError):
@@ -58,13 +59,15 @@ def lib():
                              i32, i32, P, P, i32, f32, P, P, sz, P]
     L.csa_attend_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.csa_attend_workspace_bytes.restype = sz
-    L.hca_attend.argtypes = [P, i32, i32, i64, i32, i32, P, i32, i32, P, i64, i32, i32, P, i32, f32,
+    L.hca_attend.argtypes = [P, i32, i32, i64, i32, i32, P, i32, i32, P, i64, i32, i32, i32, P, i32, f32,
                              P, P]
+    L.csa_rope_rows.argtypes = [P, i32, i32, i64, i32, f32, P, P]
     L.csa_project_in.argtypes = [P, i32, i32, P, i32, i32, i32, i32, i32, i32, P, i32, P, P, P, P, P, P, P, P, P]
     L.csa_project_qidx.argtypes = [P, i32, i32, P, i32, P, P, P, P]
     L.csa_project_out.argtypes = [P, i32, i32, i32, i32, P, i32, P, P]
     for f in ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend",
-              "hca_attend", "csa_project_in", "csa_project_qidx", "csa_project_out", "csa_version"):
+              "hca_attend", "csa_project_in", "csa_project_qidx", "csa_project_out", "csa_rope_rows",
+              "csa_version"):
         getattr(L, f).restype = i32
     L.csa_last_error.restype = C.c_char_p
     L.csa_last_error.argtypes = []

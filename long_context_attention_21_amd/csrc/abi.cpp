@@ -273,8 +273,9 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   REQUIRE(rope_dims == 0 || (std::isfinite(rope_base) && rope_base > 1.0f),
           "%s: rope_base must be finite and > 1", name);
   REQUIRE(n_win >= 0, "%s: n_win=%d must be >= 0", name, n_win);
-  REQUIRE(win_fmt == CSA_FMT_BF16 || win_fmt == CSA_FMT_FP8, "%s: win_fmt=%d unsupported", name, win_fmt);
-  REQUIRE(win_fmt == CSA_FMT_BF16 || mode == 1 || mode == 3,
+  REQUIRE(win_fmt == CSA_FMT_BF16 || win_fmt == CSA_FMT_FP8 || win_fmt == CSA_FMT_BF16_ROPED,
+          "%s: win_fmt=%d unsupported", name, win_fmt);
+  REQUIRE(win_fmt != CSA_FMT_FP8 || mode == 1 || mode == 3,
           "%s: an FP8 window needs FP8 or NVFP4 entries (the decode cache layout)", name);
   // row sources are addressed with 32-bit byte offsets inside the kernel
   REQUIRE((int64_t)N * 256 < 0x7fff0000LL && (int64_t)win_len * 256 < 0x7fff0000LL,
@@ -291,7 +292,7 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   if (mode == 3) REQUIRE(N == 0 || entry_scale, "%s: NVFP4 entries need entry_scale", name);
   if (n_win > 0) {
     REQUIRE(win_kv != nullptr, "%s: win_kv is NULL but n_win > 0", name);
-    REQUIRE(win_fmt == CSA_FMT_BF16 || win_scale != nullptr, "%s: an FP8 window needs win_scale", name);
+    REQUIRE(win_fmt != CSA_FMT_FP8 || win_scale != nullptr, "%s: an FP8 window needs win_scale", name);
     int64_t lo = q_pos0 - n_win + 1;
     if (lo < 0) lo = 0;
     const int64_t hi = q_pos0 + n - 1;
@@ -321,6 +322,7 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   p.k = (mode == 2) ? 0 : k;
   p.win = (const uint16_t*)win_kv;
   p.win_fp8 = win_fmt == CSA_FMT_FP8 ? 1 : 0;
+  p.win_roped = win_fmt == CSA_FMT_BF16_ROPED ? 1 : 0;
   p.win_scale = win_scale;
   p.win_pos0 = win_pos0;
   p.win_len = win_len;
@@ -354,11 +356,32 @@ size_t csa_attend_workspace_bytes(int B, int n, int k, int n_win, int entry_fmt)
 }
 
 int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const void* entries,
-               int N, int m, const void* win_kv, int64_t win_pos0, int win_len, int n_win,
+               int N, int m, const void* win_kv, int64_t win_pos0, int win_len, int n_win, int win_fmt,
                const float* sink, int rope_dims, float rope_base, void* out, void* stream) {
+  REQUIRE(win_fmt == CSA_FMT_BF16 || win_fmt == CSA_FMT_BF16_ROPED, "hca_attend: win_fmt=%d unsupported",
+          win_fmt);
   return attend_common(2, q, B, n, q_pos0, H, D, entries, nullptr, nullptr, N, m, nullptr, 0,
-                       win_kv, win_pos0, win_len, n_win, CSA_FMT_BF16, nullptr, sink, rope_dims, rope_base,
+                       win_kv, win_pos0, win_len, n_win, win_fmt, nullptr, sink, rope_dims, rope_base,
                        out, nullptr, 0, stream, "hca_attend");
+}
+
+int csa_rope_rows(const void* kv, int B, int T, int64_t pos0, int rope_dims, float rope_base, void* out,
+                  void* stream) {
+  REQUIRE(B >= 0 && T >= 0, "csa_rope_rows: B=%d and T=%d must be >= 0", B, T);
+  REQUIRE(rope_dims == 64, "csa_rope_rows: rope_dims=%d must be 64", rope_dims);
+  REQUIRE(std::isfinite(rope_base) && rope_base > 1.0f, "csa_rope_rows: rope_base must be finite and > 1");
+  REQUIRE(pos0 >= 0, "csa_rope_rows: pos0 must be >= 0");
+  if ((int64_t)B * T == 0) return ok();
+  REQUIRE(kv && out, "csa_rope_rows: kv and out must be non-NULL");
+  REQUIRE(((uintptr_t)kv & 3u) == 0 && ((uintptr_t)out & 3u) == 0, "csa_rope_rows: kv and out must be 4-byte aligned");
+  csa::RopeRowsParams p{};
+  p.kv = (const uint32_t*)kv;
+  p.out = (uint32_t*)out;
+  p.rows = (int64_t)B * T;
+  p.T = T;
+  p.pos0 = pos0;
+  for (int f = 0; f < 32; ++f) p.theta[f] = std::pow((double)rope_base, -2.0 * f / 64.0);
+  return hip_status(csa::launch_rope_rows(p, (hipStream_t)stream), "csa_rope_rows");
 }
 
 // ---------------------------------------------------------------- projections

@@ -328,7 +328,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
           R.r[kt][ks][2] = pack_bf16(v2[0] * sc, v2[1] * sc);
           R.r[kt][ks][3] = pack_bf16(v3[0] * sc, v3[1] * sc);
         }
-    } else if (c >= n_ent_chunks && p.rope) {
+    } else if (c >= n_ent_chunks && p.rope && !p.win_roped) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         if (!R.v[kt]) continue;
@@ -860,7 +860,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
       constexpr int slot = decltype(tag)::value;
       arrive();
       const uint8_t* kb = &Ks[slot][0];
-      if (c >= n_ent_chunks && p.rope) {
+      if (c >= n_ent_chunks && p.rope && !p.win_roped) {
         rotate_window(c, slot);
         __syncthreads();  // rotated rows visible to every wave
       }
@@ -957,7 +957,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
       arrive();
       issue(c + 2, slot_next);
       const uint32_t msk = chunk_mask(c);
-      if (c >= n_ent_chunks && p.rope) {
+      if (c >= n_ent_chunks && p.rope && !p.win_roped) {
         rotate_window(c, slot);
         __syncthreads();  // rotated rows visible to every wave
       }

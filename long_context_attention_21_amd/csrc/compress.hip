@@ -272,6 +272,29 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressParams p) {
   }
 }
 
+// One wave per row: lane l holds dims 2l, 2l+1; lanes 32..63 rotate their
+// pair at the row's position exactly as the entries are rotated (fp64).
+__global__ __launch_bounds__(256) void rope_rows_kernel(RopeRowsParams p) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= p.rows) return;
+  const uint32_t x = p.kv[row * 64 + lane];
+  uint32_t y = x;
+  if (lane >= 32) {
+    const double phi = (double)(p.pos0 + row % p.T) * p.theta[lane - 32];
+    const double c = cos(phi), s = sin(phi);
+    const double x0 = bf16lo(x), x1 = bf16hi(x);
+    y = pack_bf16((float)(x0 * c - x1 * s), (float)(x0 * s + x1 * c));
+  }
+  p.out[row * 64 + lane] = y;
+}
+
+hipError_t launch_rope_rows(const RopeRowsParams& p, hipStream_t stream) {
+  if (p.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_rows_kernel, dim3((unsigned)((p.rows + 3) / 4)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
   int64_t total = p.append ? (int64_t)p.B : (int64_t)p.B * p.n_new;
   if (total == 0) return hipSuccess;

@@ -58,6 +58,7 @@ struct AttendParams {
   const uint16_t* win;  // [B, win_len, 128] bf16 pre-RoPE, or e4m3 post-RoPE when win_fp8
   const float* win_scale;  // win_fp8: [B, win_len]
   int win_fp8;
+  int win_roped;  // bf16 window rows already rotated at their positions
   int64_t win_pos0;
   int win_len, n_win;
   const float* sink;  // [H] or null
@@ -80,6 +81,18 @@ size_t attend_workspace(int mode, int B, int n, int k, int n_win);
 // mode: 0 = CSA with bf16 entries, 1 = CSA with fp8+bf16 entries, 2 = HCA,
 // 3 = CSA with NVFP4 entries
 hipError_t launch_attend(const AttendParams& p, int mode, hipStream_t stream);
+
+// Window rows rotated once: out[row] = kv[row] with dims 64..127 rotated at
+// position pos0 + (row % T) in fp64, rounded to fp32, then to bf16.
+struct RopeRowsParams {
+  const uint32_t* kv;  // [rows, 64] bf16 pairs
+  uint32_t* out;
+  int64_t rows;
+  int T;
+  int64_t pos0;
+  double theta[32];
+};
+hipError_t launch_rope_rows(const RopeRowsParams& p, hipStream_t stream);
 
 struct IndexParams {
   const void* q;             // bf16 [B, n, H_I, 64] or mxfp4 codes [B, n, H_I, 32]

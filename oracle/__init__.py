@@ -134,6 +134,15 @@ def mxfp4_decode(codes, scales):
     return out
 
 
+def rope_rows_bf16(rows_bits, pos0, rope_dims=64, rope_base=10000.0):
+    """Raw rows [n, 128] bf16 bits of positions pos0.. -> rows rotated at
+    their positions (fp64), rounded to fp32 and then to bf16 (bits)."""
+    r = bf16_to_f64(rows_bits)
+    for i in range(r.shape[0]):
+        lib().orc_rope(_p(r[i]), r.shape[1], rope_dims, float(rope_base), float(pos0 + i))
+    return bf16_from_f32(r.astype(np.float32))
+
+
 def store_window_fp8(win_bits, pos0, rope_dims=64, rope_base=10000.0):
     """Raw window rows [n, 128] bf16 bits of positions pos0.. -> the FP8
     window cache (codes [n, 128] e4m3 of the rotated rows, scale [n] f32)."""

@@ -171,8 +171,23 @@ def test_attend_rejects(L, kw, needle):
 
 
 def test_hca_rejects(L):
-    r = L.hca_attend(FAKE, 1, 8, 0, 64, 128, FAKE, 10, 0, FAKE, 0, 8, 128, None, 64, 10000.0, FAKE2, None)
+    r = L.hca_attend(FAKE, 1, 8, 0, 64, 128, FAKE, 10, 0, FAKE, 0, 8, 128, 0, None, 64, 10000.0, FAKE2, None)
     assert r == _lib.CSA_INVALID_ARG and "m=0" in _msg(L)
+    r = L.hca_attend(FAKE, 1, 8, 0, 64, 128, FAKE, 10, 4, FAKE, 0, 8, 128, 4, None, 64, 10000.0, FAKE2, None)
+    assert r == _lib.CSA_INVALID_ARG and "win_fmt=4" in _msg(L)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(rope_dims=0), "rope_dims=0"),
+    (dict(T=-1), "T=-1"),
+    (dict(out=None), "non-NULL"),
+    (dict(kv=MIS + 2), "aligned"),
+])
+def test_rope_rows_rejects(L, kw, needle):
+    a = dict(kv=FAKE, B=2, T=5, pos0=0, rope_dims=64, rope_base=10000.0, out=FAKE2, stream=None)
+    a.update(kw)
+    assert L.csa_rope_rows(*a.values()) == _lib.CSA_INVALID_ARG
+    assert needle in _msg(L)
 
 
 def test_last_error_is_thread_local(L):

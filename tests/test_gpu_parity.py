@@ -186,6 +186,10 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
     if wfmt == "fp8":  # the FP8 window cache of the whole sequence, from the oracle
         win8 = [orc.store_window_fp8(kv[b], 0) for b in range(B)]
         win = dev(np.stack([w[0] for w in win8]))
+    roped = None
+    if wfmt == "roped":  # rows rotated once at their positions, from the oracle
+        roped = np.stack([orc.rope_rows_bf16(kv[b], 0) for b in range(B)])
+        win = dev(roped)
     if mode == "csa":
         kw = {}
         if efmt == "fp8":
@@ -195,11 +199,13 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
             kw = dict(entry_scale=dev(np.stack([e["entry_scale"] for e in ents])))
         if win8 is not None:
             kw["win_scale"] = dev(np.stack([w[1] for w in win8]))
+        if roped is not None:
+            kw["win_roped"] = True
         out = L.csa_attend(dev(q), e_dev, dev(idx), q_pos0=q_pos0, m=m, win_kv=win, win_pos0=0,
                            n_win=n_win, sink=dev(sk) if sink else None, **kw)
     else:
         out = L.hca_attend(dev(q), e_dev, q_pos0=q_pos0, m=m, win_kv=win, win_pos0=0, n_win=n_win,
-                           sink=dev(sk) if sink else None)
+                           sink=dev(sk) if sink else None, win_roped=roped is not None)
     torch.cuda.synchronize()
     got = host_bits(out)
     if check_rows is not None:
@@ -208,6 +214,8 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
         wkw = dict(win=kv[b] if n_win else None)
         if win8 is not None:
             wkw = dict(win_post=orc.load_window_fp8(*win8[b]))
+        if roped is not None:
+            wkw = dict(win_post=orc.bf16_to_f64(roped[b]))
         ref = orc.attend_rows(q[b], q_pos0, ents[b]["entries_f64"], m, rows, mode,
                               idx=None if idx is None else idx[b][rows], win_pos0=0, n_win=n_win, sink=sk,
                               **wkw)
@@ -244,6 +252,10 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
     dict(B=2, n=50, H=64, q_pos0=400, m=4, mode="csa", k=96, efmt="nvfp4", kv_scale=1.0, wfmt="fp8"),
     dict(B=3, n=2, H=64, q_pos0=2200, m=4, mode="csa", k=512, efmt="nvfp4", kv_scale=1.0, wfmt="fp8"),
     dict(B=2, n=1, H=40, q_pos0=2200, m=4, mode="csa", k=512, efmt="fp8", kv_scale=1.0, wfmt="fp8"),
+    # windows rotated once by csa_rope_rows: CSA and HCA ring kernels, the FP8 split decode
+    dict(B=2, n=77, H=64, q_pos0=50, m=4, mode="csa", k=37, wfmt="roped"),
+    dict(B=1, n=300, H=16, q_pos0=0, m=8, mode="hca", wfmt="roped"),
+    dict(B=3, n=2, H=64, q_pos0=2200, m=4, mode="csa", k=512, efmt="fp8", kv_scale=1.0, wfmt="roped"),
 ])
 def test_attend_matches_oracle(orc, case):
     print("attend case %s" % case, flush=True)
@@ -263,6 +275,18 @@ def test_hca_two_token_work_groups(orc):
                                      rng.choice(n, 60, replace=False)]))
     print("hca two-token work-groups", flush=True)
     _attend_case(orc, 12, B=2, n=n, H=40, q_pos0=4200, m=m, mode="hca", check_rows=rows)
+    _attend_case(orc, 13, B=1, n=n, H=40, q_pos0=4200, m=m, mode="hca", check_rows=rows, wfmt="roped")
+
+
+@pytest.mark.parametrize("B,T,pos0", [(2, 300, 0), (1, 257, 1048000)])
+def test_rope_rows_matches_oracle(orc, B, T, pos0):
+    """csa_rope_rows: dims 0..63 copied, each pair of dims 64..127 rotated at
+    its row's position in fp64 and rounded to fp32 then bf16, bit for bit."""
+    rng = np.random.default_rng(T)
+    kv = _bf16(rng, (B, T, 128), 0.7)
+    got = host_bits(L.csa_rope_rows(dev(kv), pos0=pos0))
+    for b in range(B):
+        assert np.array_equal(got[b], orc.rope_rows_bf16(kv[b], pos0))
 
 
 def test_attend_deterministic_and_batch_invariant(orc):
