@@ -46,6 +46,7 @@ TRAFFIC[("csa_project_in", "proj")] = {  # the GEMM (1.085e9) + the indexer-quer
     "sha256": "59d66afdeef9ae5420b43f5642fb7e92fad86f487007ac22a01617daafc9a5f5", "bytes": 1.095e9}
 KERNEL_SOURCE = {"csa_compress": "compress.hip", "hca_compress": "compress.hip", "csa_index_topk": "index_topk.hip",
                  "csa_attend": "attend.hip", "hca_attend": "attend.hip", "csa_project_in": "proj.hip",
+                 "csa_rope_rows": "compress.hip", "hca_rope_rows": "compress.hip",
                  "csa_project_out": "proj.hip"}
 
 
@@ -315,7 +316,8 @@ class CsaLayer:
             self.bufs["kidx_scale"] = torch.empty((1, N, 2), dtype=torch.uint8, device="cuda")
         self.idx = torch.empty((1, n, self.k), dtype=torch.int32, device="cuda")
         self.out = torch.empty((1, n, self.H, 128), dtype=torch.bfloat16, device="cuda")
-        self.kernels = ["csa_compress", "csa_index_topk", "csa_attend"]
+        self.kernels = ["csa_compress", "csa_rope_rows", "csa_index_topk", "csa_attend"]
+        self.kv_rot = torch.empty_like(self.kv)
         # algorithmic work (measurement)
         t = np.arange(n, dtype=np.int64)
         nv = np.minimum(N, (t + 1) // self.m)
@@ -324,6 +326,7 @@ class CsaLayer:
         kbytes = 34 if self.fmt == "mxfp4" else 128
         self.work = {
             "csa_compress": ("hbm", n * (256 + 128) + N * (256 + kbytes)),
+            "csa_rope_rows": ("hbm", n * 512),
             "csa_index_topk": ("fp4" if self.fmt == "mxfp4" else "bf16", 2.0 * 8 * 64 * pairs
                                if self.fmt == "mxfp4" else 2.0 * c["H_I"] * 64 * pairs),
             "csa_attend": ("bf16", 4.0 * self.H * 128 * keys),
@@ -335,12 +338,14 @@ class CsaLayer:
         if ev: ev[0].record()
         L.csa_compress(self.kv, self.beta, self.m, 1, ik=self.ik, kidx_fmt=self.fmt, out=self.bufs)
         if ev: ev[1].record()
+        L.csa_rope_rows(self.kv, out=self.kv_rot)
+        if ev: ev[2].record()
         L.csa_index_topk(self.qI, self.w, self.bufs["kidx"], self.k, self.m, fmt=self.fmt,
                          kidx_scale=self.bufs.get("kidx_scale"), idx_out=self.idx)
-        if ev: ev[2].record()
-        L.csa_attend(self.q, self.bufs["entries"], self.idx, m=self.m, win_kv=self.kv,
-                     sink=self.sink, out=self.out)
         if ev: ev[3].record()
+        L.csa_attend(self.q, self.bufs["entries"], self.idx, m=self.m, win_kv=self.kv_rot, win_roped=True,
+                     sink=self.sink, out=self.out)
+        if ev: ev[4].record()
 
     def cpu_baseline(self, sample):
         """The oracle on `sample` query rows spread over the sequence (plus the
@@ -388,12 +393,14 @@ class HcaLayer:
         self.N = N
         self.bufs = {"entries": torch.empty((1, N, 128), dtype=torch.bfloat16, device="cuda")}
         self.out = torch.empty((1, self.n, self.H, 128), dtype=torch.bfloat16, device="cuda")
-        self.kernels = ["csa_compress", "hca_attend"]
+        self.kernels = ["csa_compress", "csa_rope_rows", "hca_attend"]
+        self.kv_rot = torch.empty_like(self.kv)
         t = np.arange(self.n, dtype=np.int64)
         keys = int((np.minimum(N, (t + 1) // self.m) + np.minimum(t + 1, 128)).sum())
         self.keys = keys
         self.work = {
             "csa_compress": ("hbm", self.n * 256 + N * 256),
+            "csa_rope_rows": ("hbm", self.n * 512),
             "hca_attend": ("bf16", 4.0 * self.H * 128 * keys),
         }
         # HBM bytes of hca_attend: q in, out back, entries + raw rows once
@@ -404,9 +411,11 @@ class HcaLayer:
         if ev: ev[0].record()
         L.csa_compress(self.kv, self.beta, self.m, 0, out=self.bufs)
         if ev: ev[1].record()
-        L.hca_attend(self.q, self.bufs["entries"], m=self.m, win_kv=self.kv, sink=self.sink,
-                     out=self.out)
+        L.csa_rope_rows(self.kv, out=self.kv_rot)
         if ev: ev[2].record()
+        L.hca_attend(self.q, self.bufs["entries"], m=self.m, win_kv=self.kv_rot, win_roped=True, sink=self.sink,
+                     out=self.out)
+        if ev: ev[3].record()
 
     def cpu_baseline(self, sample):
         import oracle as orc
@@ -605,7 +614,10 @@ class PairLayer:
         self.c_out = torch.empty((1, n, H, 128), dtype=torch.bfloat16, device=cu)
         self.h_out = torch.empty((1, n, H, 128), dtype=torch.bfloat16, device=cu)
         log("pair inputs generated in %.1f s" % (time.time() - t0))
-        self.kernels = ["csa_compress", "csa_index_topk", "csa_attend", "hca_compress", "hca_attend"]
+        self.kernels = ["csa_compress", "csa_rope_rows", "csa_index_topk", "csa_attend", "hca_compress",
+                        "hca_rope_rows", "hca_attend"]
+        self.c_rot = torch.empty_like(self.c_win)
+        self.h_rot = torch.empty_like(self.h_win)
         t = P + np.arange(n, dtype=np.int64)
         nv = np.minimum(self.Nc, (t + 1) // 4)
         pairs = int(nv.sum())
@@ -613,9 +625,11 @@ class PairLayer:
         keys_h = int((np.minimum(self.Nh, (t + 1) // 128) + 128).sum())
         self.work = {
             "csa_compress": ("hbm", n * (256 + 128) + (n // 4) * (256 + 34)),
+            "csa_rope_rows": ("hbm", (n + 128) * 512),
             "csa_index_topk": ("fp4", 2.0 * 8 * 64 * pairs),
             "csa_attend": ("bf16", 4.0 * H * 128 * keys_c),
             "hca_compress": ("hbm", n * 256 + (n // 128) * 256),
+            "hca_rope_rows": ("hbm", (n + 128) * 512),
             "hca_attend": ("bf16", 4.0 * H * 128 * keys_h),
         }
 
@@ -627,17 +641,21 @@ class PairLayer:
                        out={"entries": self.c_ent[:, self.Nc0:], "kidx": self.c_kc[:, self.Nc0:],
                             "kidx_scale": self.c_ks[:, self.Nc0:]})
         if ev: ev[1].record()
+        L.csa_rope_rows(self.c_win, pos0=P - 128, out=self.c_rot)
+        if ev: ev[2].record()
         L.csa_index_topk(self.c_qI, self.c_w, self.c_kc, self.k, 4, q_pos0=P, fmt="mxfp4",
                          kidx_scale=self.c_ks, idx_out=self.idx)
-        if ev: ev[2].record()
-        L.csa_attend(self.c_q, self.c_ent, self.idx, q_pos0=P, m=4, win_kv=self.c_win, win_pos0=P - 128,
-                     sink=self.c_sink, out=self.c_out)
         if ev: ev[3].record()
-        L.csa_compress(self.h_win[:, 128:], self.h_beta, 128, 0, pos0=P, out={"entries": self.h_ent[:, self.Nh0:]})
+        L.csa_attend(self.c_q, self.c_ent, self.idx, q_pos0=P, m=4, win_kv=self.c_rot, win_pos0=P - 128,
+                     win_roped=True, sink=self.c_sink, out=self.c_out)
         if ev: ev[4].record()
-        L.hca_attend(self.h_q, self.h_ent, q_pos0=P, m=128, win_kv=self.h_win, win_pos0=P - 128,
-                     sink=self.h_sink, out=self.h_out)
+        L.csa_compress(self.h_win[:, 128:], self.h_beta, 128, 0, pos0=P, out={"entries": self.h_ent[:, self.Nh0:]})
         if ev: ev[5].record()
+        L.csa_rope_rows(self.h_win, pos0=P - 128, out=self.h_rot)
+        if ev: ev[6].record()
+        L.hca_attend(self.h_q, self.h_ent, q_pos0=P, m=128, win_kv=self.h_rot, win_pos0=P - 128,
+                     win_roped=True, sink=self.h_sink, out=self.h_out)
+        if ev: ev[7].record()
 
     cpu_desc = ("%d query rows of the 8192-token chunk drawn uniformly (seed 0): oracle CSA top-k + CSA "
                 "attention + HCA attention for those rows (%.1f s) plus the chunk's compression and cache "
