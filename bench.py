@@ -35,13 +35,15 @@ PEAK = {"bf16": 2500.0, "fp4": 10100.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s
 # sha256 of the kernel source they were taken on: a changed kernel reports
 # null until it is measured again.
 TRAFFIC = {  # profiles/csa_prefill_128k_hbm_counters.txt
-    ("csa_attend", 3): {"sha256": "aaa3feb197cb71834fb9cc8e437a1987c3a13c53fcc135faacfa88689471c400",
-                        "bytes": 1.954e10},
+    ("csa_attend", 3): {"sha256": "e4d67a262a771eefd506e2e8ca3a48247ea4c93dcac50b6d8d050bb353095fe5",
+                        "bytes": 1.943e10},
     ("csa_index_topk", 3): {"sha256": "ada64fe8f93a0955d7ff56bda206aa179d0e7c562b8687c43a7f870c6ba6fe35",
                             "bytes": 1.223e9},
-    ("csa_compress", 3): {"sha256": "d3119e7fe36669523a4296ee9571fe4868d60864ebeaee70af82ec86296cc975",
+    ("csa_compress", 3): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242",
                           "bytes": 7.298e7},
 }
+TRAFFIC[("csa_rope_rows", 3)] = {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242",
+                                 "bytes": 6.719e7}
 TRAFFIC[("csa_project_in", "proj")] = {  # the GEMM (1.085e9) + the indexer-query kernel (9.7e6)
     "sha256": "59d66afdeef9ae5420b43f5642fb7e92fad86f487007ac22a01617daafc9a5f5", "bytes": 1.095e9}
 KERNEL_SOURCE = {"csa_compress": "compress.hip", "hca_compress": "compress.hip", "csa_index_topk": "index_topk.hip",
