@@ -318,6 +318,7 @@ class CsaLayer:
             self.bufs["kidx_scale"] = torch.empty((1, N, 2), dtype=torch.uint8, device="cuda")
         self.idx = torch.empty((1, n, self.k), dtype=torch.int32, device="cuda")
         self.out = torch.empty((1, n, self.H, 128), dtype=torch.bfloat16, device="cuda")
+        self.fallbacks = torch.zeros(1, dtype=torch.int32, device="cuda")  # exact-path work-groups
         self.kernels = ["csa_compress", "csa_rope_rows", "csa_index_topk", "csa_attend"]
         self.kv_rot = torch.empty_like(self.kv)
         # algorithmic work (measurement)
@@ -343,7 +344,7 @@ class CsaLayer:
         L.csa_rope_rows(self.kv, out=self.kv_rot)
         if ev: ev[2].record()
         L.csa_index_topk(self.qI, self.w, self.bufs["kidx"], self.k, self.m, fmt=self.fmt,
-                         kidx_scale=self.bufs.get("kidx_scale"), idx_out=self.idx)
+                         kidx_scale=self.bufs.get("kidx_scale"), idx_out=self.idx, fallback_count=self.fallbacks)
         if ev: ev[3].record()
         L.csa_attend(self.q, self.bufs["entries"], self.idx, m=self.m, win_kv=self.kv_rot, win_roped=True,
                      sink=self.sink, out=self.out)
@@ -490,6 +491,7 @@ class DecodeLayer:
         self.q, self.qI, self.w, self.sink = dev_bf16(q), dev_bf16(q_I), dev(w_I), dev(sink)
         self.idx = torch.empty((B, 1, self.k), dtype=torch.int32, device=cu)
         self.out = torch.empty((B, 1, H, 128), dtype=torch.bfloat16, device=cu)
+        self.fallbacks = torch.zeros(1, dtype=torch.int32, device=cu)  # exact-path work-groups
         self.kernels = ["csa_index_topk", "csa_attend"]
         keys = B * (min(self.k, N) + c["n_win"])
         # bytes: the indexer scans every key (34 B); attention gathers k entries (196 B FP8 + bf16,
@@ -526,7 +528,7 @@ class DecodeLayer:
         L, c = self.L, self.c
         if ev: ev[0].record()
         L.csa_index_topk(self.qI, self.w, self.kc, self.k, 4, q_pos0=c["q_pos0"], fmt="mxfp4",
-                         kidx_scale=self.ks, idx_out=self.idx)
+                         kidx_scale=self.ks, idx_out=self.idx, fallback_count=self.fallbacks)
         if ev: ev[1].record()
         if self.win8 is None:
             L.csa_attend(self.q, self.codes, self.idx, q_pos0=c["q_pos0"], m=4, win_kv=self.swa,
@@ -613,6 +615,7 @@ class PairLayer:
         self.h_win = dev_bf16(np.concatenate([hs["state_kv"], hs["kv_new"]])[None])
         self.h_q, self.h_beta, self.h_sink = dev_bf16(hs["q"][None]), dev(hs["beta"]), dev(hs["sink"])
         self.idx = torch.empty((1, n, k), dtype=torch.int32, device=cu)
+        self.fallbacks = torch.zeros(1, dtype=torch.int32, device=cu)  # exact-path work-groups
         self.c_out = torch.empty((1, n, H, 128), dtype=torch.bfloat16, device=cu)
         self.h_out = torch.empty((1, n, H, 128), dtype=torch.bfloat16, device=cu)
         log("pair inputs generated in %.1f s" % (time.time() - t0))
@@ -646,7 +649,7 @@ class PairLayer:
         L.csa_rope_rows(self.c_win, pos0=P - 128, out=self.c_rot)
         if ev: ev[2].record()
         L.csa_index_topk(self.c_qI, self.c_w, self.c_kc, self.k, 4, q_pos0=P, fmt="mxfp4",
-                         kidx_scale=self.c_ks, idx_out=self.idx)
+                         kidx_scale=self.c_ks, idx_out=self.idx, fallback_count=self.fallbacks)
         if ev: ev[3].record()
         L.csa_attend(self.c_q, self.c_ent, self.idx, q_pos0=P, m=4, win_kv=self.c_rot, win_pos0=P - 128,
                      win_roped=True, sink=self.c_sink, out=self.c_out)

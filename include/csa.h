@@ -38,8 +38,12 @@
  *    code).  Arguments are validated on the host before anything is
  *    launched; on error nothing is launched and csa_last_error() returns a
  *    thread-local message naming the argument.  No exception crosses the ABI.
- *  - Determinism: every result is bitwise reproducible run to run and does
- *    not depend on the batch size or on which other rows are in the call.
+ *  - Determinism: every result is bitwise reproducible run to run, and a
+ *    query row's result depends only on its own inputs (its query, position
+ *    and key set), not on the batch size, the number of rows in the call or
+ *    which other rows are in it (batch invariance).  csa_index_topk writes
+ *    each row's indices in ascending order, so the attention that consumes
+ *    them sees the same key order whatever path selected them.
  */
 #ifndef CSA_MI355X_H
 #define CSA_MI355X_H
@@ -181,8 +185,7 @@ int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new,
  * (exact for MXFP4 operands), the head sum as an fp32 fma chain in
  * ascending h starting from +0.  It keeps the min(k, n_vis) largest scores,
  * ties going to the lower entry index, and writes their indices followed by
- * -1 padding up to k.  The order of the indices within a row is unspecified
- * (it is deterministic for given inputs); attention does not depend on it.
+ * -1 padding up to k.  The indices of a row are written in ascending order.
  *
  *  qidx        fmt BF16: [B, n, H_I, 64] bf16.  fmt MXFP4 with
  *              qidx_scale == NULL: [B, n, H_I, 64] bf16, quantised in-kernel
@@ -196,29 +199,26 @@ int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new,
  *  idx_out     [B, n, k] int32
  *  ws, ws_bytes  device scratch of at least csa_index_topk_workspace_bytes()
  *              bytes, 16-byte aligned (may be NULL when that is 0).  It is
- *              non-zero for few query rows over long entry lists (n <= 4,
- *              B*n <= 512, at least 65536 visible entries), where the entry
+ *              non-zero for few query rows over long entry lists (n <= 4
+ *              and at least 65536 visible entries), where each row's entry
  *              list is split over many work-groups: 32784 bytes per query
  *              row.  Its contents need no initialisation and are undefined
  *              after the call; calls that share a workspace must be ordered
  *              on one stream.
+ *  fallback_count  NULL, or a caller-owned device uint32 (4-byte aligned):
+ *              the kernels add the number of work-groups that took the exact
+ *              streaming path (the sampled threshold left fewer than k or
+ *              more candidates than a buffer holds, e.g. under massive score
+ *              ties).  A diagnostic of slow calls; results are exact either
+ *              way.  The caller clears it; it is updated in stream order.
  */
 int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* widx,
                    const void* kidx, const uint8_t* kidx_scale, int fmt,
                    int B, int n, int64_t q_pos0, int H_I, int d_idx, int N, int m, int k,
-                   int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+                   int32_t* idx_out, void* ws, size_t ws_bytes, uint32_t* fallback_count,
+                   void* stream);
 
 size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m, int k);
-
-/*
- * csa_index_topk_fallbacks -- diagnostic: the number of csa_index_topk
- * work-groups on the current device that took the exact streaming path since
- * the last reset (the sampled threshold left fewer than k or more than 4096
- * candidates for one of their query rows, e.g. under massive score ties).
- * Results are exact either way; the count only explains a slow call.
- * Synchronises the device.  reset != 0 clears the counter after reading it.
- */
-int csa_index_topk_fallbacks(uint64_t* count, int reset);
 
 /*
  * csa_attend -- CSA core attention: sparse entries + sliding window + sink.
@@ -238,9 +238,9 @@ int csa_index_topk_fallbacks(uint64_t* count, int reset);
  *               NVFP4: [B, N, 72] records as csa_compress writes them
  *  entries_rope FP8_ROPE_BF16: [B, N, 64] bf16 (dims 64..127); else NULL
  *  entry_scale  FP8_ROPE_BF16 and NVFP4: [B, N] fp32; else NULL
- *  idx          [B, n, k] int32 entry indices (-1 = unused slot), 16-byte
- *               aligned, k <= 2048; every index must be < N (not checked on
- *               the device)
+ *  idx          [B, n, k] int32 entry indices, 16-byte aligned, k <= 2048;
+ *               -1 marks an unused slot, and any index outside [0, N) is
+ *               likewise no key
  *  win_kv       win_fmt BF16: [B, win_len, 128] bf16 pre-RoPE raw rows at
  *               positions win_pos0 .. win_pos0+win_len-1; must cover
  *               [max(0, q_pos0-n_win+1), q_pos0+n-1] when n_win > 0.
@@ -248,21 +248,24 @@ int csa_index_topk_fallbacks(uint64_t* count, int reset);
  *               FP8 or NVFP4 entries only): [B, win_len, 128] e4m3 codes of
  *               the rows rotated at their positions, value = code *
  *               win_scale (csa_cache_append writes such a ring)
- *  n_win        0 (no window) .. 128
+ *  n_win        0 (no window) .. 128; larger values are rejected
  *  win_fmt      CSA_FMT_BF16 (raw rows), CSA_FMT_BF16_ROPED (rows rotated at
- *               their positions by csa_rope_rows) or CSA_FMT_FP8
+ *               their positions by csa_rope_rows; needs rope_dims = 64) or
+ *               CSA_FMT_FP8
  *  win_scale    FP8 window: [B, win_len] fp32; else NULL
  *  sink         [H] fp32 or NULL (no sink)
  *  out          [B, n, H, 128] bf16
  *  ws, ws_bytes device scratch of at least csa_attend_workspace_bytes()
  *               bytes, 16-byte aligned (may be NULL when that is 0).  It is
- *               non-zero for FP8 entries with few query rows (B*n <= 512)
- *               and at least 16 chunks of 32 keys (k + n_win >= 512): each
- *               token's keys are then split over several work-groups whose
- *               partial softmax sums are merged in a fixed order (the result
- *               does not depend on the split).  33280 bytes per (query row,
- *               part of 8 chunks).  Contents are undefined after the call;
- *               calls that share a workspace must be ordered on one stream.
+ *               non-zero for FP8 and NVFP4 entries with at least 16 chunks of
+ *               32 keys (k + n_win >= 512): each token's keys are then split
+ *               over several work-groups (parts of 8 chunks) whose partial
+ *               softmax sums are merged in ascending part order.  The split
+ *               depends on k and n_win only, never on B or n; the tokens run
+ *               in blocks of at most 512, so the workspace is 33280 bytes
+ *               per (query row, part) for min(B*n, 512) rows.  Contents are
+ *               undefined after the call; calls that share a workspace must
+ *               be ordered on one stream.
  */
 int csa_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D,
                const void* entries, const void* entries_rope, const float* entry_scale,

@@ -17,7 +17,7 @@ import torch
 from ._lib import (FMT_BF16, FMT_BF16_ROPED, FMT_FP8, FMT_FP8_ROPE_BF16, FMT_MXFP4, FMT_NVFP4, CsaError, check,
                    lib)
 
-__all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_fallbacks", "csa_attend", "hca_attend",
+__all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_attend", "hca_attend",
            "csa_project_in", "csa_project_qidx", "csa_project_out", "csa_rope_rows", "version",
            "CsaError",
            "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16", "FMT_NVFP4", "FMT_FP8"]
@@ -108,9 +108,12 @@ def csa_cache_append(kv_new, beta, m, overlap, t, kv_ring, caches, ik_new=None, 
 
 
 def csa_index_topk(qidx, widx, kidx, k, m, q_pos0=0, fmt="mxfp4", qidx_scale=None,
-                   kidx_scale=None, N=None, idx_out=None, ws=None, stream=None):
+                   kidx_scale=None, N=None, idx_out=None, ws=None, fallback_count=None, stream=None):
     """qidx [B, n, H_I, 64] bf16 (or [B, n, H_I, 32] MXFP4 codes with
-    qidx_scale), widx [B, n, H_I] fp32, kidx [B, N, 64|32] -> idx [B, n, k] int32."""
+    qidx_scale), widx [B, n, H_I] fp32, kidx [B, N, 64|32] -> idx [B, n, k]
+    int32, each row's indices ascending.  fallback_count: an optional int32
+    cuda tensor of one element, to which the kernels add the number of
+    work-groups that took the exact streaming path (the caller clears it)."""
     B, n, H_I = qidx.shape[:3]
     if N is None:
         N = kidx.shape[1]
@@ -123,18 +126,8 @@ def csa_index_topk(qidx, widx, kidx, k, m, q_pos0=0, fmt="mxfp4", qidx_scale=Non
     check(lib().csa_index_topk(
         _ptr(qidx), _ptr(qidx_scale), _ptr(widx), _ptr(kidx), _ptr(kidx_scale), f, B, n,
         int(q_pos0), H_I, 64, N, m, k, _ptr(idx_out), _ptr(ws),
-        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        0 if ws is None else ws.numel() * ws.element_size(), _ptr(fallback_count), _stream(stream)))
     return idx_out
-
-
-def csa_index_topk_fallbacks(reset=False):
-    """Work-groups of csa_index_topk on the current device that took the
-    exact streaming path since the last reset (a diagnostic of slow calls;
-    results are exact either way).  Synchronises the device."""
-    import ctypes
-    c = ctypes.c_uint64(0)
-    check(lib().csa_index_topk_fallbacks(ctypes.byref(c), 1 if reset else 0))
-    return int(c.value)
 
 
 def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=128, sink=None,

@@ -207,36 +207,27 @@ size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m
   return csa::index_topk_workspace(B, n, q_pos0, N, m, k);
 }
 
-int csa_index_topk_fallbacks(uint64_t* count, int reset) {
-  REQUIRE(count != nullptr, "csa_index_topk_fallbacks: count is NULL");
-  unsigned long long c = 0;
-  const int st = hip_status(csa::index_topk_fallbacks(&c, reset != 0), "csa_index_topk_fallbacks");
-  *count = (uint64_t)c;
-  return st;
-}
-
-int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* widx,
-                   const void* kidx, const uint8_t* kidx_scale, int fmt, int B, int n,
-                   int64_t q_pos0, int H_I, int d_idx, int N, int m, int k, int32_t* idx_out,
-                   void* ws, size_t ws_bytes, void* stream) {
-  REQUIRE(B >= 0 && n >= 0 && N >= 0, "csa_index_topk: B=%d n=%d N=%d must be >= 0", B, n, N);
-  REQUIRE(fmt == CSA_FMT_BF16 || fmt == CSA_FMT_MXFP4, "csa_index_topk: fmt=%d unsupported", fmt);
-  REQUIRE(d_idx == 64, "csa_index_topk: d_idx=%d unsupported (must be 64)", d_idx);
-  REQUIRE(H_I >= 1 && H_I <= 8, "csa_index_topk: H_I=%d must be in [1, 8]", H_I);
-  REQUIRE(k >= 1 && k <= 2048, "csa_index_topk: k=%d must be in [1, 2048]", k);
-  REQUIRE(m >= 1, "csa_index_topk: m=%d must be >= 1", m);
-  REQUIRE(q_pos0 >= 0, "csa_index_topk: q_pos0 must be >= 0");
+static int index_common(const void* qidx, const uint8_t* qidx_scale, const float* widx, const void* kidx,
+                        const uint8_t* kidx_scale, int fmt, int B, int n, int64_t q_pos0, int H_I, int d_idx, int N,
+                        int m, int k, int32_t* idx_out, void* ws, size_t ws_bytes,
+                        uint32_t* fallback_count, void* stream, const char* name) {
+  REQUIRE(B >= 0 && n >= 0 && N >= 0, "%s: B=%d n=%d N=%d must be >= 0", name, B, n, N);
+  REQUIRE(fmt == CSA_FMT_BF16 || fmt == CSA_FMT_MXFP4, "%s: fmt=%d unsupported", name, fmt);
+  REQUIRE(d_idx == 64, "%s: d_idx=%d unsupported (must be 64)", name, d_idx);
+  REQUIRE(H_I >= 1 && H_I <= 8, "%s: H_I=%d must be in [1, 8]", name, H_I);
+  REQUIRE(k >= 1 && k <= 2048, "%s: k=%d must be in [1, 2048]", name, k);
+  REQUIRE(m >= 1, "%s: m=%d must be >= 1", name, m);
+  REQUIRE(q_pos0 >= 0, "%s: q_pos0 must be >= 0", name);
   if ((int64_t)B * n == 0) return ok();
-  REQUIRE(qidx && widx && idx_out, "csa_index_topk: qidx, widx and idx_out must be non-NULL");
-  REQUIRE(N == 0 || kidx != nullptr, "csa_index_topk: kidx is NULL");
-  if (fmt == CSA_FMT_MXFP4) REQUIRE(N == 0 || kidx_scale != nullptr, "csa_index_topk: MXFP4 needs kidx_scale");
-  REQUIRE(fmt == CSA_FMT_BF16 || qidx_scale == nullptr || aligned16(qidx),
-          "csa_index_topk: qidx must be 16-byte aligned");
-  REQUIRE(aligned16(qidx) && aligned16(kidx), "csa_index_topk: qidx and kidx must be 16-byte aligned");
+  REQUIRE(qidx && widx && idx_out, "%s: qidx, widx and idx_out must be non-NULL", name);
+  REQUIRE(N == 0 || kidx != nullptr, "%s: kidx is NULL", name);
+  if (fmt == CSA_FMT_MXFP4) REQUIRE(N == 0 || kidx_scale != nullptr, "%s: MXFP4 needs kidx_scale", name);
+  REQUIRE(aligned16(qidx) && aligned16(kidx), "%s: qidx and kidx must be 16-byte aligned", name);
+  REQUIRE(((uintptr_t)fallback_count & 3u) == 0, "%s: fallback_count must be 4-byte aligned", name);
   const size_t need = csa::index_topk_workspace(B, n, q_pos0, N, m, k);
   if (ws_bytes < need)
-    return fail(CSA_WORKSPACE_TOO_SMALL, "csa_index_topk: workspace of %zu bytes < %zu needed", ws_bytes, need);
-  REQUIRE(need == 0 || (ws != nullptr && aligned16(ws)), "csa_index_topk: ws must be non-NULL and 16-byte aligned");
+    return fail(CSA_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes < %zu needed", name, ws_bytes, need);
+  REQUIRE(need == 0 || (ws != nullptr && aligned16(ws)), "%s: ws must be non-NULL and 16-byte aligned", name);
   csa::IndexParams p{};
   p.q = qidx;
   p.q_scale = (fmt == CSA_FMT_MXFP4) ? qidx_scale : nullptr;
@@ -254,7 +245,16 @@ int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* wid
   p.idx_out = idx_out;
   p.ws = ws;
   p.ws_bytes = ws_bytes;
-  return hip_status(csa::launch_index_topk(p, (hipStream_t)stream), "csa_index_topk launch");
+  p.fallback_count = fallback_count;
+  return hip_status(csa::launch_index_topk(p, (hipStream_t)stream), name);
+}
+
+int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* widx,
+                   const void* kidx, const uint8_t* kidx_scale, int fmt, int B, int n,
+                   int64_t q_pos0, int H_I, int d_idx, int N, int m, int k, int32_t* idx_out,
+                   void* ws, size_t ws_bytes, uint32_t* fallback_count, void* stream) {
+  return index_common(qidx, qidx_scale, widx, kidx, kidx_scale, fmt, B, n, q_pos0, H_I, d_idx, N, m, k, idx_out, ws,
+                      ws_bytes, fallback_count, stream, "csa_index_topk");
 }
 
 static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, int H, int D,
@@ -272,9 +272,11 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   REQUIRE(rope_dims == 0 || rope_dims == 64, "%s: rope_dims=%d must be 0 or 64", name, rope_dims);
   REQUIRE(rope_dims == 0 || (std::isfinite(rope_base) && rope_base > 1.0f),
           "%s: rope_base must be finite and > 1", name);
-  REQUIRE(n_win >= 0, "%s: n_win=%d must be >= 0", name, n_win);
+  REQUIRE(n_win >= 0 && n_win <= 128, "%s: n_win=%d must be in [0, 128]", name, n_win);
   REQUIRE(win_fmt == CSA_FMT_BF16 || win_fmt == CSA_FMT_FP8 || win_fmt == CSA_FMT_BF16_ROPED,
           "%s: win_fmt=%d unsupported", name, win_fmt);
+  REQUIRE(win_fmt != CSA_FMT_BF16_ROPED || rope_dims == 64,
+          "%s: a pre-rotated window (CSA_FMT_BF16_ROPED) needs rope_dims = 64", name);
   REQUIRE(win_fmt != CSA_FMT_FP8 || mode == 1 || mode == 3,
           "%s: an FP8 window needs FP8 or NVFP4 entries (the decode cache layout)", name);
   // row sources are addressed with 32-bit byte offsets inside the kernel

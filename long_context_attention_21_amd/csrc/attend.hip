@@ -52,7 +52,8 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
   __shared__ __attribute__((aligned(16))) int32_t Is[MODE == 2 ? 4 : kMaxK];  // the token's idx row
   const int lane = threadIdx.x;
   const int g = lane >> 4, l16 = lane & 15;
-  const int64_t tok = SPLIT ? blockIdx.x / p.parts : blockIdx.x;  // b * n + q
+  // b * n + q; the split path runs the tokens in blocks (tok0: the block's first)
+  const int64_t tok = SPLIT ? p.tok0 + blockIdx.x / p.parts : blockIdx.x;
   const int part = SPLIT ? (int)(blockIdx.x % p.parts) : 0;
   const int b = (int)(tok / p.n);
   const int qi = (int)(tok % p.n);
@@ -167,6 +168,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
         if (MODE == 2) s = kk < n_ent ? kk : -1;
         else if (kk < p.k) s = Is[kk];
       }
+      if ((uint32_t)s >= (uint32_t)p.N) s = -1;  // -1 padding, or an index past the entries: no key
       out[kt] = s;
     }
   };
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendParams p) {
 
   if constexpr (SPLIT) {
     // ---- partial results: O[h][d] unnormalised, then mref[h], L[h]
-    float* w = p.ws + ((int64_t)tok * p.parts + part) * kAttendPartFloats;
+    float* w = p.ws + ((int64_t)(tok - p.tok0) * p.parts + part) * kAttendPartFloats;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const int h = ht * 16 + l16;
@@ -539,7 +541,8 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   static_assert(MODE == 2 || TOK == 1, "CSA tokens have their own key sets");
   constexpr int WPT = NW / TOK;  // waves per token
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kRing][32 * 256];
-  // CSA: the token's idx row, padded with -1 up to a multiple of 32
+  // CSA: the token's idx row, padded with -1 up to a multiple of 32 (an
+  // index outside [0, N) is stored as -1: no key)
   __shared__ __attribute__((aligned(16))) int32_t Is[MODE == 2 ? 4 : kMaxK];
   __shared__ float2 Rt[TOK][32];  // (cos, sin) of each token's angle t * theta_f, f = 0..31
   __shared__ float Rv[32];        // theta_f / 2pi (revolutions per position)
@@ -584,7 +587,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
         const int i = 4 * tid + it * 256 * NW;
         const u32x4 x = *(const u32x4*)&irow[min(i, p.k - 4)];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[it][e] = i < p.k ? x[e] : 0xffffffffu;
+        for (int e = 0; e < 4; ++e) v[it][e] = (i + e < p.k && x[e] < (uint32_t)p.N) ? x[e] : 0xffffffffu;
       }
     } else if (p.k > 0) {
 #pragma unroll
@@ -593,7 +596,7 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t x = (uint32_t)irow[min(i + e, p.k - 1)];
-          v[it][e] = i + e < p.k ? x : 0xffffffffu;
+          v[it][e] = (i + e < p.k && x < (uint32_t)p.N) ? x : 0xffffffffu;
         }
       }
     }
@@ -656,8 +659,10 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   }
 
   // ---- key sequence of the work-group: entry chunks, then window chunks
-  // (with several tokens: the entries of the last one and the union of the
-  // windows; each wave masks what its own token does not see)
+  // (with several tokens: the entries of the last one, then each token's own
+  // window in WC chunks per token slot; each wave masks what its own token
+  // does not see, so every token's keys sit in the same chunks as in a
+  // one-token work-group)
   int n_ent, n_ent_tok;
   if (MODE == 2) {
     const int64_t nv = (t_last + 1) / p.m, nt = (t + 1) / p.m;
@@ -679,22 +684,22 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     for (int w = 1; w < NW; ++w) fb = min(fb, first_bad[w]);
     n_full = __builtin_amdgcn_readfirstlane(fb) >> 5;
   }
-  int64_t j0 = 0;
-  int n_wk = 0, wlo = 0, whi = -1;
-  if (p.n_win > 0) {
-    j0 = t0 - p.n_win + 1;
-    if (j0 < 0) j0 = 0;
-    n_wk = (int)(t_last - j0 + 1);
-    // this token's window keys j in [max(0, t - n_win + 1), t], as offsets from j0
-    const int64_t jl = t - p.n_win + 1;
-    wlo = (int)((jl < 0 ? 0 : jl) - j0);
-    whi = (int)(t - j0);
+  // token slot s: window keys j = j0s[s] + wj, wj in [0, nwks[s]) (the
+  // positions max(0, t_s - n_win + 1) .. t_s); slots past the last token hold none
+  int64_t j0s[TOK];
+  int nwks[TOK];
+  int WC = 0;  // window chunks per token slot
+#pragma unroll
+  for (int s = 0; s < TOK; ++s) {
+    const int64_t ts = t0 + s;
+    int64_t js = ts - p.n_win + 1;
+    if (js < 0) js = 0;
+    j0s[s] = js;
+    nwks[s] = (p.n_win > 0 && q_first + s <= q_last) ? (int)(ts - js + 1) : 0;
+    nwks[s] = __builtin_amdgcn_readfirstlane(nwks[s]);
+    WC = max(WC, (nwks[s] + 31) >> 5);
   }
-  n_wk = __builtin_amdgcn_readfirstlane(n_wk);
-  wlo = __builtin_amdgcn_readfirstlane(wlo);
-  whi = __builtin_amdgcn_readfirstlane(whi);
-  const int n_chunks = n_ent_chunks + ((n_wk + 31) >> 5);
-  const int dt0 = __builtin_amdgcn_readfirstlane((int)(t0 - j0));  // t0 - j of window key 0
+  const int n_chunks = n_ent_chunks + TOK * WC;
 
   auto uniform_ptr = [](const void* ptr) {
     const uint64_t v = (uint64_t)ptr;
@@ -706,7 +711,12 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   const u32x4 rW = dma_rsrc(uniform_ptr(p.win ? p.win + (int64_t)bu * p.win_len * 128 : p.q),
                             p.win ? __builtin_amdgcn_readfirstlane(p.win_len * 256) : 0);
   const u32x4 rE = dma_rsrc(uniform_ptr(p.entries + (int64_t)bu * p.N * 128), __builtin_amdgcn_readfirstlane(p.N * 256));
-  const int win_row0 = __builtin_amdgcn_readfirstlane((int)(j0 - p.win_pos0));  // window source row of key j0
+  // window chunk c: its token slot and the window offset of its key 0
+  auto win_chunk = [&](int c, int& s, int& wb) {
+    const int cw = c - n_ent_chunks;
+    s = (TOK == 1 || cw < WC) ? 0 : 1;
+    wb = (cw - s * WC) * 32;
+  };
 
   // This wave's share of the loads of chunk c into ring slot `slot`: load
   // instructions q = wave*QPW .. +QPW-1, each 4 rows.  Always issued: a
@@ -735,10 +745,13 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
         for (int e = 0; e < QPW; ++e) rows[e] = kb0 + e < n_ent ? kb0 + e : -1;
       }
     } else {
+      int s, wb;
+      win_chunk(c, s, wb);
+      const int wrow0 = __builtin_amdgcn_readfirstlane((int)(j0s[s] - p.win_pos0));  // window source row of wj = 0
 #pragma unroll
       for (int e = 0; e < QPW; ++e) {
-        const int wj = kb0 - n_ent_chunks * 32 + e;
-        rows[e] = (c < n_chunks && wj < n_wk) ? win_row0 + wj : -1;
+        const int wj = wb + 8 * hq + wave * QPW + e;
+        rows[e] = (c < n_chunks && wj < nwks[s]) ? wrow0 + wj : -1;
       }
     }
   };
@@ -764,8 +777,9 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
       if (MODE == 2) v = e < n_ent_tok;
       else v = Is[e] >= 0;  // e < kpad; the padding is -1
     } else if (c < n_chunks) {
-      const int wj = (c - n_ent_chunks) * 32 + kk;
-      v = wj >= wlo && wj <= whi;
+      int s, wb;
+      win_chunk(c, s, wb);
+      v = s == tw && wb + kk < nwks[s];
     }
     return (uint32_t)__builtin_amdgcn_ballot_w64(v && lane < 32);
   };
@@ -792,23 +806,27 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     if constexpr (NW > 1) __syncthreads();
   };
   // Window chunk c: rotate its rows in place in the ring (dims 64..127 of
-  // each key at its position j = t - d).  R(j) = R(t) R(-d) with d in
-  // [0, 127] taken in fp32 on the hardware sin/cos.  The 32 rows x 8 pieces
+  // each key at its position j = t_s - d, t_s the token of the chunk's
+  // slot).  R(j) = R(t_s) R(-d) with d in [0, 127] taken in fp32 on the
+  // hardware sin/cos.  The 32 rows x 8 pieces
   // of 16 bytes are shared out over the work-group; the caller synchronises.
   auto rotate_window = [&](int c, int slot) {
     for (int pi = tid; pi < 256; pi += 64 * NW) {
       const int r = pi >> 3, rp = pi & 7;
       uint8_t* ptr = &Ks[slot][0] + r * 256 + (((8 + rp) ^ (r & 15)) << 4);
       u32x4 w = *(const u32x4*)ptr;
-      const float d = (float)(dt0 - ((c - n_ent_chunks) * 32 + ring_key(r)));
+      int s, wb;
+      win_chunk(c, s, wb);
+      // d = t_s - j: the slot's own token, as in a one-token work-group
+      const float d = (float)((int)(t0 + s - j0s[s]) - (wb + ring_key(r)));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int f = rp * 4 + e;
         float rv = d * Rv[f];
         rv = rv - __builtin_floorf(rv);
         const float sd = __builtin_amdgcn_sinf(rv), cd = __builtin_amdgcn_cosf(rv);
-        const float2 rt = Rt[0][f];
-        const float cs = rt.x * cd + rt.y * sd, sn = rt.y * cd - rt.x * sd;  // angle t0 - d
+        const float2 rt = Rt[s][f];
+        const float cs = rt.x * cd + rt.y * sd, sn = rt.y * cd - rt.x * sd;  // angle t_s - d = j
         const float a0 = bf16lo(w[e]), a1 = bf16hi(w[e]);
         w[e] = pack_bf16(a0 * cs - a1 * sn, a0 * sn + a1 * cs);
       }
@@ -828,9 +846,12 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
   // without a sink.  The pass seeds the S accumulators with -mref (MFMA C
   // operand) and takes weights exp2(S) with no per-chunk test.  If on some
   // head the row sum left [2^-100, 2^100) (a weight overflowed, or all
-  // underflowed), a max-only pass sets mref to the exact maximum of the sink
-  // and all scores, after which every weight is <= 1 and the pass reruns.
+  // underflowed), a max-only pass sets that head's mref to the exact maximum
+  // of its sink and scores, after which its weights are <= 1, and the pass
+  // reruns.  The other heads keep their reference and recompute the same
+  // bits, so a head's result never depends on the other heads or tokens.
   float mref[NHT];
+  bool badh[NHT];  // this lane's heads whose row sum left the range
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) mref[ht] = p.sink ? skv[ht] * LOG2E : 0.0f;
   bf16x8 ones;
@@ -869,6 +890,9 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
       issue_rows(c + 2, (slot + 2) % kRing, rows_next);
       chunk_rows(c + 3, rows_next);
       const uint32_t msk = chunk_mask(c);
+      // no key of this chunk is this wave's (another token's window, entries
+      // past the token's count, index padding): it would add exact zeros
+      if (msk == 0u) return;
 
       // ---- S^T = K Q^T - mref; weights exp2
       f32x4 S[2][NHT];
@@ -941,7 +965,10 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     bool bad = false;
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) bad |= !(Lacc[ht][0] < 0x1p100f && Lacc[ht][0] >= 0x1p-100f);
+    for (int ht = 0; ht < NHT; ++ht) {
+      badh[ht] = !(Lacc[ht][0] < 0x1p100f && Lacc[ht][0] >= 0x1p-100f);
+      bad |= badh[ht];
+    }
     return any_wave(__builtin_amdgcn_ballot_w64(bad) != 0);
   };
   // max-only pass: mref = max(sink logit, every valid score) per head
@@ -986,7 +1013,10 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // every wave is done with the ring before the rerun refills it
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) mref[ht] = fmaxf(max_over_groups(m[ht]), -1e30f);
+    for (int ht = 0; ht < NHT; ++ht) {
+      const float mx = fmaxf(max_over_groups(m[ht]), -1e30f);
+      if (badh[ht]) mref[ht] = mx;
+    }
   };
   if (run()) {
     run_max();
@@ -1055,10 +1085,10 @@ static hipError_t launch_ring(const AttendParams& p, hipStream_t stream) {
 // likewise, with M the largest part reference; then normalise, inverse
 // RoPE, store bf16.
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p) {
-  const int64_t tok = blockIdx.x >> 3;
+  const int64_t tok = p.tok0 + (blockIdx.x >> 3);
   const int h = (int)(blockIdx.x & 7) * 8 + (threadIdx.x >> 5), d0 = (threadIdx.x & 31) * 4;
   if (h >= p.H) return;
-  const float* w0 = p.ws + tok * p.parts * kAttendPartFloats;
+  const float* w0 = p.ws + (tok - p.tok0) * p.parts * kAttendPartFloats;
   float M = -__builtin_inff();
   for (int q = 0; q < p.parts; ++q) M = fmaxf(M, w0[q * kAttendPartFloats + 64 * 128 + h]);
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1092,21 +1122,30 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p) {
 }
 
 template <int MODE>
-static hipError_t launch_mode(const AttendParams& p, hipStream_t stream) {
-  const int nht = (p.H + 15) / 16;
-  const bool split = (MODE == 1 || MODE == 3) && p.ws != nullptr && p.parts > 1;
-  dim3 grid((unsigned)((int64_t)p.B * p.n * (split ? p.parts : 1))), block(64);
+static hipError_t launch_mode(const AttendParams& p_in, hipStream_t stream) {
+  const int nht = (p_in.H + 15) / 16;
+  const bool split = (MODE == 1 || MODE == 3) && p_in.ws != nullptr && p_in.parts > 1;
+  const int64_t bn = (int64_t)p_in.B * p_in.n;
   if (split) {
-    switch (nht) {
-      case 1: hipLaunchKernelGGL((attend_kernel<1, MODE, true>), grid, block, 0, stream, p); break;
-      case 2: hipLaunchKernelGGL((attend_kernel<2, MODE, true>), grid, block, 0, stream, p); break;
-      case 3: hipLaunchKernelGGL((attend_kernel<3, MODE, true>), grid, block, 0, stream, p); break;
-      case 4: hipLaunchKernelGGL((attend_kernel<4, MODE, true>), grid, block, 0, stream, p); break;
-      default: return hipErrorInvalidValue;
+    // blocks of at most kAttendSplitTokens tokens through the workspace, in order
+    AttendParams p = p_in;
+    for (int64_t tok0 = 0; tok0 < bn; tok0 += kAttendSplitTokens) {
+      const int64_t cnt = bn - tok0 < kAttendSplitTokens ? bn - tok0 : kAttendSplitTokens;
+      p.tok0 = tok0;
+      dim3 grid((unsigned)(cnt * p.parts)), block(64);
+      switch (nht) {
+        case 1: hipLaunchKernelGGL((attend_kernel<1, MODE, true>), grid, block, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((attend_kernel<2, MODE, true>), grid, block, 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((attend_kernel<3, MODE, true>), grid, block, 0, stream, p); break;
+        case 4: hipLaunchKernelGGL((attend_kernel<4, MODE, true>), grid, block, 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+      }
+      hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)(cnt * 8)), dim3(256), 0, stream, p);
     }
-    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)((int64_t)p.B * p.n * 8)), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
+  const AttendParams& p = p_in;
+  dim3 grid((unsigned)bn), block(64);
   switch (nht) {
     case 1: hipLaunchKernelGGL((attend_kernel<1, MODE>), grid, block, 0, stream, p); break;
     case 2: hipLaunchKernelGGL((attend_kernel<2, MODE>), grid, block, 0, stream, p); break;
@@ -1117,24 +1156,30 @@ static hipError_t launch_mode(const AttendParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// FP8 or NVFP4 entries with few query rows: one work-group per token would leave most
-// CUs idle, so each token's chunks are split over several work-groups.
-static int attend_parts(int mode, int B, int n, int k, int n_win) {
-  if ((mode != 1 && mode != 3) || (int64_t)B * n > 512) return 1;
+// FP8 or NVFP4 entries over long key lists: each token's chunks are split
+// over several work-groups (decode: one work-group per token would leave
+// most CUs idle).  The choice depends on the token's own key count only, so
+// a token's result is the same whatever else is in the call.
+static int attend_parts(int mode, int k, int n_win) {
+  if (mode != 1 && mode != 3) return 1;
   const int chunks = (k + 31) / 32 + (n_win + 31) / 32;
   if (chunks < 2 * kAttendChunksPerPart) return 1;
   return (chunks + kAttendChunksPerPart - 1) / kAttendChunksPerPart;
 }
 
 size_t attend_workspace(int mode, int B, int n, int k, int n_win) {
-  const int parts = attend_parts(mode, B, n, k, n_win);
-  return parts > 1 ? (size_t)B * n * parts * kAttendPartFloats * sizeof(float) : 0;
+  const int parts = attend_parts(mode, k, n_win);
+  if (parts <= 1) return 0;
+  int64_t bn = (int64_t)B * n;
+  if (bn > kAttendSplitTokens) bn = kAttendSplitTokens;
+  return (size_t)bn * parts * kAttendPartFloats * sizeof(float);
 }
 
 hipError_t launch_attend(const AttendParams& p_in, int mode, hipStream_t stream) {
   if ((int64_t)p_in.B * p_in.n == 0) return hipSuccess;
   AttendParams p = p_in;
-  p.parts = attend_parts(mode, p.B, p.n, p.k, p.n_win);
+  p.parts = attend_parts(mode, p.k, p.n_win);
+  p.tok0 = 0;
   p.cpp = kAttendChunksPerPart;
   switch (mode) {
     case 0: return launch_ring<0>(p, stream);

@@ -89,7 +89,6 @@ struct TopkSmem {
   uint2 cand[QT][kCap];       // {fp32 score bits, entry}; samples in phase 1; output bitmap at the end
   uint32_t hist[2][QT][256];  // double-buffered radix histograms, one per token group
   uint32_t xchg[kWaves][2];   // per-wave values read by the other group members
-  int kept[QT][kWaves];       // kept candidates per (token, region)
   int gdone[2][QT];           // radix selection finished, per token group (double-buffered)
   int wcnt[kWaves][QT];       // candidates per (wave, token) region
   float thr[QT];
@@ -432,6 +431,67 @@ __device__ void wg_bitonic_sort(TopkSmem<QT>& sm, int j, int cnt) {
 }
 
 // ----------------------------------------------------------------------------
+// Ascending output of a token group's kept indices (ir[sl] where bit sl of
+// keep is set; every kept index is < nvj).  The entry range is covered in
+// segments of kSegBits entries: the group marks its kept indices in a bitmap
+// held in its token's (now free) candidate buffer, counts the marks of each
+// lane's words, and every lane writes the indices of its marks at its offset.
+// Every wave of the work-group calls it (it synchronises the work-group);
+// groups of rows past n pass live = false and write nothing.
+constexpr int kSegBits = kCap * 64;  // bits in a token's candidate buffer
+
+template <int QT, int NS>
+__device__ void emit_ascending(TopkSmem<QT>& sm, bool live, const uint32_t (&ir)[NS], uint32_t keep, int nvj,
+                               int nv_all, int32_t* o) {
+  constexpr int G = Shape<QT>::W / QT;
+  constexpr int GL = G * 64;  // lanes of the group
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = wave % QT, h = wave / QT;
+  const int gl = h * 64 + lane;
+  uint32_t* bm = (uint32_t*)&sm.cand[j][0];
+  int out0 = 0;  // indices written by the previous segments
+  for (int s0 = 0; s0 < nv_all; s0 += kSegBits) {
+    int len = live ? nvj - s0 : 0;
+    len = len < 0 ? 0 : (len > kSegBits ? kSegBits : len);
+    const int nw = (len + 31) >> 5;
+    for (int w = gl; w < nw; w += GL) bm[w] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      const uint32_t e = ir[sl] - (uint32_t)s0;
+      if (((keep >> sl) & 1u) && e < (uint32_t)len) atomicOr(&bm[e >> 5], 1u << (e & 31u));
+    }
+    __syncthreads();
+    // lane gl takes words [gl * wpl, (gl + 1) * wpl)
+    const int wpl = (nw + GL - 1) / GL;
+    const int w0 = gl * wpl, w1 = min(w0 + wpl, nw);
+    uint32_t cnt = 0u;
+    for (int w = w0; w < w1; ++w) cnt += __builtin_popcount(bm[w]);
+    const uint32_t incl = wave_prefix_sum(cnt);
+    if (lane == 63) sm.xchg[wave][0] = incl;
+    __syncthreads();
+    uint32_t before = 0u, total = 0u;
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+      const uint32_t tm = sm.xchg[j + QT * m][0];
+      before += m < h ? tm : 0u;
+      total += tm;
+    }
+    int pos = out0 + (int)(before + incl - cnt);
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bits = bm[w];
+      while (bits) {
+        const int bit = __builtin_ctz(bits);
+        o[pos++] = s0 + 32 * w + bit;
+        bits &= bits - 1u;
+      }
+    }
+    out0 += (int)total;
+    __syncthreads();  // the bitmap and the counts are reused by the next segment
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Scores of one 32-column tile for the work-group's tokens.  Lane column
 // lane % 32 is entry e (any entry index; e >= N gives a zero column).
 
@@ -645,11 +705,6 @@ __device__ __forceinline__ void init_scorer(Scorer<FMT>& sc, const IndexParams& 
   }
 }
 
-// Token groups that took the exact streaming fallback (this device), for
-// diagnostics: the sampled threshold normally leaves between k and kCap
-// candidates.
-__device__ unsigned long long g_fallbacks;
-
 // Workspace row of the split path (few query rows over long entry lists):
 // the row's threshold, then the candidates the partitions append.
 struct SplitRow {
@@ -658,6 +713,7 @@ struct SplitRow {
   int pad[2];
   uint2 cand[kCap];
 };
+static_assert(sizeof(SplitRow) == kSplitRowBytes, "split workspace row size");
 
 // SPLIT 0: the whole selection.  SPLIT 1: only the threshold of each token
 // row, written to its workspace row.  SPLIT 2: the exact selection among the
@@ -927,7 +983,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
 
   if (sm.fallback) {
     // ---- exact streaming fallback for every token of this work-group
-    if (tid == 0) atomicAdd(&g_fallbacks, 1ull);
+    if (tid == 0 && p.fallback_count) atomicAdd(p.fallback_count, 1u);
     if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = __uint_as_float(0u); }
     __syncthreads();
     for (int base = 0; base < maxnv; base += kTile) {
@@ -1018,48 +1074,14 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
       if (need_ties && kr[sl] == ro.T) kp = ~ir[sl] >= tinv;
       keep |= (kp ? 1u : 0u) << sl;
     }
-    // output: the kept entries region by region (regions 0..kWaves-1 of the
-    // token, each in its append order), padded with -1
+    // output: the kept indices in ascending order, then -1 padding
+    int maxnv_live = 0;
 #pragma unroll
-    for (int rr = 0; rr < QT; ++rr) {
-      int cnt = 0;
-#pragma unroll
-      for (int m = 0; m < kPer; ++m) cnt += __builtin_popcountll(ballot((keep >> (rr * kPer + m)) & 1u));
-      if (lane == 0) sm.kept[j][grp_h * QT + rr] = cnt;
-    }
-    __syncthreads();
-    if (live) {
-      int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
-      int pos = 0;
-      for (int w = 0; w < grp_h * QT; ++w) pos += sm.kept[j][w];
-#pragma unroll
-      for (int rr = 0; rr < QT; ++rr) {
-#pragma unroll
-        for (int m = 0; m < kPer; ++m) {
-          const int sl = rr * kPer + m;
-          const bool kp = (keep >> sl) & 1u;
-          const uint64_t bal = ballot(kp);
-          const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-          if (SPLIT == 2) {
-            if (kp && pos + rank < kCap) sm.cand[0][pos + rank].y = ir[sl];  // staged for sorting
-          } else {
-            if (kp && pos + rank < p.k) o[pos + rank] = (int32_t)ir[sl];
-          }
-          pos += __builtin_popcountll(bal);
-        }
-      }
-      if (SPLIT != 2)
-        for (int i = kk + grp_h * 64 + lane; i < p.k; i += G * 64) o[i] = -1;
-    }
-    if constexpr (SPLIT == 2) {
-      // the candidates arrived in atomic order: sort the kept indices so
-      // the output is the same on every run
-      __syncthreads();
-      wg_bitonic_sort(sm, 0, kk);
-      int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
-      for (int i = tid; i < p.k; i += kThreads) o[i] = i < kk ? (int32_t)sm.cand[0][i].y : -1;
-    }
+    for (int jj = 0; jj < QT; ++jj) maxnv_live = max(maxnv_live, q0 + jj < p.n ? nv[jj] : 0);
+    int32_t* o = p.idx_out + ((int64_t)b * p.n + (live ? q : 0)) * p.k;
+    emit_ascending<QT, NS>(sm, live, ir, keep, nv[j], maxnv_live, o);
+    if (live)
+      for (int i = kk + grp_h * 64 + lane; i < p.k; i += G * 64) o[i] = -1;
   }
 }
 
@@ -1118,20 +1140,13 @@ __global__ __launch_bounds__(256) void index_split_score_kernel(IndexParams p, i
 // Few query rows over long entry lists (decode): the split path keeps every
 // CU busy (threshold per row, entries scored by partitions, selection per row).
 constexpr int kSplitPart = 8192;
+// The choice depends on the rows of one batch entry only, never on B.
 static bool split_path(int B, int n, int64_t q_pos0, int N, int m) {
-  if (n > 4 || (int64_t)B * n > 512) return false;
+  (void)B;
+  if (n > 4) return false;
   int64_t nv = (q_pos0 + n) / m;
   if (nv > N) nv = N;
   return nv >= 65536;
-}
-
-hipError_t index_topk_fallbacks(unsigned long long* count, bool reset) {
-  hipError_t e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_fallbacks), sizeof(*count), 0, hipMemcpyDeviceToHost);
-  if (e == hipSuccess && reset) {
-    const unsigned long long z = 0;
-    e = hipMemcpyToSymbol(HIP_SYMBOL(g_fallbacks), &z, sizeof(z), 0, hipMemcpyHostToDevice);
-  }
-  return e;
 }
 
 size_t index_topk_workspace(int B, int n, int64_t q_pos0, int N, int m, int) {

@@ -70,12 +70,14 @@ struct AttendParams {
   // take `cpp` chunks each and leave partial results in ws
   float* ws;
   int parts, cpp;
+  int64_t tok0;  // split path: first token of the launch's block
 };
 
 // Workspace of the split decode path: per (token, part) the unnormalised
 // O[64][128], then the softmax reference and the row sum of each head.
 constexpr int kAttendPartFloats = 64 * 128 + 2 * 64;
 constexpr int kAttendChunksPerPart = 8;
+constexpr int kAttendSplitTokens = 512;  // tokens per split launch (bounds the workspace)
 size_t attend_workspace(int mode, int B, int n, int k, int n_win);
 
 // mode: 0 = CSA with bf16 entries, 1 = CSA with fp8+bf16 entries, 2 = HCA,
@@ -106,11 +108,14 @@ struct IndexParams {
   int32_t* idx_out;          // [B, n, k]
   void* ws;
   size_t ws_bytes;
+  uint32_t* fallback_count;  // caller-owned device counter or null
 };
 
 hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream);
 size_t index_topk_workspace(int B, int n, int64_t q_pos0, int N, int m, int k);
-hipError_t index_topk_fallbacks(unsigned long long* count, bool reset);
+
+// Workspace row of the indexer's split path.
+constexpr size_t kSplitRowBytes = 32784;
 
 // bf16 GEMM C = A . B^T (A [M, K] rows lda apart, B [N, K] rows ldb apart,
 // fp32 accumulation; K a multiple of 32).  Output column c (plus z * c_zcol

@@ -91,7 +91,7 @@ def test_compress_empty_is_ok(L):
 def _index(L, **kw):
     a = dict(qidx=FAKE, qidx_scale=None, widx=FAKE, kidx=FAKE, kidx_scale=FAKE, fmt=1, B=1, n=16,
              q_pos0=0, H_I=8, d_idx=64, N=4, m=4, k=16, idx_out=FAKE2, ws=None, ws_bytes=0,
-             stream=None)
+             fallback_count=None, stream=None)
     a.update(kw)
     return L.csa_index_topk(*a.values())
 
@@ -111,6 +111,7 @@ def _index(L, **kw):
     (dict(kidx_scale=None), "kidx_scale"),
     (dict(kidx=MIS), "aligned"),
     (dict(n=-1), "n=-1"),
+    (dict(fallback_count=FAKE + 2), "fallback_count"),
 ])
 def test_index_rejects(L, kw, needle):
     assert _index(L, **kw) == _lib.CSA_INVALID_ARG
@@ -124,6 +125,8 @@ def test_index_workspace_query(L):
     assert L.csa_index_topk_workspace_bytes(2, 4, 4 * 70000 - 4, 90000, 4, 2048) == 8 * 32784
     assert L.csa_index_topk_workspace_bytes(1, 5, 4 * 70000, 90000, 4, 2048) == 0     # too many rows
     assert L.csa_index_topk_workspace_bytes(64, 1, 4 * 60000, 262144, 4, 2048) == 0  # too few visible
+    # the path depends on the rows of one batch entry, not on B
+    assert L.csa_index_topk_workspace_bytes(600, 1, 4 * 262144, 262144, 4, 2048) == 600 * 32784
 
 
 def test_index_rejects_small_or_misaligned_workspace(L):
@@ -153,6 +156,8 @@ def _attend(L, **kw):
     (dict(entry_fmt=2), "FP8 entries"),
     (dict(rope_dims=16), "rope_dims"),
     (dict(n_win=-1), "n_win"),
+    (dict(n_win=129), "n_win=129"),
+    (dict(win_fmt=5, rope_dims=0), "pre-rotated window"),
     (dict(q=None), "non-NULL"),
     (dict(idx=None), "idx is NULL"),
     (dict(entries=None), "entries is NULL"),
@@ -247,12 +252,14 @@ def test_cache_append_needs_no_cache_between_blocks(L):
 
 
 def test_attend_workspace_query(L):
-    # bf16 entries never split; FP8 entries with few rows and >= 16 chunks do
+    # bf16 entries never split; FP8 and NVFP4 entries with >= 16 chunks do,
+    # whatever B and n are (tokens run in blocks of at most 512)
     assert L.csa_attend_workspace_bytes(64, 1, 2048, 128, 0) == 0
     assert L.csa_attend_workspace_bytes(64, 1, 2048, 128, 2) == 64 * 9 * 33280
     assert L.csa_attend_workspace_bytes(64, 1, 512, 128, 2) == 64 * 3 * 33280  # 20 chunks
     assert L.csa_attend_workspace_bytes(64, 1, 64, 128, 2) == 0       # 6 chunks: one work-group
-    assert L.csa_attend_workspace_bytes(600, 1, 2048, 128, 2) == 0    # enough rows already
+    assert L.csa_attend_workspace_bytes(600, 1, 2048, 128, 2) == 512 * 9 * 33280
+    assert L.csa_attend_workspace_bytes(2, 4096, 2048, 128, 3) == 512 * 9 * 33280
 
 
 def test_attend_rejects_small_workspace(L):
@@ -333,3 +340,4 @@ def test_binding_checks_the_entry_row_width():
     ent = torch.zeros((1, 16, 64), dtype=torch.uint8)
     with pytest.raises(ValueError, match="nvfp4"):
         Lb.csa_attend(q, ent, torch.zeros((1, 1, 4), dtype=torch.int32), entry_scale=torch.zeros((1, 16)))
+

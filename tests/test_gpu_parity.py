@@ -102,21 +102,24 @@ def _index_case(orc, rng, B, n, N, H_I, k, q_pos0, fmt, m=4, dup_rows=0, prequan
         kdec = orc.bf16_to_f64(kc).astype(np.float32)
         kdev, ksdev = dev(kc), None
     qdec = oracle_q_dec(orc, q, fmt)
-    L.csa_index_topk_fallbacks(reset=True)
+    fc = torch.zeros(1, dtype=torch.int32, device="cuda")
     if prequant:
         qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(q).astype(np.float32))
         got = L.csa_index_topk(dev(qc), dev(w), kdev, k, m, q_pos0=q_pos0, fmt=fmt,
-                               qidx_scale=dev(qs), kidx_scale=ksdev)
+                               qidx_scale=dev(qs), kidx_scale=ksdev, fallback_count=fc)
     else:
-        got = L.csa_index_topk(dev(q), dev(w), kdev, k, m, q_pos0=q_pos0, fmt=fmt, kidx_scale=ksdev)
+        got = L.csa_index_topk(dev(q), dev(w), kdev, k, m, q_pos0=q_pos0, fmt=fmt, kidx_scale=ksdev,
+                               fallback_count=fc)
     torch.cuda.synchronize()
-    nfb = L.csa_index_topk_fallbacks()
+    nfb = int(fc.item())
     # the sampled threshold leaves between k and 4096 candidates on untied
     # scores; the exact streaming path is for massive ties only
     if fallback is not None:
         assert (nfb > 0) == fallback, "%d work-groups took the exact streaming path" % nfb
     got = host(got)
     rows = np.arange(n, dtype=np.int32)
+    # every row: ascending indices, then the -1 padding
+    assert np.array_equal(got, canon_idx(got)), "rows are not in ascending order"
     for b in range(B):
         ref = orc.index_topk_rows(qdec[b], w[b], kdec[b], m, q_pos0, rows, k)
         if fmt == "mxfp4":
@@ -158,15 +161,38 @@ def test_index_topk_matches_oracle(orc, B, n, N, H_I, k, q_pos0, fmt, extra):
 
 # ----------------------------------------------------------------- attention --
 
+def _with_offset(rng, shape, scale, offset):
+    """bf16 N(0,1) * scale draws, plus `offset` on dim 0 (not rotated)."""
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    x[..., 0] += np.float32(offset)
+    return synth.to_bf16_bits(x)
+
+
 def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True, q_scale=1.0,
-                 efmt="bf16", kv_scale=None, sink_shift=0.0, check_rows=None, wfmt="bf16"):
+                 efmt="bf16", kv_scale=None, sink_shift=0.0, check_rows=None, wfmt="bf16",
+                 kv_offset=0.0, q_offset=0.0, sink_heads=None, forced_rerun=None):
+    """One attention call against the oracle.  kv_offset / q_offset add a
+    constant to dim 0 of every raw KV row / query row; sink_heads (a boolean
+    mask over heads) applies sink_shift to those heads only.  forced_rerun
+    "overflow" / "underflow" asserts from the inputs that every checked row
+    sum leaves [2^-100, 2^100) against the kernel's first reference (the
+    sink logit; 0 without a sink), so the max-only pass must run."""
     rng = np.random.default_rng(seed)
     T = q_pos0 + n
     kv_scale = kv_scale or 1 / np.sqrt(128)
-    kv = _bf16(rng, (B, T, 128), kv_scale)
-    q = _bf16(rng, (B, n, H, 128), q_scale / np.sqrt(128))
+    if kv_offset:
+        kv = _with_offset(rng, (B, T, 128), kv_scale, kv_offset)
+    else:
+        kv = _bf16(rng, (B, T, 128), kv_scale)
+    if q_offset:
+        q = _with_offset(rng, (B, n, H, 128), q_scale / np.sqrt(128), q_offset)
+    else:
+        q = _bf16(rng, (B, n, H, 128), q_scale / np.sqrt(128))
     beta = rng.standard_normal(2 * m if mode == "csa" else m).astype(np.float32)
-    sk = (rng.standard_normal(H) + sink_shift).astype(np.float32) if sink else None
+    sk = None
+    if sink:
+        sh = sink_shift if sink_heads is None else np.where(sink_heads, sink_shift, 0.0)
+        sk = (rng.standard_normal(H) + sh).astype(np.float32)
     ents = [oracle_compress_store(orc, kv[b], beta, m, 1 if mode == "csa" else 0, entry_fmt=efmt)
             for b in range(B)]
     N = ents[0]["entries_f64"].shape[0]
@@ -210,6 +236,8 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
     got = host_bits(out)
     if check_rows is not None:
         rows = np.asarray(check_rows, np.int32)
+    if forced_rerun:
+        _assert_rerun_forced(forced_rerun, q, kv, ents, sk, rows, heads=sink_heads)
     for b in range(B):
         wkw = dict(win=kv[b] if n_win else None)
         if win8 is not None:
@@ -223,6 +251,29 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
     return got
 
 
+def _assert_rerun_forced(kind, q, kv, ents, sk, rows, heads=None):
+    """Bounds from the inputs alone.  Dim 0 is never rotated and the rotation
+    keeps the norm of the rest, so every logit lambda = <q~, key> / sqrt(128)
+    lies within (q_0 key_0 +- |q_1..| |key_1..|) / sqrt(128).  overflow:
+    every key's weight against the sink logit is above 2^100, so a row sum
+    is too.  underflow (no sink, reference 0): every logit is below
+    -80, so the row sum (at most 2^12 keys) is below 2^-100."""
+    keys = [np.concatenate([e["entries_f64"], bf16_f64(kv[b])]) for b, e in enumerate(ents)]
+    for b, kb in enumerate(keys):
+        qb = bf16_f64(q[b][rows])                       # [r, H, 128]
+        qn = np.linalg.norm(qb[..., 1:], axis=-1)       # [r, H]
+        kn = np.linalg.norm(kb[:, 1:], axis=-1)         # [keys]
+        if kind == "overflow":
+            lo = (-np.abs(qb[..., 0])[..., None] * np.abs(kb[:, 0]) - qn[..., None] * kn) / np.sqrt(128)
+            margin = lo.min(axis=-1) - sk[None, :]      # log weight of the weakest key
+            sel = margin if heads is None else margin[:, heads]
+            assert sel.min() > 100 * np.log(2), sel.min()
+        else:
+            assert sk is None
+            hi = (qb[..., 0][..., None] * kb[None, None, :, 0] + qn[..., None] * kn) / np.sqrt(128)
+            assert hi.max() < -80, hi.max()
+
+
 @pytest.mark.parametrize("case", [
     dict(B=2, n=77, H=64, q_pos0=50, m=4, mode="csa", k=37),
     dict(B=1, n=64, H=8, q_pos0=300, m=4, mode="csa", k=64, q_scale=24.0),     # sharp logits
@@ -232,9 +283,32 @@ def _attend_case(orc, seed, B, n, H, q_pos0, m, mode, k=0, n_win=128, sink=True,
     dict(B=1, n=300, H=16, q_pos0=0, m=8, mode="hca"),
     dict(B=1, n=129, H=64, q_pos0=2000, m=128, mode="hca", q_scale=24.0),
     dict(B=2, n=40, H=24, q_pos0=700, m=16, mode="hca", n_win=0, sink=False),
-    # sink far below the scores: weights exceed the sink reference by > 2^64,
-    # which forces the restart with a larger reference
+    # sink 60 below the scores: weights up to ~2^94 against the sink
+    # reference (the bf16 ring kernel stays in range; the FP8 kernel's kSlack
+    # restart is what this exercises in the cases further down)
     dict(B=1, n=20, H=32, q_pos0=300, m=4, mode="csa", k=40, sink_shift=-60.0, q_scale=24.0),
+    # the ring kernel's max-only rerun: row sums above 2^100 (sink 80 below
+    # scores near 0) -- CSA over raw and pre-rotated windows, HCA
+    dict(B=2, n=45, H=64, q_pos0=300, m=4, mode="csa", k=40, sink_shift=-80.0, forced_rerun="overflow"),
+    dict(B=1, n=45, H=64, q_pos0=300, m=4, mode="csa", k=40, sink_shift=-80.0, wfmt="roped",
+         forced_rerun="overflow"),
+    dict(B=1, n=60, H=40, q_pos0=900, m=8, mode="hca", sink_shift=-80.0, forced_rerun="overflow"),
+    # ... and row sums below 2^-100: no sink, every logit below -80 (keys
+    # share +1 on dim 0, queries -1500 there)
+    dict(B=1, n=40, H=64, q_pos0=300, m=4, mode="csa", k=40, sink=False, kv_offset=1.0, q_offset=-1500.0,
+         forced_rerun="underflow"),
+    dict(B=1, n=40, H=32, q_pos0=300, m=4, mode="csa", k=40, sink=False, kv_offset=1.0, q_offset=-1500.0,
+         wfmt="roped", forced_rerun="underflow"),
+    dict(B=1, n=50, H=64, q_pos0=900, m=8, mode="hca", sink=False, kv_offset=1.0, q_offset=-1500.0,
+         forced_rerun="underflow"),
+    # only some heads out of range: those rerun, the others keep their pass
+    dict(B=1, n=30, H=64, q_pos0=300, m=4, mode="csa", k=40, sink_shift=-80.0,
+         sink_heads=np.arange(64) % 3 == 0, forced_rerun="overflow"),
+    # sharp logits (q x 128: logit std ~ 1) on the ring kernels
+    dict(B=2, n=77, H=64, q_pos0=50, m=4, mode="csa", k=37, q_scale=128.0),
+    dict(B=1, n=77, H=64, q_pos0=500, m=4, mode="csa", k=64, q_scale=128.0, wfmt="roped"),
+    dict(B=1, n=200, H=64, q_pos0=1000, m=8, mode="hca", q_scale=128.0),
+    dict(B=1, n=100, H=16, q_pos0=1000, m=8, mode="hca", q_scale=128.0, wfmt="roped"),
     # FP8 entries with few query rows: each token's 20 chunks are split over
     # 3 work-groups and merged
     dict(B=3, n=2, H=64, q_pos0=2200, m=4, mode="csa", k=512, efmt="fp8", kv_scale=1.0),
@@ -289,7 +363,8 @@ def test_rope_rows_matches_oracle(orc, B, T, pos0):
         assert np.array_equal(got[b], orc.rope_rows_bf16(kv[b], pos0))
 
 
-def test_attend_deterministic_and_batch_invariant(orc):
+def test_attend_deterministic(orc):
+    """Run to run bit-identity of one call (batch invariance: test_gpu_invariance.py)."""
     a = _attend_case(orc, 5, B=2, n=40, H=32, q_pos0=100, m=4, mode="csa", k=20)
     b = _attend_case(orc, 5, B=2, n=40, H=32, q_pos0=100, m=4, mode="csa", k=20)
     assert np.array_equal(a, b)
