@@ -221,6 +221,25 @@ int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* wid
 size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m, int k);
 
 /*
+ * csa_index_topk_noalloc -- csa_index_topk for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without ws / ws_bytes, the same
+ * kernels and results.  The split path's workspace is a static device array
+ * of 8 MiB that every GPU the library runs on holds until the process ends
+ * (256 query rows of the split path: B * n <= 256 when n <= 4 and a row sees
+ * at least 65536 entries).  A call that would need more returns
+ * CSA_WORKSPACE_TOO_SMALL and launches nothing.  The first call on a device
+ * looks up the array's address there (no allocation); nothing is allocated,
+ * freed or synchronised.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (different streams, or host threads) race
+ * and must be ordered by the caller.
+ */
+int csa_index_topk_noalloc(const void* qidx, const uint8_t* qidx_scale, const float* widx,
+                           const void* kidx, const uint8_t* kidx_scale, int fmt,
+                           int B, int n, int64_t q_pos0, int H_I, int d_idx, int N, int m, int k,
+                           int32_t* idx_out, uint32_t* fallback_count, void* stream);
+
+/*
  * csa_attend -- CSA core attention: sparse entries + sliding window + sink.
  * "deepseek V4 技术论文" 1.1 (each query attends to its top-k entries; the
  * entries are both key and value, shared by all heads: MQA), wiki summary

@@ -17,7 +17,7 @@ import torch
 from ._lib import (FMT_BF16, FMT_BF16_ROPED, FMT_FP8, FMT_FP8_ROPE_BF16, FMT_MXFP4, FMT_NVFP4, CsaError, check,
                    lib)
 
-__all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_attend", "hca_attend",
+__all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_noalloc", "csa_attend", "hca_attend",
            "csa_project_in", "csa_project_qidx", "csa_project_out", "csa_rope_rows", "version",
            "CsaError",
            "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16", "FMT_NVFP4", "FMT_FP8"]
@@ -127,6 +127,20 @@ def csa_index_topk(qidx, widx, kidx, k, m, q_pos0=0, fmt="mxfp4", qidx_scale=Non
         _ptr(qidx), _ptr(qidx_scale), _ptr(widx), _ptr(kidx), _ptr(kidx_scale), f, B, n,
         int(q_pos0), H_I, 64, N, m, k, _ptr(idx_out), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _ptr(fallback_count), _stream(stream)))
+    return idx_out
+
+
+def csa_index_topk_noalloc(qidx, widx, kidx, k, m, idx_out, q_pos0=0, fmt="mxfp4", qidx_scale=None,
+                           kidx_scale=None, N=None, fallback_count=None, stream=None):
+    """csa_index_topk without a workspace (csa_index_topk_noalloc): the
+    split path uses the library's static device scratch (at most 256 split
+    rows); the caller passes idx_out and the call allocates nothing."""
+    B, n, H_I = qidx.shape[:3]
+    if N is None:
+        N = kidx.shape[1]
+    check(lib().csa_index_topk_noalloc(
+        _ptr(qidx), _ptr(qidx_scale), _ptr(widx), _ptr(kidx), _ptr(kidx_scale), _fmt(fmt), B, n,
+        int(q_pos0), H_I, 64, N, m, k, _ptr(idx_out), _ptr(fallback_count), _stream(stream)))
     return idx_out
 
 

@@ -24,6 +24,7 @@ FMT_FP8 = 4
 FMT_BF16_ROPED = 5
 
 EXPORTS = ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_workspace_bytes",
+           "csa_index_topk_noalloc",
            "csa_attend", "csa_attend_workspace_bytes", "hca_attend", "csa_project_in",
            "csa_project_qidx", "csa_project_out", "csa_rope_rows", "csa_last_error", "csa_version")
 
@@ -52,6 +53,7 @@ def lib():
                                    P, P, i32, i32, P]
     L.csa_index_topk.argtypes = [P, P, P, P, P, i32, i32, i32, i64, i32, i32, i32, i32, i32, P, P,
                                  sz, P, P]
+    L.csa_index_topk_noalloc.argtypes = [P, P, P, P, P, i32, i32, i32, i64, i32, i32, i32, i32, i32, P, P, P]
     L.csa_index_topk_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.csa_index_topk_workspace_bytes.restype = sz
     L.csa_attend.argtypes = [P, i32, i32, i64, i32, i32, P, P, P, i32, i32, i32, P, i32, P, i64, i32,
@@ -64,7 +66,7 @@ def lib():
     L.csa_project_in.argtypes = [P, i32, i32, P, i32, i32, i32, i32, i32, i32, P, i32, P, P, P, P, P, P, P, P, P]
     L.csa_project_qidx.argtypes = [P, i32, i32, P, i32, P, P, P, P]
     L.csa_project_out.argtypes = [P, i32, i32, i32, i32, P, i32, P, P]
-    for f in ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_attend",
+    for f in ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_noalloc", "csa_attend",
               "hca_attend", "csa_project_in", "csa_project_qidx", "csa_project_out", "csa_rope_rows",
               "csa_version"):
         getattr(L, f).restype = i32

@@ -34,6 +34,7 @@ SOURCES = {
                                 "-mllvm", "-amdgpu-mfma-vgpr-form"],
     # GEMM accumulators in VGPRs; the indexer-query chain is explicit fmas
     "proj.hip": DEVICE + ["-ffp-contract=off"],
+    "scratch.hip": DEVICE,
     "abi.cpp": ["-ffp-contract=off"],
 }
 

@@ -209,7 +209,7 @@ size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m
 
 static int index_common(const void* qidx, const uint8_t* qidx_scale, const float* widx, const void* kidx,
                         const uint8_t* kidx_scale, int fmt, int B, int n, int64_t q_pos0, int H_I, int d_idx, int N,
-                        int m, int k, int32_t* idx_out, void* ws, size_t ws_bytes,
+                        int m, int k, int32_t* idx_out, void* ws, size_t ws_bytes, bool static_ws,
                         uint32_t* fallback_count, void* stream, const char* name) {
   REQUIRE(B >= 0 && n >= 0 && N >= 0, "%s: B=%d n=%d N=%d must be >= 0", name, B, n, N);
   REQUIRE(fmt == CSA_FMT_BF16 || fmt == CSA_FMT_MXFP4, "%s: fmt=%d unsupported", name, fmt);
@@ -225,9 +225,23 @@ static int index_common(const void* qidx, const uint8_t* qidx_scale, const float
   REQUIRE(aligned16(qidx) && aligned16(kidx), "%s: qidx and kidx must be 16-byte aligned", name);
   REQUIRE(((uintptr_t)fallback_count & 3u) == 0, "%s: fallback_count must be 4-byte aligned", name);
   const size_t need = csa::index_topk_workspace(B, n, q_pos0, N, m, k);
-  if (ws_bytes < need)
-    return fail(CSA_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes < %zu needed", name, ws_bytes, need);
-  REQUIRE(need == 0 || (ws != nullptr && aligned16(ws)), "%s: ws must be non-NULL and 16-byte aligned", name);
+  if (static_ws) {
+    if (need > csa::kStaticScratchBytes)
+      return fail(CSA_WORKSPACE_TOO_SMALL,
+                  "%s: the call needs %zu bytes of scratch; the static scratch holds %zu (%zu rows of the split "
+                  "path); use csa_index_topk with a workspace",
+                  name, need, csa::kStaticScratchBytes, csa::kStaticScratchBytes / csa::kSplitRowBytes);
+    ws_bytes = csa::kStaticScratchBytes;
+    ws = nullptr;
+    if (need > 0) {
+      const int st = hip_status(csa::static_scratch(&ws), "csa_index_topk_noalloc (scratch address)");
+      if (st != CSA_OK) return st;
+    }
+  } else {
+    if (ws_bytes < need)
+      return fail(CSA_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes < %zu needed", name, ws_bytes, need);
+    REQUIRE(need == 0 || (ws != nullptr && aligned16(ws)), "%s: ws must be non-NULL and 16-byte aligned", name);
+  }
   csa::IndexParams p{};
   p.q = qidx;
   p.q_scale = (fmt == CSA_FMT_MXFP4) ? qidx_scale : nullptr;
@@ -254,7 +268,15 @@ int csa_index_topk(const void* qidx, const uint8_t* qidx_scale, const float* wid
                    int64_t q_pos0, int H_I, int d_idx, int N, int m, int k, int32_t* idx_out,
                    void* ws, size_t ws_bytes, uint32_t* fallback_count, void* stream) {
   return index_common(qidx, qidx_scale, widx, kidx, kidx_scale, fmt, B, n, q_pos0, H_I, d_idx, N, m, k, idx_out, ws,
-                      ws_bytes, fallback_count, stream, "csa_index_topk");
+                      ws_bytes, false, fallback_count, stream, "csa_index_topk");
+}
+
+int csa_index_topk_noalloc(const void* qidx, const uint8_t* qidx_scale, const float* widx,
+                           const void* kidx, const uint8_t* kidx_scale, int fmt, int B, int n,
+                           int64_t q_pos0, int H_I, int d_idx, int N, int m, int k, int32_t* idx_out,
+                           uint32_t* fallback_count, void* stream) {
+  return index_common(qidx, qidx_scale, widx, kidx, kidx_scale, fmt, B, n, q_pos0, H_I, d_idx, N, m, k, idx_out,
+                      nullptr, 0, true, fallback_count, stream, "csa_index_topk_noalloc");
 }
 
 static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, int H, int D,

@@ -114,8 +114,12 @@ struct IndexParams {
 hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream);
 size_t index_topk_workspace(int B, int n, int64_t q_pos0, int N, int m, int k);
 
-// Workspace row of the indexer's split path.
+// Workspace row of the indexer's split path, and the device scratch of the
+// allocation-free variant: 256 such rows.  static_scratch() gives the
+// scratch's address on the current device.
 constexpr size_t kSplitRowBytes = 32784;
+constexpr size_t kStaticScratchBytes = 256 * kSplitRowBytes;
+hipError_t static_scratch(void** ptr);
 
 // bf16 GEMM C = A . B^T (A [M, K] rows lda apart, B [N, K] rows ldb apart,
 // fp32 accumulation; K a multiple of 32).  Output column c (plus z * c_zcol

@@ -341,3 +341,22 @@ def test_binding_checks_the_entry_row_width():
     with pytest.raises(ValueError, match="nvfp4"):
         Lb.csa_attend(q, ent, torch.zeros((1, 1, 4), dtype=torch.int32), entry_scale=torch.zeros((1, 16)))
 
+
+def _index_noalloc(L, **kw):
+    a = dict(qidx=FAKE, qidx_scale=None, widx=FAKE, kidx=FAKE, kidx_scale=FAKE, fmt=1, B=1, n=16,
+             q_pos0=0, H_I=8, d_idx=64, N=4, m=4, k=16, idx_out=FAKE2, fallback_count=None, stream=None)
+    a.update(kw)
+    return L.csa_index_topk_noalloc(*a.values())
+
+
+def test_index_noalloc_rejects_beyond_the_static_scratch(L):
+    """257 split rows need more than the 8 MiB static scratch: rejected on the
+    host, before any device call; bad arguments are rejected as by
+    csa_index_topk."""
+    assert L.csa_index_topk_workspace_bytes(257, 1, 4 * 70000, 70000, 4, 2048) == 257 * 32784
+    r = _index_noalloc(L, B=257, n=1, q_pos0=4 * 70000, N=70000, k=2048)
+    assert r == _lib.CSA_WORKSPACE_TOO_SMALL
+    assert "static scratch" in _msg(L) and "csa_index_topk_noalloc" in _msg(L)
+    assert _index_noalloc(L, k=0) == _lib.CSA_INVALID_ARG and "k=0" in _msg(L)
+    assert _index_noalloc(L, kidx=MIS) == _lib.CSA_INVALID_ARG
+    assert _index_noalloc(L, B=0) == _lib.CSA_OK

@@ -1,0 +1,43 @@
+"""The allocation-free entry point (csa_index_topk_noalloc) against
+csa_index_topk with a caller workspace, through the C ABI, on two calls in a
+row -- the second with a smaller input -- bit for bit (GPU).  Both calls take
+the split decode path, the one that uses the static scratch."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_21_amd as L
+from long_context_attention_21_amd import synth
+
+from _helpers import dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(orc, seed, B, N):
+    rng = np.random.default_rng(seed)
+    q = synth.to_bf16_bits((rng.standard_normal((B, 1, 8, 64)) / 8).astype(np.float32))
+    w = (rng.standard_normal((B, 1, 8)) / np.sqrt(8)).astype(np.float32)
+    kc, ks = orc.mxfp4_encode((rng.standard_normal((B, N, 64)) / 8).astype(np.float32))
+    return dev(q), dev(w), dev(kc), dev(ks)
+
+
+def test_noalloc_matches_workspace_entry_point(orc):
+    k = 2048
+    for seed, B, N in ((1, 40, 90000), (2, 7, 66000)):  # the second call is smaller
+        print("noalloc case B=%d N=%d" % (B, N), flush=True)
+        assert L._lib.lib().csa_index_topk_workspace_bytes(B, 1, 4 * N, N, 4, k) > 0  # split path
+        q, w, kc, ks = _inputs(orc, seed, B, N)
+        ref = L.csa_index_topk(q, w, kc, k, 4, q_pos0=4 * N, kidx_scale=ks)
+        out = torch.full((B, 1, k), -7, dtype=torch.int32, device="cuda")
+        fc = torch.zeros(1, dtype=torch.int32, device="cuda")
+        L.csa_index_topk_noalloc(q, w, kc, k, 4, out, q_pos0=4 * N, kidx_scale=ks, fallback_count=fc)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), host(ref)), "B=%d N=%d" % (B, N)
+        assert int(fc.item()) == 0
+        # one row against the oracle as well
+        qd = orc.mxfp4_decode(*orc.mxfp4_encode(orc.bf16_to_f64(host(q.view(torch.int16)).view(np.uint16)[B - 1])
+                                                 .astype(np.float32)))
+        r = orc.index_topk_rows(qd, host(w)[B - 1], orc.mxfp4_decode(host(kc)[B - 1], host(ks)[B - 1]), 4, 4 * N,
+                                np.zeros(1, np.int32), k)
+        assert np.array_equal(host(out)[B - 1], r)
