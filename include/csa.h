@@ -42,8 +42,8 @@
  *    query row's result depends only on its own inputs (its query, position
  *    and key set), not on the batch size, the number of rows in the call or
  *    which other rows are in it (batch invariance).  csa_index_topk writes
- *    each row's indices in ascending order, so the attention that consumes
- *    them sees the same key order whatever path selected them.
+ *    each row's indices in one canonical order, so the attention that
+ *    consumes them sees the same key order whatever path selected them.
  */
 #ifndef CSA_MI355X_H
 #define CSA_MI355X_H
@@ -185,7 +185,9 @@ int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new,
  * (exact for MXFP4 operands), the head sum as an fp32 fma chain in
  * ascending h starting from +0.  It keeps the min(k, n_vis) largest scores,
  * ties going to the lower entry index, and writes their indices followed by
- * -1 padding up to k.  The indices of a row are written in ascending order.
+ * -1 padding up to k.  The indices of a row are written in a canonical order
+ * that depends on the selected set only: grouped by (index / 32) % 8, the
+ * groups in ascending order, ascending within each group.
  *
  *  qidx        fmt BF16: [B, n, H_I, 64] bf16.  fmt MXFP4 with
  *              qidx_scale == NULL: [B, n, H_I, 64] bf16, quantised in-kernel

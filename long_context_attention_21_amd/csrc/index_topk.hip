@@ -63,6 +63,10 @@ constexpr int kDepth = 4;              // score tiles in flight per wave
 constexpr int kMinAbove = 256;         // sampled entries expected above the threshold
 constexpr int kList = 512;             // per-member key list after the first radix digit
 
+// Sort key of the canonical row order (see emit_canonical): the 32-entry
+// tile modulo 8, then the entry (entries are below 2^24).
+__device__ __forceinline__ uint32_t canon_key(uint32_t e) { return (((e >> 5) & 7u) << 24) | e; }
+
 // Lane mask of a predicate (the compare result itself, no int round trip).
 __device__ __forceinline__ uint64_t ballot(bool pred) { return __builtin_amdgcn_ballot_w64(pred); }
 
@@ -95,6 +99,8 @@ struct TopkSmem {
   int cnt[QT];
   int fallback;
   int ties;
+  uint32_t vcnt[QT][8];       // kept entries per canonical group (output)
+  int staged;                 // split path: kept entries staged for sorting
   uint32_t sel[4];
 };
 
@@ -306,6 +312,126 @@ __device__ __forceinline__ RadixOut group_radix(TopkSmem<QT>& sm, const uint32_t
 }
 
 // ----------------------------------------------------------------------------
+// Linear-bin selection over a token group's keys (kr[NS] per member lane,
+// 0 = empty slot).  Bins are (key - lo) >> s over the order keys, 256 of
+// them; every member counts its keys into the group's histogram with LDS
+// atomics and scans it alike.  Unlike group_radix it needs no per-slot
+// register masks and spreads the keys over all members.
+
+// extremes of the group's real keys (kmin = 0 when it has none); every wave
+// calls it (one barrier); also clears both histogram buffers of the group
+template <int QT, int NS>
+__device__ __forceinline__ void group_extremes(TopkSmem<QT>& sm, const uint32_t (&kr)[NS], uint32_t& kmin,
+                                               uint32_t& kmax) {
+  constexpr int G = Shape<QT>::W / QT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = wave % QT, h = wave / QT;
+  uint32_t mx = 0u, mn1 = 0xffffffffu;  // mn1 = min(key - 1): empty (0) slots wrap to the top
+#pragma unroll
+  for (int m = 0; m < NS; ++m) {
+    mx = max(mx, kr[m]);
+    mn1 = min(mn1, kr[m] - 1u);
+  }
+  mx = wave_max_dpp(mx);
+  mn1 = wave_min_dpp(mn1);
+  if (lane == 0) { sm.xchg[wave][0] = mx; sm.xchg[wave][1] = mn1; }
+  if (lane < 64 / G) {
+    *(u32x4*)&sm.hist[0][j][h * (256 / G) + 4 * lane] = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)&sm.hist[1][j][h * (256 / G) + 4 * lane] = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  mx = 0u;
+  mn1 = 0xffffffffu;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    mx = max(mx, sm.xchg[j + QT * g][0]);
+    mn1 = min(mn1, sm.xchg[j + QT * g][1]);
+  }
+  kmax = mx;
+  kmin = mn1 + 1u;
+}
+
+// The bin of the r-th largest key within [lo, lo + (256 << s)) counted from
+// `above` keys already known to lie above that range: its index b, its count
+// hb and the count above it (including `above`).  Histogram buffer `buf` of
+// the group must be zero; every wave calls it (one barrier).
+struct BinOut {
+  uint32_t b, hb, above;
+};
+template <int QT, int NS>
+__device__ __forceinline__ BinOut group_bin(TopkSmem<QT>& sm, int buf, const uint32_t (&kr)[NS], uint32_t lo, int s,
+                                            uint32_t r, uint32_t above, bool active) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = wave % QT;
+  uint32_t* hc = sm.hist[buf][j];
+  if (active) {
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+      const uint32_t x = kr[m];
+      if (x != 0u && x >= lo) {
+        const uint32_t d = (x - lo) >> s;
+        if (d < 256u) atomicAdd(&hc[d], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  BinOut o{0u, 0u, above};
+  if (active) {
+    // lane l owns bins 252-4l .. 255-4l: a prefix sum over lanes counts the
+    // keys in bins >= the lane's lowest bin
+    const u32x4 hv = *(const u32x4*)(hc + 252 - 4 * lane);
+    const uint32_t c = hv[0] + hv[1] + hv[2] + hv[3];
+    const uint32_t incl = wave_prefix_sum(c) + above;
+    const uint64_t hit = ballot(incl >= r);
+    const int L = hit ? __builtin_ctzll(hit) : 63;
+    uint32_t acc = incl - c, d = 0u, hd = 0u;
+    if (lane == L) {
+      d = 252 - 4 * lane;
+      if (acc + hv[3] >= r) { d += 3; hd = hv[3]; }
+      else {
+        acc += hv[3];
+        if (acc + hv[2] >= r) { d += 2; hd = hv[2]; }
+        else {
+          acc += hv[2];
+          if (acc + hv[1] >= r) { d += 1; hd = hv[1]; }
+          else { acc += hv[1]; hd = hv[0]; }
+        }
+      }
+    }
+    o.b = (uint32_t)__builtin_amdgcn_readlane((int)d, L);
+    o.above = (uint32_t)__builtin_amdgcn_readlane((int)acc, L);
+    o.hb = (uint32_t)__builtin_amdgcn_readlane((int)hd, L);
+  }
+  return o;
+}
+
+// shift that maps [kmin, kmax] onto at most 256 bins
+__device__ __forceinline__ int bin_shift(uint32_t kmin, uint32_t kmax) {
+  const uint32_t span = kmax - kmin;
+  const int top = span ? 31 - __builtin_clz(span) : 0;
+  return top > 7 ? top - 7 : 0;
+}
+
+// Approximate r-th largest of the group's keys (a cut with at least r keys at
+// or above it, and about r): the lower edge of the bin holding the r-th key,
+// refined once inside that bin when it holds more than r / 16 keys.  Returns
+// the order key of the cut (0 for groups with no keys).  Every wave calls it.
+template <int QT, int NS>
+__device__ __forceinline__ uint32_t group_cut(TopkSmem<QT>& sm, const uint32_t (&kr)[NS], uint32_t r, bool active) {
+  uint32_t kmin, kmax;
+  group_extremes<QT, NS>(sm, kr, kmin, kmax);
+  active = active && kmax != 0u && r >= 1u;
+  const int s = bin_shift(kmin, kmax);
+  const BinOut o = group_bin<QT, NS>(sm, 0, kr, kmin, s, r, 0u, active);
+  uint32_t lo = kmin + (o.b << s);
+  const bool refine = active && s > 0 && o.hb > max(r >> 4, 1u);
+  const int s2 = s > 8 ? s - 8 : 0;
+  const BinOut o2 = group_bin<QT, NS>(sm, 1, kr, lo, s2, r, o.above, refine);
+  if (refine) lo += o2.b << s2;
+  return active ? lo : 0u;
+}
+
+// ----------------------------------------------------------------------------
 // Exact streaming fallback (work-group wide): buffers hold order keys and are
 // shrunk to exactly k whenever they fill.
 
@@ -414,7 +540,7 @@ __device__ void wg_bitonic_sort(TopkSmem<QT>& sm, int j, int cnt) {
   int P = 1;
   while (P < cnt) P <<= 1;
   uint2* s = sm.cand[j];  // sorts the entry field
-  for (int i = cnt + tid; i < P; i += kThreads) s[i].y = 0x7fffffffu;
+  for (int i = cnt + tid; i < P; i += kThreads) s[i].y = 0x7fffffffu;  // canon_key: largest
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -422,8 +548,8 @@ __device__ void wg_bitonic_sort(TopkSmem<QT>& sm, int j, int cnt) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const bool asc = (lo & size) == 0;
-        const int32_t a = (int32_t)s[lo].y, bb = (int32_t)s[hi].y;
-        if ((a > bb) == asc) { s[lo].y = (uint32_t)bb; s[hi].y = (uint32_t)a; }
+        const uint32_t a = s[lo].y, bb = s[hi].y;
+        if ((canon_key(a) > canon_key(bb)) == asc) { s[lo].y = bb; s[hi].y = a; }
       }
       __syncthreads();
     }
@@ -431,64 +557,87 @@ __device__ void wg_bitonic_sort(TopkSmem<QT>& sm, int j, int cnt) {
 }
 
 // ----------------------------------------------------------------------------
-// Ascending output of a token group's kept indices (ir[sl] where bit sl of
-// keep is set; every kept index is < nvj).  The entry range is covered in
-// segments of kSegBits entries: the group marks its kept indices in a bitmap
-// held in its token's (now free) candidate buffer, counts the marks of each
-// lane's words, and every lane writes the indices of its marks at its offset.
-// Every wave of the work-group calls it (it synchronises the work-group);
-// groups of rows past n pass live = false and write nothing.
-constexpr int kSegBits = kCap * 64;  // bits in a token's candidate buffer
+// Canonical row order.  The indices of a row are written grouped by
+// (index / 32) % 8 -- the 32-entry tile modulo 8 -- groups in ascending
+// order, ascending within each group; -1 padding follows.  The order depends
+// on the selected set only, so every path (work-groups of 1, 2 or 4 tokens,
+// the split decode path, the exact streaming path) writes the same row, and
+// attention, whose sums follow the row's order, sees the same keys in the
+// same order.  Wave w of the scoring pass scores the tiles T with
+// T % kWaves == w in ascending order, so its region of a token's buffer
+// holds whole groups (w and, with 4 waves, w + 4), each in ascending order:
+// the row is written straight from the regions.
 
+// Entries 0 .. nv-1 (all kept), in the canonical order: position i.
+__device__ __forceinline__ int32_t canon_all(int i, int nv) {
+  const int nt = nv >> 5, rem = nv & 31;
+  int base = 0;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int full = nt > v ? (nt - v + 7) >> 3 : 0;  // full tiles T < nt with T % 8 == v
+    const int cnt = 32 * full + ((nt & 7) == v ? rem : 0);
+    if (i < base + cnt) {
+      const int r = i - base;
+      return 32 * (v + 8 * (r >> 5)) + (r & 31);
+    }
+    base += cnt;
+  }
+  return -1;
+}
+
+// Main path output of a token group's kept entries (ir[sl] where bit sl of
+// keep is set; kk of them), then -1 padding up to k.  Every wave of the
+// work-group calls it (one barrier); groups of rows past n pass live = false.
 template <int QT, int NS>
-__device__ void emit_ascending(TopkSmem<QT>& sm, bool live, const uint32_t (&ir)[NS], uint32_t keep, int nvj,
-                               int nv_all, int32_t* o) {
-  constexpr int G = Shape<QT>::W / QT;
-  constexpr int GL = G * 64;  // lanes of the group
+__device__ __forceinline__ void emit_canonical(TopkSmem<QT>& sm, bool live, const uint32_t (&ir)[NS], uint32_t keep,
+                                               int kk, int k, int32_t* o) {
+  constexpr int W = Shape<QT>::W, G = W / QT, VPW = 8 / W;  // canonical groups per region
+  constexpr int kPer = Shape<QT>::Reg / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = wave % QT, h = wave / QT;
-  const int gl = h * 64 + lane;
-  uint32_t* bm = (uint32_t*)&sm.cand[j][0];
-  int out0 = 0;  // indices written by the previous segments
-  for (int s0 = 0; s0 < nv_all; s0 += kSegBits) {
-    int len = live ? nvj - s0 : 0;
-    len = len < 0 ? 0 : (len > kSegBits ? kSegBits : len);
-    const int nw = (len + 31) >> 5;
-    for (int w = gl; w < nw; w += GL) bm[w] = 0u;
-    __syncthreads();
+  // kept entries per canonical group of each of this member's regions
 #pragma unroll
-    for (int sl = 0; sl < NS; ++sl) {
-      const uint32_t e = ir[sl] - (uint32_t)s0;
-      if (((keep >> sl) & 1u) && e < (uint32_t)len) atomicOr(&bm[e >> 5], 1u << (e & 31u));
-    }
-    __syncthreads();
-    // lane gl takes words [gl * wpl, (gl + 1) * wpl)
-    const int wpl = (nw + GL - 1) / GL;
-    const int w0 = gl * wpl, w1 = min(w0 + wpl, nw);
-    uint32_t cnt = 0u;
-    for (int w = w0; w < w1; ++w) cnt += __builtin_popcount(bm[w]);
-    const uint32_t incl = wave_prefix_sum(cnt);
-    if (lane == 63) sm.xchg[wave][0] = incl;
-    __syncthreads();
-    uint32_t before = 0u, total = 0u;
+  for (int rr = 0; rr < QT; ++rr) {
+    const int w = h * QT + rr;
 #pragma unroll
-    for (int m = 0; m < G; ++m) {
-      const uint32_t tm = sm.xchg[j + QT * m][0];
-      before += m < h ? tm : 0u;
-      total += tm;
+    for (int sv = 0; sv < VPW; ++sv) {
+      uint32_t c = 0u;
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const int sl = rr * kPer + m;
+        c += (uint32_t)__builtin_popcountll(ballot(((keep >> sl) & 1u) && ((ir[sl] >> 5) & 7u) == (uint32_t)(w + sv * W)));
+      }
+      if (lane == 0) sm.vcnt[j][w + sv * W] = c;
     }
-    int pos = out0 + (int)(before + incl - cnt);
-    for (int w = w0; w < w1; ++w) {
-      uint32_t bits = bm[w];
-      while (bits) {
-        const int bit = __builtin_ctz(bits);
-        o[pos++] = s0 + 32 * w + bit;
-        bits &= bits - 1u;
+  }
+  __syncthreads();
+  uint32_t vb[8];  // first position of each group
+  uint32_t acc = 0u;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    vb[v] = acc;
+    acc += sm.vcnt[j][v];
+  }
+  if (!live) return;
+#pragma unroll
+  for (int rr = 0; rr < QT; ++rr) {
+    const int w = h * QT + rr;
+#pragma unroll
+    for (int sv = 0; sv < VPW; ++sv) {
+      const int v = w + sv * W;
+      uint32_t run = vb[v];
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const int sl = rr * kPer + m;
+        const bool in = ((keep >> sl) & 1u) && ((ir[sl] >> 5) & 7u) == (uint32_t)v;
+        const uint64_t bal = ballot(in);
+        const uint32_t pos = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (in && pos < (uint32_t)k) o[pos] = (int32_t)ir[sl];
+        run += (uint32_t)__builtin_popcountll(bal);
       }
     }
-    out0 += (int)total;
-    __syncthreads();  // the bitmap and the counts are reused by the next segment
   }
+  for (int i = kk + h * 64 + lane; i < k; i += G * 64) o[i] = -1;
 }
 
 // ----------------------------------------------------------------------------
@@ -754,7 +903,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
       const int q = q0 + j;
       if (q < p.n) {
         int32_t* o = p.idx_out + ((int64_t)b * p.n + q) * p.k;
-        for (int i = tid; i < p.k; i += kThreads) o[i] = i < nv[j] ? i : -1;
+        for (int i = tid; i < p.k; i += kThreads) o[i] = i < nv[j] ? canon_all(i, nv[j]) : -1;
       }
     }
     return;
@@ -788,7 +937,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   const bool two_stage = sampling && S >= 32;
   const int target_a = two_stage ? 4 * target : target;
   if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = -__builtin_inff(); }
-  if (tid == 0) { sm.fallback = 0; sm.ties = 0; }
+  if (tid == 0) { sm.fallback = 0; sm.ties = 0; sm.staged = 0; }
   if (SPLIT != 2 && sampling) {
     // sample tiles wave, wave + kWaves, ...; kDepth tiles in flight per wave
     const int ntile = ((maxnv + S - 1) / S + 31) / 32;
@@ -822,23 +971,21 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
       }
     }
     __syncthreads();
-    // sample quantile: member h of token j's group holds samples h*kCap/G + lane + 64m
+    // sample quantile: sample i of token j sits in slot m of member h, lane
+    // l with i = (m * G + h) * 64 + l, so every member holds a share
     const int nsj = (q0 + grp_j < p.n && nv[grp_j] > kCap) ? (nv[grp_j] + S - 1) / S : 0;
     uint32_t kr[NS];
-    uint32_t smask = 0u;
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
-      const int i0 = grp_h * (kCap / G) + 64 * m;
-      const int i = i0 + lane;
-      smask |= (i0 < nsj ? 1u : 0u) << m;
+      const int i = (m * G + grp_h) * 64 + lane;
       kr[m] = i < nsj ? okey(sm.cand[grp_j][i].x) : 0u;
     }
     int r = nsj > 0 ? (int)(((int64_t)target_a * nsj + nv[grp_j] - 1) / nv[grp_j]) : 0;
     r = r < 1 ? 1 : (r > nsj ? nsj : r);
-    // the cut need not be exact: a bin of up to r/16 samples is close enough
-    const RadixOut ro = group_radix<QT, NS>(sm, kr, smask, (uint32_t)r, (uint32_t)nsj, nsj > 0, (uint32_t)(r >> 4));
+    // the cut need not be exact (a bin of up to r/16 samples is close enough);
     // never above the r-th sample; at least the order key of -inf
-    if (nsj > 0 && grp_h == 0 && lane == 0) sm.thr[grp_j] = key_to_float(max(ro.T, 0x007fffffu));
+    const uint32_t cut = group_cut<QT, NS>(sm, kr, (uint32_t)r, nsj > 0);
+    if (nsj > 0 && grp_h == 0 && lane == 0) sm.thr[grp_j] = key_to_float(max(cut, 0x007fffffu));
 
     if (two_stage) {
       __syncthreads();  // first cuts visible; the sample buffers are free
@@ -931,14 +1078,19 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   #pragma unroll
     for (int tt = 0; tt < TPL; ++tt) {
       const int j = jl0 + 2 * tt;
-      thr2[tt] = (j < QT) ? sm.thr[j < QT ? j : 0] : 0.0f;
+      // rows past n (or slots past QT) never pass: the full tiles below do
+      // not test visibility
+      thr2[tt] = (j < QT && nvl[tt] > 0) ? sm.thr[j < QT ? j : 0] : __builtin_inff();
       // the LDS read completes here, not inside the scoring loop (whose LDS
       // stores would otherwise be waited for on every tile)
       asm volatile("" : "+v"(thr2[tt]));
     }
     {
       // kDepth tiles in flight per wave; each tile's registers are reloaded
-      // right after its MFMA has read them
+      // right after its MFMA has read them.  Wave w scores the tiles
+      // T = e / 32 with T % kWaves == w, in ascending order, so its region of
+      // a token's buffer holds that token's candidates of those tiles in
+      // ascending entry order.
       const int ecol = wave * 32 + l32;
       int wcnt[2] = {0, 0};
       BTile<FMT> t[kDepth];
@@ -1053,35 +1205,55 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
     }
     const int c = sm.cnt[j];
     const bool sel = live && c > kk;
-    const RadixOut ro = group_radix<QT, NS>(sm, kr, smask, (uint32_t)kk, (uint32_t)c, sel);
-    const bool need_ties = sel && ro.exact && (uint32_t)kk - ro.above < ro.inbin;
-    if (need_ties && grp_h == 0 && lane == 0) sm.ties = 1;
-    __syncthreads();
-    uint32_t tinv = 0u;
-    if (sm.ties) {
-      // ties at the k-th score: keep the (kk - above) smallest entry indices among them
-      uint32_t k2[NS];
-#pragma unroll
-      for (int sl = 0; sl < NS; ++sl) k2[sl] = (need_ties && kr[sl] == ro.T) ? ~ir[sl] : 0u;
-      const RadixOut r2 = group_radix<QT, NS>(sm, k2, smask, (uint32_t)kk - ro.above, ro.inbin, need_ties);
-      tinv = r2.T;
-    }
-    const uint32_t Tk = sel ? max(ro.T, 1u) : 1u;  // empty slots (key 0) are never kept
     uint32_t keep = 0u;
+    {
+      const RadixOut ro = group_radix<QT, NS>(sm, kr, smask, (uint32_t)kk, (uint32_t)c, sel);
+      const bool need_ties = sel && ro.exact && (uint32_t)kk - ro.above < ro.inbin;
+      if (need_ties && grp_h == 0 && lane == 0) sm.ties = 1;
+      __syncthreads();
+      uint32_t tinv = 0u;
+      if (sm.ties) {
+        // ties at the k-th score: keep the (kk - above) smallest entry indices among them
+        uint32_t k2[NS];
 #pragma unroll
-    for (int sl = 0; sl < NS; ++sl) {
-      bool kp = kr[sl] >= Tk;
-      if (need_ties && kr[sl] == ro.T) kp = ~ir[sl] >= tinv;
-      keep |= (kp ? 1u : 0u) << sl;
+        for (int sl = 0; sl < NS; ++sl) k2[sl] = (need_ties && kr[sl] == ro.T) ? ~ir[sl] : 0u;
+        const RadixOut r2 = group_radix<QT, NS>(sm, k2, smask, (uint32_t)kk - ro.above, ro.inbin, need_ties);
+        tinv = r2.T;
+      }
+      const uint32_t Tr = sel ? max(ro.T, 1u) : 1u;  // empty slots (key 0) are never kept
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        bool kp = kr[sl] >= Tr;
+        if (need_ties && kr[sl] == ro.T) kp = ~ir[sl] >= tinv;
+        keep |= (kp ? 1u : 0u) << sl;
+      }
     }
-    // output: the kept indices in ascending order, then -1 padding
-    int maxnv_live = 0;
-#pragma unroll
-    for (int jj = 0; jj < QT; ++jj) maxnv_live = max(maxnv_live, q0 + jj < p.n ? nv[jj] : 0);
+    // output in the canonical order, then -1 padding
     int32_t* o = p.idx_out + ((int64_t)b * p.n + (live ? q : 0)) * p.k;
-    emit_ascending<QT, NS>(sm, live, ir, keep, nv[j], maxnv_live, o);
-    if (live)
-      for (int i = kk + grp_h * 64 + lane; i < p.k; i += G * 64) o[i] = -1;
+    if constexpr (SPLIT == 0) {
+      emit_canonical<QT, NS>(sm, live, ir, keep, kk, p.k, o);
+    } else {
+      // the split path's candidates arrived in atomic order: stage the kept
+      // entries and sort them into the canonical order
+      int mine = 0;
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) mine += __builtin_popcountll(ballot((keep >> sl) & 1u));
+      int pos = 0;
+      if (lane == 0 && mine) pos = atomicAdd(&sm.staged, mine);  // this wave's range of the staging area
+      pos = __builtin_amdgcn_readfirstlane(pos);
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        const bool kp = (keep >> sl) & 1u;
+        const uint64_t bal = ballot(kp);
+        const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (kp && pos + rank < kCap) sm.cand[0][pos + rank].y = ir[sl];
+        pos += __builtin_popcountll(bal);
+      }
+      __syncthreads();
+      wg_bitonic_sort(sm, 0, kk);
+      if (live)
+        for (int i = tid; i < p.k; i += kThreads) o[i] = i < kk ? (int32_t)sm.cand[0][i].y : -1;
+    }
   }
 }
 

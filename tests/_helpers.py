@@ -66,6 +66,19 @@ def canon_idx(rows):
     return out
 
 
+def canonical_rows(rows):
+    """Top-k rows in the library's canonical order: the selected indices
+    grouped by (index // 32) % 8, groups ascending, ascending within a group,
+    then the -1 padding."""
+    rows = np.asarray(rows)
+    out = np.full_like(rows, -1)
+    for r in np.ndindex(rows.shape[:-1]):
+        v = rows[r][rows[r] >= 0].astype(np.int64)
+        v = v[np.lexsort((v, (v >> 5) & 7))]
+        out[r][:v.size] = v
+    return out
+
+
 def topk_tie_ok(got, ref, scores, nv, k):
     """bf16 rule: equal set sizes; the symmetric difference lies within
     TIE_BAND of the k-th largest oracle score.  Returns the number of rows

@@ -10,7 +10,7 @@ import long_context_attention_21_amd as L
 from long_context_attention_21_amd import synth
 
 from _helpers import (assert_close, bf16_f64, dev, host, host_bits, oracle_compress_store,
-                      oracle_q_dec, topk_tie_ok, canon_idx)
+                      oracle_q_dec, topk_tie_ok, canon_idx, canonical_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,8 +118,8 @@ def _index_case(orc, rng, B, n, N, H_I, k, q_pos0, fmt, m=4, dup_rows=0, prequan
         assert (nfb > 0) == fallback, "%d work-groups took the exact streaming path" % nfb
     got = host(got)
     rows = np.arange(n, dtype=np.int32)
-    # every row: ascending indices, then the -1 padding
-    assert np.array_equal(got, canon_idx(got)), "rows are not in ascending order"
+    # every row in the canonical order, then the -1 padding
+    assert np.array_equal(got, canonical_rows(got)), "rows are not in the canonical order"
     for b in range(B):
         ref = orc.index_topk_rows(qdec[b], w[b], kdec[b], m, q_pos0, rows, k)
         if fmt == "mxfp4":
