@@ -339,10 +339,11 @@ def test_attend_matches_oracle(orc, case):
 def test_hca_two_token_work_groups(orc):
     """HCA with at least 4096 query rows, more than 32 heads and at least
     512 entries visible to every row runs two tokens per work-group: one key
-    ring for both, the union of their windows, each token masking what it
-    does not see.  An odd row count leaves the last work-group a single
-    token.  The first and last rows, the rows around entry-block boundaries
-    and a random sample are checked against the oracle."""
+    ring for both, each token with its own window chunks, each wave masking
+    what its token does not see.  An odd row count leaves the last
+    work-group a single token.  The first and last rows, the rows around
+    entry-block boundaries and a random sample are checked against the
+    oracle."""
     n, m = 2049, 8
     rng = np.random.default_rng(7)
     rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(n - 40, n), np.arange(m - 3, 4 * m + 3),
