@@ -5,13 +5,21 @@ batch 1, 131072 query tokens, 64 heads of dim 128 with RoPE on the last 64
 dims, m = 4 overlapped compression (32768 entries), MXFP4 Lightning Indexer
 (8 heads x 64, q quantised in-kernel), top-k 2048, 128-token window, per-head
 sink.  One step = csa_compress -> csa_index_topk -> csa_attend over the whole
-sequence, inputs resident in HBM.  --config 2 times the HCA layer (32768
-tokens, m' = 128), --config 1 the small CSA layer.
+sequence, inputs resident in HBM.
+
+The default run also times, with the same steps, the two HBM-bound
+workloads and reports each under "workloads" with its own roofline and
+oracle baseline: the HCA layer forward (32768 tokens, m' = 128) and the CSA
+decode step (64 sequences at t = 1M).  --config N times one workload alone
+(1: the small CSA layer, 2: HCA, 3: the default, 4: decode, 5: the chunked
+prefill of a CSA + HCA layer pair).
 
 Prints one JSON line: throughput (query tokens/s), the roofline of the
 dominant kernel (per-kernel durations from HIP events recorded on the launch
 stream over the timed region), per-kernel figures, and the CPU oracle timed
-on a bounded sample of the same workload (rank 0, N = 1 only).
+on a bounded sample of the same workload with all host cores and with one
+thread (N = 1 only); a rate scaled up from a row sample says
+"extrapolated".
 """
 from __future__ import annotations
 
@@ -75,9 +83,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help="time this workload alone (default: config 3, with configs 2 and 4 beside it "
+                         "under 'workloads')")
+    ap.add_argument("--no-extra", action="store_true", help="default run: leave out configs 2 and 4")
     ap.add_argument("--cpu-sample", type=int, default=None,
-                    help="query rows of the oracle sample (default per config)")
+                    help="query rows (config 4: sequences) of the oracle sample (default per config)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (HBM counter calibration)")
@@ -350,34 +361,55 @@ class CsaLayer:
                      sink=self.sink, out=self.out)
         if ev: ev[4].record()
 
+    def _cpu_prep(self):
+        """Whole-sequence oracle work, done once: compression, the entries'
+        bf16 values and the indexer's keys and queries as the kernel sees them."""
+        if getattr(self, "_prep", None) is None:
+            import oracle as orc
+            c = self.c
+            t0 = time.time()
+            ent, kid = orc.compress(c["kv"][0], c["beta"], self.m, 1, ik=c["ik"][0])
+            E = orc.bf16_to_f64(orc.bf16_from_f32(ent))
+            qf = orc.bf16_to_f64(c["q_I"][0]).astype(np.float32)
+            if self.fmt == "mxfp4":
+                kdec = orc.mxfp4_decode(*orc.mxfp4_encode(kid))
+                qdec = orc.mxfp4_decode(*orc.mxfp4_encode(qf))
+            else:
+                kdec = orc.bf16_to_f64(orc.bf16_from_f32(kid)).astype(np.float32)
+                qdec = qf
+            self._prep = (E, kdec, qdec, time.time() - t0)
+        return self._prep
+
+    def row_work(self, rows):
+        """Oracle flops of each query row: indexer scores over the visible
+        entries, attention over its top-k entries and window."""
+        t = np.asarray(rows, dtype=np.int64)
+        nv = np.minimum(self.N, (t + 1) // self.m)
+        return (2.0 * self.c["H_I"] * 64 * nv
+                + 4.0 * self.H * 128 * (np.minimum(self.k, nv) + np.minimum(t + 1, 128)))
+
     def cpu_baseline(self, sample):
-        """The oracle on `sample` query rows spread over the sequence (plus the
-        compression of the whole sequence, charged pro rata)."""
+        """The oracle on `sample` query rows drawn uniformly over the sequence,
+        extrapolated to all rows by per-row flops, plus the whole-sequence
+        compression and encoding (timed whole)."""
         import oracle as orc
         c = self.c
+        E, kdec, qdec, t_whole = self._cpu_prep()
         rng = np.random.default_rng(0)
         rows = np.sort(rng.choice(self.n, size=min(sample, self.n), replace=False)).astype(np.int32)
-        t0 = time.time()
-        ent, kid = orc.compress(c["kv"][0], c["beta"], self.m, 1, ik=c["ik"][0])
-        t_comp = time.time() - t0
-        E = orc.bf16_to_f64(orc.bf16_from_f32(ent))
-        qf = orc.bf16_to_f64(c["q_I"][0]).astype(np.float32)
-        if self.fmt == "mxfp4":
-            kc, ks = orc.mxfp4_encode(kid)
-            kdec = orc.mxfp4_decode(kc, ks)
-            qc, qs = orc.mxfp4_encode(qf)
-            qdec = orc.mxfp4_decode(qc, qs)
-        else:
-            kdec = orc.bf16_to_f64(orc.bf16_from_f32(kid)).astype(np.float32)
-            qdec = qf
-        t_prep = time.time() - t0 - t_comp
         t1 = time.time()
         idx = orc.index_topk_rows(qdec, c["w_I"][0], kdec, self.m, 0, rows, self.k)
-        _ = orc.attend_rows(c["q"][0], 0, E, self.m, rows, "csa", idx=idx, win=c["kv"][0],
-                            sink=c["sink"])
+        orc.attend_rows(c["q"][0], 0, E, self.m, rows, "csa", idx=idx, win=c["kv"][0], sink=c["sink"])
         t_rows = time.time() - t1
-        total = t_rows + (t_comp + t_prep) * rows.size / self.n
-        return rows.size / total, rows.size, t_comp + t_prep, t_rows
+        frac = self.row_work(rows).sum() / self.row_work(np.arange(self.n)).sum()
+        total = t_rows / frac + t_whole
+        ext = rows.size < self.n
+        return {"value": self.n / total, "extrapolated": ext,
+                "sample": "%d of %d query rows%s: oracle top-k + attention (%.2f s)%s, "
+                          "plus whole-sequence compression and indexer encoding (%.2f s)"
+                          % (rows.size, self.n, " drawn uniformly (seed 0)" if ext else "", t_rows,
+                             ", scaled to all rows by per-row flops (indexer scores + attention keys)" if ext
+                             else "", t_whole)}
 
 
 class HcaLayer:
@@ -420,20 +452,37 @@ class HcaLayer:
                      out=self.out)
         if ev: ev[3].record()
 
+    def _cpu_prep(self):
+        if getattr(self, "_prep", None) is None:
+            import oracle as orc
+            c = self.c
+            t0 = time.time()
+            ent, _ = orc.compress(c["kv"][0], c["beta"], self.m, 0)
+            self._prep = (orc.bf16_to_f64(orc.bf16_from_f32(ent)), time.time() - t0)
+        return self._prep
+
+    def row_work(self, rows):
+        t = np.asarray(rows, dtype=np.int64)
+        return 4.0 * self.H * 128 * (np.minimum(self.N, (t + 1) // self.m) + np.minimum(t + 1, 128))
+
     def cpu_baseline(self, sample):
+        """The oracle on `sample` query rows (all rows by default), plus the
+        whole-sequence compression."""
         import oracle as orc
         c = self.c
+        E, t_whole = self._cpu_prep()
         rng = np.random.default_rng(0)
         rows = np.sort(rng.choice(self.n, size=min(sample, self.n), replace=False)).astype(np.int32)
-        t0 = time.time()
-        ent, _ = orc.compress(c["kv"][0], c["beta"], self.m, 0)
-        t_comp = time.time() - t0
-        E = orc.bf16_to_f64(orc.bf16_from_f32(ent))
         t1 = time.time()
         orc.attend_rows(c["q"][0], 0, E, self.m, rows, "hca", win=c["kv"][0], sink=c["sink"])
         t_rows = time.time() - t1
-        total = t_rows + t_comp * rows.size / self.n
-        return rows.size / total, rows.size, t_comp, t_rows
+        frac = self.row_work(rows).sum() / self.row_work(np.arange(self.n)).sum()
+        ext = rows.size < self.n
+        return {"value": self.n / (t_rows / frac + t_whole), "extrapolated": ext,
+                "sample": "%d of %d query rows%s: oracle attention (%.2f s)%s, plus whole-sequence "
+                          "compression (%.2f s)" % (rows.size, self.n, " drawn uniformly (seed 0)" if ext else "",
+                                                    t_rows, ", scaled to all rows by per-row flops" if ext else "",
+                                                    t_whole)}
 
 
 def encode_cache(L, entries_bf16, keys_bf16, entry_fmt, out):
@@ -540,11 +589,9 @@ class DecodeLayer:
                          out=self.out)
         if ev: ev[2].record()
 
-    cpu_desc = ("%d sequences (all): oracle top-k over 262144 entries + attention for each query "
-                "(%.1f s); reading back and decoding the stored caches (%.1f s) is not charged")
-
     def cpu_baseline(self, sample):
-        """The oracle on `sample` of the sequences (decoded caches read back)."""
+        """The oracle on the first `sample` sequences (decoded caches read
+        back); every sequence does the same work, so the rate is theirs."""
         import oracle as orc
         c = self.c
         nb = min(sample, self.B)
@@ -573,7 +620,12 @@ class DecodeLayer:
             idx = orc.index_topk_rows(orc.mxfp4_decode(qc, qs), w[b], kdec, 4, c["q_pos0"], rows, self.k)
             orc.attend_rows(q[b], c["q_pos0"], E, 4, rows, "csa", idx=idx, sink=sink, **wkw)
             t_rows += time.time() - t1
-        return nb / t_rows, nb, time.time() - t0 - t_rows, t_rows
+        t_read = time.time() - t0 - t_rows
+        return {"value": nb / t_rows, "extrapolated": nb < self.B,
+                "sample": "%d of %d sequences: oracle top-k over %d entries + attention for each query (%.2f s)%s; "
+                          "reading back and decoding the stored caches (%.1f s) is not charged"
+                          % (nb, self.B, self.N, t_rows, ", every sequence the same work" if nb < self.B else "",
+                             t_read)}
 
 
 class PairLayer:
@@ -662,40 +714,59 @@ class PairLayer:
                      win_roped=True, sink=self.h_sink, out=self.h_out)
         if ev: ev[7].record()
 
-    cpu_desc = ("%d query rows of the 8192-token chunk drawn uniformly (seed 0): oracle CSA top-k + CSA "
-                "attention + HCA attention for those rows (%.1f s) plus the chunk's compression and cache "
-                "decoding (%.1f s, compression charged pro rata)")
+    def _cpu_prep(self):
+        """The chunk's compression (both layers) and the caches as the
+        kernels see them, done once."""
+        if getattr(self, "_prep", None) is None:
+            import oracle as orc
+            cs, hs = self.c["csa"], self.c["hca"]
+            t0 = time.time()
+            ent_new, kid_new = orc.compress(cs["kv_new"], cs["beta"], 4, 1, pos0=self.P, ik=cs["ik_new"],
+                                            prev_kv=cs["state_kv"][124:], prev_ik=cs["state_ik"])
+            hent_new, _ = orc.compress(hs["kv_new"], hs["beta"], 128, 0, pos0=self.P)
+            t_comp = time.time() - t0
+            E = np.concatenate([orc.bf16_to_f64(cs["entries_prior"]),
+                                orc.bf16_to_f64(orc.bf16_from_f32(ent_new))])
+            kq, ks = orc.mxfp4_encode(orc.bf16_to_f64(orc.bf16_from_f32(cs["kI_prior_f32"])).astype(np.float32))
+            kn, ksn = orc.mxfp4_encode(kid_new)
+            kdec = np.concatenate([orc.mxfp4_decode(kq, ks), orc.mxfp4_decode(kn, ksn)])
+            qdec = orc.mxfp4_decode(*orc.mxfp4_encode(orc.bf16_to_f64(cs["q_I"]).astype(np.float32)))
+            HE = np.concatenate([orc.bf16_to_f64(hs["entries_prior"]),
+                                 orc.bf16_to_f64(orc.bf16_from_f32(hent_new))])
+            self._prep = (E, kdec, qdec, HE, t_comp, time.time() - t0 - t_comp)
+        return self._prep
+
+    def row_work(self, rows):
+        t = self.P + np.asarray(rows, dtype=np.int64)
+        nv = np.minimum(self.Nc, (t + 1) // 4)
+        return (2.0 * 8 * 64 * nv + 4.0 * self.H * 128 * (np.minimum(self.k, nv) + 128)
+                + 4.0 * self.H * 128 * (np.minimum(self.Nh, (t + 1) // 128) + 128))
 
     def cpu_baseline(self, sample):
-        """The oracle on `sample` query rows of the chunk (both layers), the
-        chunk's compression charged pro rata."""
+        """The oracle on `sample` query rows of the chunk (both layers),
+        extrapolated to the chunk by per-row flops, plus the chunk's
+        compression (timed whole); decoding the prior caches is not charged."""
         import oracle as orc
-        c, cs, hs = self.c, self.c["csa"], self.c["hca"]
+        cs, hs = self.c["csa"], self.c["hca"]
+        E, kdec, qdec, HE, t_comp, t_dec = self._cpu_prep()
         rng = np.random.default_rng(0)
         rows = np.sort(rng.choice(self.n, size=min(sample, self.n), replace=False)).astype(np.int32)
-        t0 = time.time()
-        ent_new, kid_new = orc.compress(cs["kv_new"], cs["beta"], 4, 1, pos0=self.P, ik=cs["ik_new"],
-                                        prev_kv=cs["state_kv"][124:], prev_ik=cs["state_ik"])
-        hent_new, _ = orc.compress(hs["kv_new"], hs["beta"], 128, 0, pos0=self.P)
-        t_comp = time.time() - t0
-        E = np.concatenate([orc.bf16_to_f64(cs["entries_prior"]),
-                            orc.bf16_to_f64(orc.bf16_from_f32(ent_new))])
-        kq, ks = orc.mxfp4_encode(orc.bf16_to_f64(orc.bf16_from_f32(cs["kI_prior_f32"])).astype(np.float32))
-        kn, ksn = orc.mxfp4_encode(kid_new)
-        kdec = np.concatenate([orc.mxfp4_decode(kq, ks), orc.mxfp4_decode(kn, ksn)])
-        qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(cs["q_I"]).astype(np.float32))
-        HE = np.concatenate([orc.bf16_to_f64(hs["entries_prior"]), orc.bf16_to_f64(orc.bf16_from_f32(hent_new))])
         win_c = np.concatenate([cs["state_kv"], cs["kv_new"]])
         win_h = np.concatenate([hs["state_kv"], hs["kv_new"]])
-        t_prep = time.time() - t0 - t_comp
         t1 = time.time()
-        idx = orc.index_topk_rows(orc.mxfp4_decode(qc, qs), cs["w_I"], kdec, 4, self.P, rows, self.k)
+        idx = orc.index_topk_rows(qdec, cs["w_I"], kdec, 4, self.P, rows, self.k)
         orc.attend_rows(cs["q"], self.P, E, 4, rows, "csa", idx=idx, win=win_c, win_pos0=self.P - 128,
                         sink=cs["sink"])
         orc.attend_rows(hs["q"], self.P, HE, 128, rows, "hca", win=win_h, win_pos0=self.P - 128, sink=hs["sink"])
         t_rows = time.time() - t1
-        total = t_rows + t_comp * rows.size / self.n
-        return rows.size / total, rows.size, t_comp + t_prep, t_rows
+        frac = self.row_work(rows).sum() / self.row_work(np.arange(self.n)).sum()
+        ext = rows.size < self.n
+        return {"value": self.n / (t_rows / frac + t_comp), "extrapolated": ext,
+                "sample": "%d of %d query rows of the chunk drawn uniformly (seed 0): oracle CSA top-k + CSA "
+                          "attention + HCA attention (%.2f s)%s, plus the chunk's compression (%.2f s); decoding "
+                          "the prior caches (%.1f s) is not charged"
+                          % (rows.size, self.n, t_rows, ", scaled to the chunk by per-row flops" if ext else "",
+                             t_comp, t_dec)}
 
 
 def torch_int16():
@@ -710,6 +781,96 @@ WORKLOAD = {
     2: "HCA layer forward, batch 1, 32768 tokens, 64 heads x 128, m'=128 (256 entries), SWA 128, sink",
     3: "CSA prefill, batch 1, 131072 tokens, 64 heads x 128, m=4 overlapped (32768 entries), MXFP4 indexer 8x64, top-k 2048, SWA 128, sink",
 }
+
+
+DTYPE = {1: "bf16", 2: "bf16", 3: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)",
+         4: "fp8 e4m3 + bf16 entries, bf16 MFMA (attention) + mxfp4 (indexer MFMA)",
+         5: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)"}
+CPU_SAMPLE = {1: 1024, 2: 32768, 3: 8192, 4: 16, 5: 1024}  # query rows (config 4: sequences)
+CPU_SAMPLE_1T = {1: 128, 2: 512, 3: 256, 4: 2, 5: 32}  # the same at one thread
+# the two HBM-bound workloads timed beside the default one, under these names
+EXTRA = (("hca_prefill_32k", 2), ("csa_decode_64x1m", 4))
+
+
+def cpu_leg(wl, cfg_id, sample):
+    """The oracle on a bounded sample of the workload: all host cores, then
+    one thread on a smaller sample."""
+    import oracle
+    oracle.build()
+    log("cpu baseline: oracle on %d sampled %s" % (sample, "sequences" if cfg_id == 4 else "query rows"))
+    r = wl.cpu_baseline(sample)
+    cpu = {"value": round(r["value"], 2), "unit": "query-tokens/s", "cores": _cores(), "kind": "oracle",
+           "extrapolated": r["extrapolated"], "sample": r["sample"]}
+    prev = oracle.set_threads(1)
+    try:
+        r1 = wl.cpu_baseline(min(sample, CPU_SAMPLE_1T[cfg_id]))
+    finally:
+        oracle.set_threads(prev)
+    cpu["one_thread"] = {"value": round(r1["value"], 2), "cores": 1, "extrapolated": r1["extrapolated"],
+                         "sample": r1["sample"]}
+    return cpu
+
+
+def measure(cfg_id, args, cpu_sample=None):
+    """Warm up, time args.steps steps of workload `cfg_id` (per-kernel HIP
+    events on the launch stream), then the oracle baseline."""
+    import torch
+    wl = {1: CsaLayer, 2: HcaLayer, 3: CsaLayer, 4: DecodeLayer, 5: PairLayer}[cfg_id](cfg_id)
+    nk = len(wl.kernels)
+    log("config %d: warmup %d steps" % (cfg_id, args.warmup))
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    log("config %d: timing %d steps" % (cfg_id, args.steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        wl.step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_k = np.zeros(nk)
+    for s in range(args.steps):
+        for i in range(nk):
+            per_k[i] += evs[s][i].elapsed_time(evs[s][i + 1])
+    per_k /= args.steps  # ms per launch
+    ms_step = wall * 1e3 / args.steps
+
+    kernels = {}
+    for i, name in enumerate(wl.kernels):
+        kind, amount = wl.work[name]
+        sec = per_k[i] / 1e3
+        if kind == "hbm":
+            ach, peak, unit = amount / sec / 1e9, PEAK["hbm"], "GB/s"
+        else:
+            ach, peak, unit = amount / sec / 1e12, PEAK[kind], "TFLOP/s"
+        kernels[name] = {"ms": round(per_k[i], 4), "bound": "hbm" if kind == "hbm" else "mfma",
+                         "dtype": kind, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                         "frac": round(ach / peak, 4), "work": amount,
+                         "traffic": traffic_bytes(name, cfg_id)}
+    dom = wl.kernels[int(np.argmax(per_k))]
+    dk = kernels[dom]
+    roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
+                "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic_bytes(dom, cfg_id)}
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_leg(wl, cfg_id, cpu_sample or CPU_SAMPLE[cfg_id])
+
+    wname, dname = WORKLOAD[cfg_id], DTYPE[cfg_id]
+    if cfg_id == 4 and DecodeLayer.entry_fmt == "nvfp4":
+        wname = wname.replace("262144 FP8+bf16 entries", "262144 NVFP4 entries + an FP8 window cache "
+                                                         "(post-RoPE, the V4.1 variant)")
+        dname = dname.replace("fp8 e4m3 + bf16 entries", "nvfp4 entries")
+    cfg = {"workload": wname, "global_batch": getattr(wl, "B", 1), "seq_len": wl.n,
+           "heads": wl.H, "head_dim": 128}
+    res = {"value": round(wl.n / (ms_step / 1e3), 1), "unit": "query-tokens/s", "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "dtype": dname, "config": cfg,
+           "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu}
+    if hasattr(wl, "fallbacks"):  # top-k work-groups that took the exact streaming path, per call
+        res["topk_fallbacks_per_call"] = round(int(wl.fallbacks.item()) / (args.warmup + args.steps), 2)
+    del wl
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -737,81 +898,17 @@ def main():
         if args.config != 4:
             sys.exit("--entry-fmt applies to config 4 only")
         DecodeLayer.entry_fmt = args.entry_fmt
-    wl = {1: CsaLayer, 2: HcaLayer, 3: CsaLayer, 4: DecodeLayer, 5: PairLayer}[args.config](args.config)
-    nk = len(wl.kernels)
-    log("warmup %d steps" % args.warmup)
-    for _ in range(args.warmup):
-        wl.step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
-    log("timing %d steps" % args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        wl.step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_k = np.zeros(nk)
-    for s in range(args.steps):
-        for i in range(nk):
-            per_k[i] += evs[s][i].elapsed_time(evs[s][i + 1])
-    per_k /= args.steps  # ms per launch
-    ms_step = wall * 1e3 / args.steps
-    value = wl.n / (ms_step / 1e3)
-
-    kernels = {}
-    for i, name in enumerate(wl.kernels):
-        kind, amount = wl.work[name]
-        sec = per_k[i] / 1e3
-        if kind == "hbm":
-            ach, peak, unit = amount / sec / 1e9, PEAK["hbm"], "GB/s"
-        else:
-            ach, peak, unit = amount / sec / 1e12, PEAK[kind], "TFLOP/s"
-        kernels[name] = {"ms": round(per_k[i], 4), "bound": "hbm" if kind == "hbm" else "mfma",
-                         "dtype": kind, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                         "frac": round(ach / peak, 4), "work": amount,
-                         "traffic": traffic_bytes(name, args.config)}
-    dom = wl.kernels[int(np.argmax(per_k))]
-    dk = kernels[dom]
-    roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
-                "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic_bytes(dom, args.config)}
-
-    cpu = None
-    if not args.no_cpu:
-        sample = args.cpu_sample or {1: 1024, 2: 32768, 3: 8192, 4: 64, 5: 256}[args.config]
-        log("cpu baseline: oracle on %d sampled query rows" % sample)
-        import oracle
-        oracle.build()
-        v, rows, t_comp, t_rows = wl.cpu_baseline(sample)
-        desc = getattr(wl, "cpu_desc", None)
-        cores = len(os.sched_getaffinity(0))
-        omp = os.environ.get("OMP_NUM_THREADS")
-        if omp:
-            cores = min(cores, int(omp))
-        cpu = {"value": round(v, 2), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
-               "sample": (desc % (rows, t_rows, t_comp)) if desc else
-                         "%d query rows drawn uniformly over the sequence (seed 0): oracle top-k + "
-                         "attention for those rows (%.1f s) plus whole-sequence compression "
-                         "(%.1f s) charged pro rata" % (rows, t_rows, t_comp)}
-
-    wname = WORKLOAD[args.config]
-    dname = {1: "bf16", 2: "bf16", 3: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)",
-             4: "fp8 e4m3 + bf16 entries, bf16 MFMA (attention) + mxfp4 (indexer MFMA)",
-             5: "bf16 (attention MFMA) + mxfp4 (indexer MFMA)"}[args.config]
-    if args.entry_fmt == "nvfp4":
-        wname = wname.replace("262144 FP8+bf16 entries", "262144 NVFP4 entries + an FP8 window cache "
-                                                         "(post-RoPE, the V4.1 variant)")
-        dname = dname.replace("fp8 e4m3 + bf16 entries", "nvfp4 entries")
-    cfg = {"workload": wname, "global_batch": getattr(wl, "B", 1), "seq_len": wl.n,
-           "heads": wl.H, "head_dim": 128}
+    cfg_id = args.config or 3
+    res = measure(cfg_id, args, args.cpu_sample)
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": dname,
-        "data": "synthetic (seeded, numpy default_rng)", "config": cfg,
-        "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+        "dtype": res["dtype"], "data": "synthetic (seeded, numpy default_rng)", "config": res["config"],
+        "roofline": res["roofline"], "kernels": res["kernels"], "cpu_baseline": res["cpu_baseline"],
     }
+    if args.config is None and not args.no_extra:
+        line["workloads"] = {name: measure(c, args) for name, c in EXTRA}
     print(json.dumps(line), flush=True)
 
 

@@ -65,6 +65,7 @@ def lib():
             "orc_attend_rows": (i32, [P, i32, i32, i64, P, i32, i32, P, i32, i32, P, P, i64,
                                       i32, i32, P, i32, dbl, P, i32, P]),
             "orc_store_window_fp8_n": (None, [P, i64, i64, i32, dbl, P, P]),
+            "orc_set_threads": (i32, [i32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -72,6 +73,11 @@ def lib():
             f.argtypes = args
         _lib = L
     return _lib
+
+
+def set_threads(n):
+    """Thread count of the row-parallel loops (timing only); returns the previous one."""
+    return lib().orc_set_threads(int(n))
 
 
 def _p(a):

@@ -38,6 +38,7 @@
 
 #include <fenv.h>
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -560,6 +561,16 @@ int orc_attend_rows(const uint16_t* q, int H, int D, int64_t q_pos0,
 /* ========================================================================== */
 /* Array helpers for the Python wrapper                                       */
 /* ========================================================================== */
+
+/* Thread count of the row-parallel loops (top-k rows, attention rows), for
+ * timing only: every row is computed by one thread on its own, so results do
+ * not depend on it.  Returns the previous count. */
+int orc_set_threads(int n)
+{
+    int prev = omp_get_max_threads();
+    if (n > 0) omp_set_num_threads(n);
+    return prev;
+}
 
 void orc_bf16_from_f32_n(const float* x, int64_t n, uint16_t* out)
 {

@@ -106,6 +106,7 @@ int orc_attend_rows(const uint16_t* q, int H, int D, int64_t q_pos0,
 
 
 /* ---- array helpers (used by the Python wrapper) --------------------------- */
+int orc_set_threads(int n);
 void orc_bf16_from_f32_n(const float* x, int64_t n, uint16_t* out);
 void orc_bf16_to_f64_n(const uint16_t* b, int64_t n, double* out);
 void orc_e4m3_from_f32_n(const float* x, int64_t n, uint8_t* out);
