@@ -209,8 +209,9 @@ int csa_cache_append(const void* kv_new, const void* ik_new, const float* z_new,
  *              on one stream.
  *  fallback_count  NULL, or a caller-owned device uint32 (4-byte aligned):
  *              the kernels add the number of work-groups that took the exact
- *              streaming path (the sampled threshold left fewer than k or
- *              more candidates than a buffer holds, e.g. under massive score
+ *              streaming path (the sampled threshold, or on the split path
+ *              the partitions' own cuts, left fewer than k or more
+ *              candidates than a buffer holds, e.g. under massive score
  *              ties).  A diagnostic of slow calls; results are exact either
  *              way.  The caller clears it; it is updated in stream order.
  */

@@ -8,7 +8,8 @@
 // at every entry, so the scorer must be light).  Score (DSA form):
 //     I[t,s] = sum_h w[t,h] * relu(<qI[t,h], kI[s]>),   h ascending, fp32 fma chain.
 // Selection: the min(k, n_vis) largest scores, ties to the lower entry index,
-// written followed by -1 padding (the order within a row is unspecified).
+// written in a canonical order (grouped by (entry / 32) % 8, the groups in
+// ascending order, ascending within each group) followed by -1 padding.
 //
 // Design for CDNA4
 //  * A work-group serves QT query tokens: 4 waves and 2 tokens for rows of up
@@ -41,6 +42,13 @@
 //    the exact streaming method (buffers shrunk to exactly k whenever they
 //    fill).
 //  * Tokens whose visible entries all fit in k skip scoring.
+//  * Few tokens over long entry lists (decode) split each row over
+//    partitions of 16384 entries: each partition keeps its highest scores by
+//    a cut of its own (a histogram over its scores held in LDS), and a
+//    selection work-group per row checks that the cuts kept every top-k
+//    member before it selects (see index_split_cut_kernel).
+#include <cmath>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -101,6 +109,7 @@ struct TopkSmem {
   int ties;
   uint32_t vcnt[QT][8];       // kept entries per canonical group (output)
   int staged;                 // split path: kept entries staged for sorting
+  int above;                  // split path: candidates at or above the row's bound
   uint32_t sel[4];
 };
 
@@ -858,8 +867,9 @@ __device__ __forceinline__ void init_scorer(Scorer<FMT>& sc, const IndexParams& 
 // the row's threshold, then the candidates the partitions append.
 struct SplitRow {
   int cnt;
-  float thr;
-  int pad[2];
+  float thr;      // the sampled threshold (rows scored against one threshold)
+  uint32_t tkey;  // order key every entry left out is below (rows cut per partition)
+  int pad;
   uint2 cand[kCap];
 };
 static_assert(sizeof(SplitRow) == kSplitRowBytes, "split workspace row size");
@@ -937,7 +947,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   const bool two_stage = sampling && S >= 32;
   const int target_a = two_stage ? 4 * target : target;
   if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = -__builtin_inff(); }
-  if (tid == 0) { sm.fallback = 0; sm.ties = 0; sm.staged = 0; }
+  if (tid == 0) { sm.fallback = 0; sm.ties = 0; sm.staged = 0; sm.above = 0; }
   if (SPLIT != 2 && sampling) {
     // sample tiles wave, wave + kWaves, ...; kDepth tiles in flight per wave
     const int ntile = ((maxnv + S - 1) / S + 31) / 32;
@@ -1058,15 +1068,25 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   }
   __syncthreads();
   if constexpr (SPLIT == 1) {
-    if (tid == 0) { srow->cnt = 0; srow->thr = sm.thr[0]; }
+    if (tid == 0) { srow->cnt = 0; srow->thr = sm.thr[0]; srow->tkey = 0u; }
     return;
   }
 
   if constexpr (SPLIT == 2) {
-    // ---- the candidates appended by the partitions, laid out as the regions
+    // ---- the candidates appended by the partitions, laid out as the regions;
+    // count those at or above the row's bound (every entry left out lies
+    // below it, so with k of them the top-k are all candidates)
     const int cnt = srow->cnt;
+    const uint32_t tkey = srow->tkey;
     const int cc = cnt < kCap ? cnt : kCap;
-    for (int i = tid; i < cc; i += kThreads) sm.cand[0][i] = srow->cand[i];
+    int ab = 0;
+    for (int i = tid; i < cc; i += kThreads) {
+      const uint2 v = srow->cand[i];
+      sm.cand[0][i] = v;
+      ab += okey(v.x) >= tkey ? 1 : 0;
+    }
+    for (int off = 32; off >= 1; off >>= 1) ab += __shfl_xor(ab, off);
+    if (lane == 0 && ab) atomicAdd(&sm.above, ab);
     if (tid < kWaves) {
       const int c0 = cc - tid * kReg;
       sm.wcnt[tid][0] = c0 < 0 ? 0 : (c0 > kReg ? kReg : c0);
@@ -1129,7 +1149,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
     }
     sm.cnt[wave] = c;
     const int want = nv[wave] < p.k ? nv[wave] : p.k;
-    if (over || c < want) atomicOr(&sm.fallback, 1);
+    if (over || c < want || (SPLIT == 2 && sm.above < want)) atomicOr(&sm.fallback, 1);
   }
   __syncthreads();
 
@@ -1309,8 +1329,206 @@ __global__ __launch_bounds__(256) void index_split_score_kernel(IndexParams p, i
   }
 }
 
+// Split path, one-pass partition stage (rows of at most kCutMaxN entries):
+// one work-group of 8 waves scores entries [part * kCutPart, ...) of one
+// token row into LDS and keeps about r_keep of its highest: a 256-bin
+// histogram over the part's score range [lo, hi] (one more level over the
+// cut bin when that bin is crowded) gives a cut, and every entry at or above
+// the cut is appended to the row's candidates with one atomic per
+// work-group.  The bin of a score is monotone in the score, so every entry
+// left out lies below the smallest kept one, t_p; the row's maximum of the
+// t_p goes to the workspace row, and the selection stage takes the row's
+// exact path unless at least k candidates reach it (then every member of the
+// row's top-k is a candidate, ties included).
+constexpr int kCutPart = 16384;
+constexpr int kCutMaxN = 16 * kCutPart;
+constexpr int kCutKeep = 1024;  // kept entries per part staged in LDS
+
+__global__ __launch_bounds__(256) void index_split_init_kernel(IndexParams p, int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r < rows) {
+    SplitRow* s = (SplitRow*)p.ws + r;
+    s->cnt = 0;
+    s->thr = 0.0f;
+    s->tkey = 0u;
+  }
+}
+
+// Bin of score x in [lo, hi] (256 bins of width 1 / inv), monotone in x:
+// (x - lo) * inv is rounded monotonically, then clamped to [0, 255].
+__device__ __forceinline__ int cut_bin(float x, float lo, float inv) {
+  const float f = (x - lo) * inv;
+  return !(f > 0.0f) ? 0 : (f >= 255.0f ? 255 : (int)f);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(512) void index_split_cut_kernel(IndexParams p, int parts, int r_keep) {
+  constexpr int W = 8, T = 64 * W;
+  __shared__ float ssc[kCutPart];
+  __shared__ uint2 kept[kCutKeep];
+  __shared__ uint32_t hist[256];
+  __shared__ float red[2][W];
+  __shared__ int s_cut[2], s_nkept, s_base;
+  __shared__ uint32_t s_tmin;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x / parts;
+  const int part = (int)(blockIdx.x % parts);
+  const int b = (int)(row / p.n), q = (int)(row % p.n);
+  SplitRow* srow = (SplitRow*)p.ws + row;
+  const int64_t c = (p.q_pos0 + q + 1) / p.m;
+  const int nv = (int)(c < p.N ? c : p.N);
+  const int e0 = part * kCutPart;
+  const int e1 = nv < e0 + kCutPart ? nv : e0 + kCutPart;
+  if (nv <= p.k || e0 >= e1) return;  // the selection stage writes 0 .. nv-1 / past the row
+  const int n = e1 - e0;
+  Scorer<FMT> sc;
+  int nvl[2];
+  init_scorer<1, FMT>(sc, p, b, q, nvl);
+  const int l32 = lane & 31;
+  if (tid < 256) hist[tid] = 0u;
+  if (tid == 0) { s_nkept = 0; s_tmin = 0xffffffffu; }
+
+  // ---- score the part into LDS (token 0 lives in lanes 0..31)
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  {
+    const int ntile = (n + 31) >> 5;
+    BTile<FMT> t[kDepth];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      t[u] = sc.load(e0 + (wave + u * W) * 32 + l32);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int tile0 = wave; tile0 < ntile; tile0 += kDepth * W) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int tile = tile0 + u * W;
+        const f32x16 C = sc.mfma(t[u]);
+        t[u] = sc.load(e0 + (tile + kDepth * W) * 32 + l32);
+        float I[2];
+        sc.template epilogue<1>(C, I);
+        // the MFMA's result is used outside the lane mask below (see the
+        // sampling loop of index_topk_kernel)
+        asm volatile("" : "+v"(I[0]));
+        const int i = tile * 32 + l32;
+        if (lane < 32 && i < n) {
+          ssc[i] = I[0];
+          lo = fminf(lo, I[0]);
+          hi = fmaxf(hi, I[0]);
+        }
+      }
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, off));
+    hi = fmaxf(hi, __shfl_xor(hi, off));
+  }
+  if (lane == 0) { red[0][wave] = lo; red[1][wave] = hi; }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < W; ++w) { lo = fminf(lo, red[0][w]); hi = fmaxf(hi, red[1][w]); }
+  const float inv = 256.0f / (hi - lo);
+  const bool spread = hi > lo && inv < __builtin_inff();
+
+  // highest bin b with (bins >= b) + base >= need; -1 if none (wave 0)
+  auto find_cut = [&](int need, int& above) -> int {
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = hist[4 * lane + i];
+    const uint32_t s4 = h[0] + h[1] + h[2] + h[3];
+    uint32_t suf = s4;  // bins 4 * lane and above
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_down(suf, off);
+      if (lane + off < 64) suf += y;
+    }
+    uint32_t S = suf - s4;  // bins above this lane's four
+    int bl = -1, ab = 0;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      if (bl < 0 && S + h[i] >= (uint32_t)need) { bl = 4 * lane + i; ab = (int)S; }
+      S += h[i];
+    }
+    int best = bl;
+    for (int off = 32; off >= 1; off >>= 1) best = max(best, __shfl_xor(best, off));
+    above = best >= 0 ? __shfl(ab, best >> 2) : 0;
+    return best;
+  };
+
+  int cut = 0, sub = 0;
+  float lo2 = 0.0f, inv2 = 0.0f;
+  if (spread) {
+    for (int i = tid; i < n; i += T) atomicAdd(&hist[cut_bin(ssc[i], lo, inv)], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      int above = 0;
+      const int cb = find_cut(r_keep, above);
+      const int crowd = cb >= 0 ? (int)hist[cb] + above - r_keep : 0;
+      // still needed from the cut bin when it holds more than 16 extra
+      if (lane == 0) { s_cut[0] = cb < 0 ? 0 : cb; s_cut[1] = (cb >= 0 && crowd > 16) ? r_keep - above : 0; }
+    }
+    __syncthreads();
+    cut = s_cut[0];
+    const int need2 = inv * 256.0f < __builtin_inff() ? s_cut[1] : 0;
+    if (need2 > 0) {
+      // the cut bin is crowded: a second histogram over its range
+      lo2 = lo + (float)cut / inv;
+      inv2 = inv * 256.0f;
+      if (tid < 256) hist[tid] = 0u;
+      __syncthreads();
+      for (int i = tid; i < n; i += T) {
+        const float x = ssc[i];
+        if (cut_bin(x, lo, inv) == cut) atomicAdd(&hist[cut_bin(x, lo2, inv2)], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        int above = 0;
+        const int sb = find_cut(need2, above);
+        if (lane == 0) s_cut[1] = sb < 0 ? 0 : sb;
+      }
+      __syncthreads();
+      sub = s_cut[1];
+    }
+  }
+  const bool drops = spread && (cut > 0 || sub > 0);
+
+  // ---- append the kept entries to LDS, then to the row with one atomic
+  uint32_t tmin = 0xffffffffu;
+  for (int i0 = 0; i0 < n; i0 += T) {
+    const int i = i0 + tid;
+    const bool in = i < n;
+    const float x = ssc[in ? i : 0];
+    bool kp = in;
+    if (spread && in) {
+      const int b1 = cut_bin(x, lo, inv);
+      kp = b1 > cut || (b1 == cut && (sub == 0 || cut_bin(x, lo2, inv2) >= sub));
+    }
+    const uint64_t bal = ballot(kp);
+    int base = 0;
+    if (lane == 0 && bal) base = atomicAdd(&s_nkept, __builtin_popcountll(bal));
+    base = __builtin_amdgcn_readfirstlane(base);
+    const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (kp) {
+      if (pos < kCutKeep) kept[pos] = make_uint2(__float_as_uint(x), (uint32_t)(e0 + i));
+      tmin = min(tmin, okey(__float_as_uint(x)));
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, off));
+  if (lane == 0) atomicMin(&s_tmin, tmin);
+  __syncthreads();
+  if (tid == 0) {
+    const int m = s_nkept;
+    // too many kept for the staging area: count past the row's capacity (exact path)
+    s_base = m > kCutKeep ? -1 : atomicAdd(&srow->cnt, m);
+    if (m > kCutKeep) atomicAdd(&srow->cnt, kCap + 1);
+    if (drops) atomicMax(&srow->tkey, s_tmin);
+  }
+  __syncthreads();
+  const int m = s_nkept, base = s_base;
+  if (base >= 0)
+    for (int i = tid; i < m && base + i < kCap; i += T) srow->cand[base + i] = kept[i];
+}
+
 // Few query rows over long entry lists (decode): the split path keeps every
-// CU busy (threshold per row, entries scored by partitions, selection per row).
+// CU busy (entries scored by partitions, selection per row).
 constexpr int kSplitPart = 8192;
 // The choice depends on the rows of one batch entry only, never on B.
 static bool split_path(int B, int n, int64_t q_pos0, int N, int m) {
@@ -1341,10 +1559,22 @@ static hipError_t launch_split(const IndexParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.B * p.n;
   int64_t nv = (p.q_pos0 + p.n) / p.m;
   if (nv > p.N) nv = p.N;
-  const int parts = (int)((nv + kSplitPart - 1) / kSplitPart);
-  hipLaunchKernelGGL((index_topk_kernel<1, FMT, 1>), dim3((unsigned)rows), dim3(Shape<1>::T), 0, stream, p);
-  hipLaunchKernelGGL((index_split_score_kernel<FMT>), dim3((unsigned)(rows * parts)), dim3(256), 0, stream, p,
-                     parts, kSplitPart);
+  if (nv <= kCutMaxN) {
+    // one pass: each partition cuts its own scores; r_keep covers the part's
+    // expected share of the top-k plus six standard deviations
+    const int parts = (int)((nv + kCutPart - 1) / kCutPart);
+    const double share = (double)p.k * kCutPart / (double)nv;
+    const int r_keep = (int)std::ceil(share + 6.0 * std::sqrt(share) + 8.0);
+    hipLaunchKernelGGL(index_split_init_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p, rows);
+    hipLaunchKernelGGL((index_split_cut_kernel<FMT>), dim3((unsigned)(rows * parts)), dim3(512), 0, stream, p, parts,
+                       r_keep);
+  } else {
+    // sampled threshold per row, then partitions scored against it
+    const int parts = (int)((nv + kSplitPart - 1) / kSplitPart);
+    hipLaunchKernelGGL((index_topk_kernel<1, FMT, 1>), dim3((unsigned)rows), dim3(Shape<1>::T), 0, stream, p);
+    hipLaunchKernelGGL((index_split_score_kernel<FMT>), dim3((unsigned)(rows * parts)), dim3(256), 0, stream, p,
+                       parts, kSplitPart);
+  }
   hipLaunchKernelGGL((index_topk_kernel<1, FMT, 2>), dim3((unsigned)rows), dim3(Shape<1>::T), 0, stream, p);
   return hipGetLastError();
 }

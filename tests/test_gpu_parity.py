@@ -145,13 +145,17 @@ def _index_case(orc, rng, B, n, N, H_I, k, q_pos0, fmt, m=4, dup_rows=0, prequan
     (1, 64, 2000, 8, 100, 8000, "mxfp4", {"prequant": True}),
     (1, 301, 75, 4, 16, 0, "bf16", {}),               # bf16 indexer, 4 heads
     (1, 40, 5000, 1, 300, 20000, "bf16", {}),
-    # split path (few query rows over >= 65536 visible entries): threshold per
-    # row, partitions append candidates, selection per row
+    # split path (few query rows over >= 65536 visible entries): partitions of
+    # up to 262144 visible entries each keep their highest scores by their
+    # own cut; longer rows take a sampled threshold per row first; then the
+    # selection per row
     (1, 9, 70000, 8, 2048, 280000 - 9, "mxfp4", {}),     # long rows: 4-token work-groups
     (3, 1, 70000, 8, 512, 280000, "mxfp4", {}),          # ragged last partition
     (2, 4, 90000, 8, 2048, 280000 - 4, "mxfp4", {}),     # entries past the causal bound
     (1, 2, 70000, 8, 512, 280000, "mxfp4", {"dup_rows": 3, "fallback": True}),  # candidates overflow
     (2, 1, 66000, 4, 300, 264000, "bf16", {}),
+    (2, 1, 300000, 8, 2048, 1200000, "mxfp4", {}),     # past 262144 entries: sampled threshold first
+    (1, 3, 262144, 8, 2048, 1048576 - 3, "mxfp4", {}),  # 16 full partitions
 ])
 def test_index_topk_matches_oracle(orc, B, n, N, H_I, k, q_pos0, fmt, extra):
     print("index case B=%d n=%d N=%d H_I=%d k=%d pos0=%d %s %s" % (B, n, N, H_I, k, q_pos0, fmt, extra),
