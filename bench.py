@@ -920,6 +920,8 @@ def main():
         "dtype": res["dtype"], "data": "synthetic (seeded, numpy default_rng)", "config": res["config"],
         "roofline": res["roofline"], "kernels": res["kernels"], "cpu_baseline": res["cpu_baseline"],
     }
+    if "topk_fallbacks_per_call" in res:
+        line["topk_fallbacks_per_call"] = res["topk_fallbacks_per_call"]
     if args.config is None and not args.no_extra:
         line["workloads"] = {name: measure(c, args) for name, c in EXTRA}
     print(json.dumps(line), flush=True)

@@ -56,8 +56,9 @@ def assert_close(gpu_bits, ref, what=""):
 
 
 def canon_idx(rows):
-    """Top-k rows in a canonical form: the selected indices ascending, then
-    the -1 padding.  The library leaves the order within a row unspecified."""
+    """Top-k rows as sets in the oracle's form: the selected indices
+    ascending, then the -1 padding (the library's own order is checked
+    separately by canonical_rows)."""
     rows = np.asarray(rows)
     out = np.full_like(rows, -1)
     for r in np.ndindex(rows.shape[:-1]):

@@ -123,7 +123,7 @@ def _index_case(orc, rng, B, n, N, H_I, k, q_pos0, fmt, m=4, dup_rows=0, prequan
     for b in range(B):
         ref = orc.index_topk_rows(qdec[b], w[b], kdec[b], m, q_pos0, rows, k)
         if fmt == "mxfp4":
-            # the oracle's rows are ascending; the library's order is unspecified
+            # the oracle's rows are ascending: compare the sets
             bad = np.nonzero(~np.all(canon_idx(got[b]) == ref, axis=1))[0]
             assert bad.size == 0, "rows %s differ (first: gpu %s ref %s)" % (
                 bad[:5], got[b][bad[0]][:8], ref[bad[0]][:8])
