@@ -12,9 +12,9 @@
 // ascending order, ascending within each group) followed by -1 padding.
 //
 // Design for CDNA4
-//  * A work-group serves QT query tokens: 4 waves and 2 tokens for rows of up
-//    to 64K entries (two work-groups per CU), 8 waves and 4 tokens for
-//    longer rows, 8 waves and 1 token for single-token decode.  Scores: one
+//  * A work-group of 8 waves serves QT query tokens: 2 tokens for rows of up
+//    to 64K entries (two work-groups per CU), 4 tokens for longer rows, 1
+//    token for single-token decode.  Scores: one
 //    v_mfma_scale_f32_32x32x64_f8f6f4 (MXFP4) or four
 //    v_mfma_f32_32x32x16_bf16 per 32 entries.  The 32 A rows are 4 token
 //    slots x 8 heads, placed so each lane's accumulator rows are all 8 heads
@@ -55,13 +55,14 @@
 namespace csa {
 
 constexpr int kCap = 4096;             // candidate buffer per token
-// Work-group shape for QT tokens: 8 waves (2 per SIMD) for 1 or 4 tokens; 4
-// waves for 2 tokens, whose 70 KB of LDS lets two work-groups share a CU so
-// that one's scoring overlaps the other's selections.  Each lane scores TPL
-// tokens of a tile (all 64 lanes are busy once QT >= 2).
+// Work-group shape for QT tokens: 8 waves.  With 2 tokens the 70 KB of LDS
+// lets two work-groups share a CU (4 waves per SIMD), so one's scoring
+// overlaps the other's selections, and each token's selection is shared by
+// 4 waves.  Each lane scores TPL tokens of a tile (all 64 lanes are busy
+// once QT >= 2).
 template <int QT>
 struct Shape {
-  static constexpr int W = QT == 2 ? 4 : 8;  // waves per work-group
+  static constexpr int W = 8;  // waves per work-group
   static constexpr int T = 64 * W;          // threads
   static constexpr int Tile = 32 * W;       // entries per round of the work-group
   static constexpr int Reg = kCap / W;      // per-wave candidate region of a token's buffer

@@ -67,7 +67,7 @@ def test_config3_csa_full(orc):
     wl.step()
     # rows whose k-th score falls on the point mass of exact zeros (every head
     # product <= 0 under mostly negative head weights) may take the exact
-    # path: allow one work-group in 4096 (30,720 work-groups here)
+    # path: allow at most 8 work-groups (65,536 work-groups of 2 rows here)
     nfb = int(wl.fallbacks.item())
     assert nfb <= 8, "%d indexer work-groups took the exact streaming path" % nfb
     torch.cuda.synchronize()
