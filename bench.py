@@ -44,8 +44,8 @@ PEAK = {"bf16": 2500.0, "fp4": 10100.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s
 # taken on: a changed kernel reports null until it is measured again.  The
 # summaries are profiles/<workload>_hbm_counters.txt.
 TRAFFIC = {
-    ('csa_attend', 3): {"sha256": "31c20eb0ccd4bdd7bff40d38b3beb93075540dbbb51dc4aebc70dedb40a6100d", "bytes": 1.95e+10},  # csa_prefill_128k
-    ('csa_index_topk', 3): {"sha256": "3819c0636307e8f2a5bc14344ed5610cfd87052a2e8153e05add613974a84c6f", "bytes": 1.225e+09},  # csa_prefill_128k
+    ('csa_attend', 3): {"sha256": "31c20eb0ccd4bdd7bff40d38b3beb93075540dbbb51dc4aebc70dedb40a6100d", "bytes": 1.939e+10},  # csa_prefill_128k
+    ('csa_index_topk', 3): {"sha256": "b271a0477a3b8c97aa83e895db9bcad8be75f05509b2745cabd97ace7e95350a", "bytes": 1.222e+09},  # csa_prefill_128k
     ('csa_compress', 3): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 7.299e+07},  # csa_prefill_128k
     ('csa_rope_rows', 3): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 6.719e+07},  # csa_prefill_128k
     ('hca_attend', 2): {"sha256": "31c20eb0ccd4bdd7bff40d38b3beb93075540dbbb51dc4aebc70dedb40a6100d", "bytes": 1.142e+09},  # hca_32k
