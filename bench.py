@@ -334,7 +334,7 @@ class CsaLayer:
         self.fallbacks = torch.zeros(1, dtype=torch.int32, device="cuda")  # exact-path work-groups
         self.kernels = ["csa_compress", "csa_rope_rows", "csa_index_topk", "csa_attend"]
         self.kv_rot = torch.empty_like(self.kv)
-        # algorithmic work (measurement)
+        # algorithmic work: indexer pairs (query, visible entry) and attention keys
         t = np.arange(n, dtype=np.int64)
         nv = np.minimum(N, (t + 1) // self.m)
         pairs = int(nv.sum())
