@@ -51,7 +51,7 @@ TRAFFIC = {
     ('hca_attend', 2): {"sha256": "31c20eb0ccd4bdd7bff40d38b3beb93075540dbbb51dc4aebc70dedb40a6100d", "bytes": 1.142e+09},  # hca_32k
     ('csa_compress', 2): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 8.835e+06},  # hca_32k
     ('csa_rope_rows', 2): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 1.685e+07},  # hca_32k
-    ('csa_index_topk', 4): {"sha256": "3819c0636307e8f2a5bc14344ed5610cfd87052a2e8153e05add613974a84c6f", "bytes": 6.093e+08},  # csa_decode_1m
+    ('csa_index_topk', 4): {"sha256": "b271a0477a3b8c97aa83e895db9bcad8be75f05509b2745cabd97ace7e95350a", "bytes": 6.093e+08},  # csa_decode_1m
     ('csa_attend', 4): {"sha256": "31c20eb0ccd4bdd7bff40d38b3beb93075540dbbb51dc4aebc70dedb40a6100d", "bytes": 1.037e+08},  # csa_decode_1m
 }
 TRAFFIC[("csa_project_in", "proj")] = {  # the GEMM (1.085e9) + the indexer-query kernel (9.7e6)
