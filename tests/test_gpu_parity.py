@@ -405,3 +405,46 @@ def test_config1_layer_end_to_end(orc):
                               sink=sink)
     mx, mr = assert_close(host_bits(out)[0], ref_out, "config 1")
     print("config 1: max-abs %.3g mean-rel %.3g" % (mx, mr))
+
+
+# ---------------------------------------------------------- degenerate rows --
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_attention_rows_without_keys(orc, fmt):
+    """Rows whose key set is empty give a zero output, as the oracle's
+    softmax over nothing does: HCA rows before the first complete entry with
+    no window and no sink, and CSA rows whose top-k slots all hold -1 (bf16
+    entries: the ring kernel; FP8 entries with k = 512: the per-token split).
+    A row whose only term is the sink is zero too (the sink has no value)."""
+    rng = np.random.default_rng(91)
+    B, n, H, m = 2, 12, 40, 16
+    q = _bf16(rng, (B, n, H, 128), 1 / np.sqrt(128))
+    ent = _bf16(rng, (B, 4, 128), 1 / np.sqrt(128))
+    win = _bf16(rng, (B, n, 128), 1 / np.sqrt(128))
+    sink = rng.standard_normal(H).astype(np.float32)
+    # HCA: t = 0 .. 11 < m - 1, so no entry is visible; no window
+    for sk in (None, sink):
+        out = L.hca_attend(dev(q), dev(ent), q_pos0=0, m=m, win_kv=dev(win), n_win=0,
+                           sink=None if sk is None else dev(sk))
+        torch.cuda.synchronize()
+        got = bf16_f64(host_bits(out))
+        assert not np.any(got), "HCA rows without keys (sink %s)" % (sk is not None)
+        ref = orc.attend_rows(q[0], 0, orc.bf16_to_f64(ent[0]), m, np.arange(n, dtype=np.int32), "hca",
+                              win=win[0], n_win=0, sink=sk)
+        assert not np.any(ref), "the oracle's empty rows"
+    # CSA: every idx slot -1, no window
+    k = 64 if fmt == "bf16" else 512
+    N = 600
+    idx = np.full((B, n, k), -1, np.int32)
+    if fmt == "bf16":
+        e = _bf16(rng, (B, N, 128), 1 / np.sqrt(128))
+        out = L.csa_attend(dev(q), dev(e), dev(idx), q_pos0=4 * N, m=4, win_kv=dev(win), n_win=0, sink=None)
+    else:
+        rows = oracle_compress_store(orc, _bf16(rng, (4 * N, 128), 1 / np.sqrt(128)),
+                                     rng.standard_normal(8).astype(np.float32), 4, 1, entry_fmt="fp8")
+        out = L.csa_attend(dev(q), dev(np.stack([rows["entries"]] * B)), dev(idx), q_pos0=4 * N, m=4,
+                           win_kv=dev(win), n_win=0, sink=None,
+                           entries_rope=dev(np.stack([rows["entries_rope"]] * B)),
+                           entry_scale=dev(np.stack([rows["entry_scale"]] * B)))
+    torch.cuda.synchronize()
+    assert not np.any(bf16_f64(host_bits(out))), "CSA rows with no selected entry (%s)" % fmt
