@@ -24,10 +24,10 @@
 //    sequential evaluation).  Entry rows come through range-checked buffer
 //    loads, four tiles in flight per wave.
 //  * Selection in one scoring pass:
-//      1. a strided sample of the visible entries (sized so that about
-//         kMinAbove samples lie above the cut) is scored; each token's
-//         threshold is the sample quantile that leaves about k + 850 entries
-//         above it;
+//      1. a sample of the visible entries (one in S, in runs of 8 consecutive
+//         entries; sized so that about kMinAbove samples lie above the cut)
+//         is scored; each token's threshold is the sample quantile that
+//         leaves about k + 850 entries above it;
 //      2. every entry is scored once; scores >= threshold are appended to the
 //         wave's private region of the token's LDS candidate buffer (ballot +
 //         mbcnt, counts in registers: no atomics);
@@ -368,10 +368,43 @@ __device__ __forceinline__ void group_extremes(TopkSmem<QT>& sm, const uint32_t 
 struct BinOut {
   uint32_t b, hb, above;
 };
+
+// The bin of the r-th largest key in a 256-bin histogram hc (bin 255 the
+// highest), counted from `above` keys known to lie above bin 255; every lane
+// of the wave calls it and gets the same result.
+__device__ __forceinline__ BinOut find_bin(const uint32_t* hc, uint32_t r, uint32_t above) {
+  const int lane = threadIdx.x & 63;
+  // lane l owns bins 252-4l .. 255-4l: a prefix sum over lanes counts the
+  // keys in bins >= the lane's lowest bin
+  const u32x4 hv = *(const u32x4*)(hc + 252 - 4 * lane);
+  const uint32_t c = hv[0] + hv[1] + hv[2] + hv[3];
+  const uint32_t incl = wave_prefix_sum(c) + above;
+  const uint64_t hit = ballot(incl >= r);
+  const int L = hit ? __builtin_ctzll(hit) : 63;
+  uint32_t acc = incl - c, d = 0u, hd = 0u;
+  if (lane == L) {
+    d = 252 - 4 * lane;
+    if (acc + hv[3] >= r) { d += 3; hd = hv[3]; }
+    else {
+      acc += hv[3];
+      if (acc + hv[2] >= r) { d += 2; hd = hv[2]; }
+      else {
+        acc += hv[2];
+        if (acc + hv[1] >= r) { d += 1; hd = hv[1]; }
+        else { acc += hv[1]; hd = hv[0]; }
+      }
+    }
+  }
+  BinOut o;
+  o.b = (uint32_t)__builtin_amdgcn_readlane((int)d, L);
+  o.above = (uint32_t)__builtin_amdgcn_readlane((int)acc, L);
+  o.hb = (uint32_t)__builtin_amdgcn_readlane((int)hd, L);
+  return o;
+}
 template <int QT, int NS>
 __device__ __forceinline__ BinOut group_bin(TopkSmem<QT>& sm, int buf, const uint32_t (&kr)[NS], uint32_t lo, int s,
                                             uint32_t r, uint32_t above, bool active) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
   const int j = wave % QT;
   uint32_t* hc = sm.hist[buf][j];
   if (active) {
@@ -385,34 +418,7 @@ __device__ __forceinline__ BinOut group_bin(TopkSmem<QT>& sm, int buf, const uin
     }
   }
   __syncthreads();
-  BinOut o{0u, 0u, above};
-  if (active) {
-    // lane l owns bins 252-4l .. 255-4l: a prefix sum over lanes counts the
-    // keys in bins >= the lane's lowest bin
-    const u32x4 hv = *(const u32x4*)(hc + 252 - 4 * lane);
-    const uint32_t c = hv[0] + hv[1] + hv[2] + hv[3];
-    const uint32_t incl = wave_prefix_sum(c) + above;
-    const uint64_t hit = ballot(incl >= r);
-    const int L = hit ? __builtin_ctzll(hit) : 63;
-    uint32_t acc = incl - c, d = 0u, hd = 0u;
-    if (lane == L) {
-      d = 252 - 4 * lane;
-      if (acc + hv[3] >= r) { d += 3; hd = hv[3]; }
-      else {
-        acc += hv[3];
-        if (acc + hv[2] >= r) { d += 2; hd = hv[2]; }
-        else {
-          acc += hv[2];
-          if (acc + hv[1] >= r) { d += 1; hd = hv[1]; }
-          else { acc += hv[1]; hd = hv[0]; }
-        }
-      }
-    }
-    o.b = (uint32_t)__builtin_amdgcn_readlane((int)d, L);
-    o.above = (uint32_t)__builtin_amdgcn_readlane((int)acc, L);
-    o.hb = (uint32_t)__builtin_amdgcn_readlane((int)hd, L);
-  }
-  return o;
+  return active ? find_bin(hc, r, above) : BinOut{0u, 0u, above};
 }
 
 // shift that maps [kmin, kmax] onto at most 256 bins
@@ -750,31 +756,36 @@ __device__ __forceinline__ void append(TopkSmem<QT>& sm, const bool pass[2], con
 }
 
 // Appends the passing lanes of a half-wave (token j) to this wave's private
-// region of the token's buffer.  The running count wcnt is uniform over the
-// half-wave and lives in a register: no LDS atomic, no cross-lane round trip.
+// region of the token's buffer.  The running counts of the two half-waves
+// (wc[0]: lanes 0..31, wc[1]: lanes 32..63) are wave-uniform and stay on the
+// scalar unit: no LDS atomic, no cross-lane round trip.
 template <int QT>
 __device__ __forceinline__ void append_private(TopkSmem<QT>& sm, bool vis, bool ge, uint32_t val, int e, int j,
-                                               int& wcnt) {
+                                               uint32_t (&wc)[2]) {
   constexpr int kReg = Shape<QT>::Reg;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   // the two compares' lane masks, combined on the scalar unit
   const uint64_t bal = ballot(vis) & ballot(ge);
   const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
-  // position = count + passing lanes below this one in its half-wave: the
-  // lower half counts bits of lo, the upper half bits of hi
-  const int pos = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lane < 32 ? lo : 0u, (uint32_t)wcnt));
+  const uint32_t nlo = (uint32_t)__builtin_popcount(lo), nhi = (uint32_t)__builtin_popcount(hi);
+  // position = count + passing lanes below this one in its half-wave; the
+  // upper half's mbcnt_lo counts every bit of lo, taken off its count first
+  const uint32_t base = lane < 32 ? wc[0] : wc[1] - nlo;
+  const int pos = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, base));
   if (vis && ge && pos < kReg) sm.cand[j][wave * kReg + pos] = make_uint2(val, (uint32_t)e);
-  wcnt += __builtin_popcount(lane < 32 ? lo : hi);
+  wc[0] += nlo;
+  wc[1] += nhi;
 }
 
 // Scorer of a work-group's QT query tokens q0 .. q0+QT-1 of batch row b:
 // the MFMA A operand (rows = (token, head); MXFP4 quantised in-kernel from
 // bf16 q when no scales are given), the head weights, and the entry-key
-// buffer descriptors.  nvl[tt]: visible entries of this lane's token
-// jl0 + tt (0 for tokens past n).
+// buffer descriptors.  nvq[j]: visible entries of token q0 + j (0 past n),
+// work-group uniform; nvl[tt]: the same for this lane's token jl0 + 2 tt.
 template <int QT, int FMT>
-__device__ __forceinline__ void init_scorer(Scorer<FMT>& sc, const IndexParams& p, int b, int q0, int nvl[2]) {
+__device__ __forceinline__ void init_scorer(Scorer<FMT>& sc, const IndexParams& p, int b, int q0,
+                                            const int (&nvq)[QT], int nvl[2]) {
   const int lane = threadIdx.x & 63;
 
   {
@@ -794,24 +805,39 @@ __device__ __forceinline__ void init_scorer(Scorer<FMT>& sc, const IndexParams& 
           for (int i = 0; i < 4; ++i) sc.A_fp4[i] = (int)cw[i];
           sc.a_scale = p.q_scale[qrow * 2 + (lane >> 5)];
         } else {
-          // quantise this (row, 32-element block) of the bf16 query to MXFP4
+          // quantise this (row, 32-element block) of the bf16 query to MXFP4.
+          // The block maximum is taken on the bf16 bit patterns (sign
+          // cleared, the integer order of finite values is their order), two
+          // halves at a time.  v_cvt_scalef32_pk_fp4_f32 divides by the
+          // scale 2^E and rounds to the nearest e2m1 value, ties to even,
+          // saturating at 6: the same codes as the bit-level encoder for
+          // every finite bf16 value and every E (a -0 code where that gives
+          // +0, which scores alike).  Word e of load i holds elements
+          // 8i + 2e (low half) and 8i + 2e + 1: they become byte e of code
+          // word i.
           const u32x4* src = (const u32x4*)((const uint16_t*)p.q + qrow * 64 + (lane >> 5) * 32);
-          float x[32];
+          u32x4 v[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const u32x4 v = src[i];
+          for (int i = 0; i < 4; ++i) v[i] = src[i];
+          u16x2 am = {0, 0};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { x[8 * i + 2 * e] = bf16lo(v[e]); x[8 * i + 2 * e + 1] = bf16hi(v[e]); }
-          }
-          float amax = 0.0f;
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-          if (amax > 0.0f) {
-            const int E = mxfp4_exponent(amax);
+            for (int e = 0; e < 4; ++e) am = __builtin_elementwise_max(am, __builtin_bit_cast(u16x2, v[i][e] & 0x7fff7fffu));
+          const uint32_t abits = am[0] > am[1] ? am[0] : am[1];
+          if (abits != 0u) {
+            const int E = mxfp4_exponent(bf16_to_f32(abits));
             sc.a_scale = E + 127;
+            const float scale = __builtin_ldexpf(1.0f, E);
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
-              sc.A_fp4[i >> 3] |= (int)(f32_to_e2m1(__builtin_ldexpf(x[i], -E)) << (4 * (i & 7)));
+            for (int i = 0; i < 4; ++i) {
+              uint32_t w = 0u;
+              w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo(v[i][0]), bf16hi(v[i][0]), scale, 0);
+              w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo(v[i][1]), bf16hi(v[i][1]), scale, 1);
+              w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo(v[i][2]), bf16hi(v[i][2]), scale, 2);
+              w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo(v[i][3]), bf16hi(v[i][3]), scale, 3);
+              sc.A_fp4[i] = (int)w;
+            }
           } else {
             sc.a_scale = 0;
           }
@@ -834,10 +860,9 @@ __device__ __forceinline__ void init_scorer(Scorer<FMT>& sc, const IndexParams& 
   for (int tt = 0; tt < 2; ++tt) {
     const int q = q0 + jl0 + 2 * tt;
     int v = 0;
-    if (jl0 + 2 * tt < QT && q < p.n) {
-      const int64_t c = (p.q_pos0 + q + 1) / p.m;
-      v = (int)(c < p.N ? c : p.N);
-    }
+#pragma unroll
+    for (int jj = 0; jj < QT; ++jj)
+      if (jj == jl0 + 2 * tt) v = nvq[jj];
     nvl[tt] = v;
 #pragma unroll
     for (int h = 0; h < 8; ++h)
@@ -864,6 +889,27 @@ __device__ __forceinline__ void init_scorer(Scorer<FMT>& sc, const IndexParams& 
   }
 }
 
+// Threshold sample of a work-group whose longest row sees maxnv > kCap
+// entries: one entry in S, taken in runs of kRun consecutive entries (run r
+// starts at entry r * kRun * S), so that a tile of 32 samples reads 4 runs
+// of rows rather than 32 scattered ones.  S is chosen so that about
+// kMinAbove samples lie above a cut leaving `target` entries of the row
+// above it (k + 850, at most kCap - 1024), with at most kCap samples.
+constexpr int kRun = 8;
+__device__ __forceinline__ int sample_entry(int i, int S) { return (i / kRun) * (kRun * S) + (i % kRun); }
+// samples of a row of nv entries: those with sample_entry(i) < nv, a prefix
+__device__ __forceinline__ int sample_count(int nv, int S) {
+  const int full = nv / (kRun * S), rest = nv - full * (kRun * S);
+  return full * kRun + (rest < kRun ? rest : kRun);
+}
+__device__ __forceinline__ int sample_stride(int maxnv, int k, int& target) {
+  target = k + 850;
+  if (target > kCap - 1024) target = kCap - 1024;
+  int64_t want = ((int64_t)kMinAbove * maxnv + target - 1) / target;
+  if (want > kCap) want = kCap;
+  return (int)((maxnv + want - 1) / want);
+}
+
 // Workspace row of the split path (few query rows over long entry lists):
 // the row's threshold, then the candidates the partitions append.
 struct SplitRow {
@@ -888,20 +934,24 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   const int b = blockIdx.x / nblk;
   const int q0 = (nblk - 1 - (int)(blockIdx.x % nblk)) * QT;  // heavy (late) blocks first
 
+  // visible entries of token q: (q_pos0 + q + 1) / m, capped at N (one
+  // division, then stepped token by token)
   int nv[QT];
   int maxnv = 0;
   bool all_small = true;
+  int64_t cq = (p.q_pos0 + q0 + 1) / p.m;
+  int rq = (int)(p.q_pos0 + q0 + 1 - cq * p.m);
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
     const int q = q0 + j;
     int v = 0;
     if (q < p.n) {
-      const int64_t c = (p.q_pos0 + q + 1) / p.m;
-      v = (int)(c < p.N ? c : p.N);
+      v = (int)(cq < p.N ? cq : p.N);
       if (v > p.k) all_small = false;
     }
     nv[j] = v;
     maxnv = v > maxnv ? v : maxnv;
+    if (++rq == p.m) { rq = 0; ++cq; }
   }
   SplitRow* srow = SPLIT != 0 ? (SplitRow*)p.ws + ((int64_t)b * p.n + q0) : nullptr;
   if (all_small) {
@@ -923,24 +973,17 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   // ---- A operand: rows (token, head); lane row = lane % 32, k-block = lane / 32
   Scorer<FMT> sc;
   int nvl[2];
-  init_scorer<QT, FMT>(sc, p, b, q0, nvl);
+  init_scorer<QT, FMT>(sc, p, b, q0, nv, nvl);
   const int jl0 = lane >> 5;  // this lane's tokens: jl0 + 2 tt, tt < TPL
   const int l32 = lane & 31;
   const int grp_j = wave % QT, grp_h = wave / QT;  // this wave's token group and member index
   constexpr int G = kWaves / QT;                    // waves per token group
   constexpr int NS = kCap / G / 64;                 // register slots per lane in a group selection
 
-  // ---- phase 1: per-token thresholds from a strided sample (entry S*i)
+  // ---- phase 1: per-token thresholds from a sample (sample_entry(i, S))
   const bool sampling = maxnv > kCap;
-  int target = p.k + 850;
-  if (target > kCap - 1024) target = kCap - 1024;
-  int S = 1;
-  if (sampling) {
-    // about kMinAbove sampled entries above the threshold, at most kCap samples
-    int64_t want = ((int64_t)kMinAbove * maxnv + target - 1) / target;
-    if (want > kCap) want = kCap;
-    S = (int)((maxnv + want - 1) / want);
-  }
+  int target = 0;
+  const int S = sampling ? sample_stride(maxnv, p.k, target) : 1;
   // Sparser than 1/32, kCap samples leave too few above the cut for a
   // reliable count: the first sample then sets a low cut (about 4 x target
   // entries above it) and a 4x denser second sample, filtered by that cut,
@@ -951,11 +994,11 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   if (tid == 0) { sm.fallback = 0; sm.ties = 0; sm.staged = 0; sm.above = 0; }
   if (SPLIT != 2 && sampling) {
     // sample tiles wave, wave + kWaves, ...; kDepth tiles in flight per wave
-    const int ntile = ((maxnv + S - 1) / S + 31) / 32;
+    const int ntile = (sample_count(maxnv, S) + 31) / 32;
     BTile<FMT> t[kDepth];
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
-      t[u] = sc.load(S * ((wave + u * kWaves) * 32 + l32));
+      t[u] = sc.load(sample_entry((wave + u * kWaves) * 32 + l32, S));
       __builtin_amdgcn_sched_barrier(0);  // issue order = consumption order (tight waits)
     }
     for (int tile0 = wave; tile0 < ntile; tile0 += kDepth * kWaves) {
@@ -964,7 +1007,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
         // unconditional: tiles past the end store nothing (e >= nvl)
         const int tile = tile0 + u * kWaves;
         const f32x16 C = sc.mfma(t[u]);
-        t[u] = sc.load(S * ((tile + kDepth * kWaves) * 32 + l32));
+        t[u] = sc.load(sample_entry((tile + kDepth * kWaves) * 32 + l32, S));
         float I[2];
         sc.template epilogue<TPL>(C, I);
         // The MFMA takes operands from all 64 lanes.  Its result must be used
@@ -973,7 +1016,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
         // lanes would feed stale registers.
         asm volatile("" : "+v"(I[0]), "+v"(I[1]));
         const int i = tile * 32 + l32;
-        const int e = S * i;
+        const int e = sample_entry(i, S);
 #pragma unroll
         for (int tt = 0; tt < TPL; ++tt) {
           const int j = jl0 + 2 * tt;
@@ -984,7 +1027,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
     __syncthreads();
     // sample quantile: sample i of token j sits in slot m of member h, lane
     // l with i = (m * G + h) * 64 + l, so every member holds a share
-    const int nsj = (q0 + grp_j < p.n && nv[grp_j] > kCap) ? (nv[grp_j] + S - 1) / S : 0;
+    const int nsj = (q0 + grp_j < p.n && nv[grp_j] > kCap) ? sample_count(nv[grp_j], S) : 0;
     uint32_t kr[NS];
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
@@ -1007,15 +1050,15 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
         thr_a[tt] = (j < QT) ? sm.thr[j < QT ? j : 0] : 0.0f;
         asm volatile("" : "+v"(thr_a[tt]));
       }
-      // second sample (entries SB*i) filtered by the first cut into the
+      // second sample (sample_entry(i, SB)) filtered by the first cut into the
       // wave-private regions of the token buffers
       const int SB = S / 4;
-      const int ntile_b = ((maxnv + SB - 1) / SB + 31) / 32;
-      int wc2[2] = {0, 0};
+      const int ntile_b = (sample_count(maxnv, SB) + 31) / 32;
+      uint32_t wc2[2][2] = {{0u, 0u}, {0u, 0u}};
       BTile<FMT> t[kDepth];
 #pragma unroll
       for (int u = 0; u < kDepth; ++u) {
-        t[u] = sc.load(SB * ((wave + u * kWaves) * 32 + l32));
+        t[u] = sc.load(sample_entry((wave + u * kWaves) * 32 + l32, SB));
         __builtin_amdgcn_sched_barrier(0);
       }
       for (int tile0 = wave; tile0 < ntile_b; tile0 += kDepth * kWaves) {
@@ -1023,19 +1066,21 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
         for (int u = 0; u < kDepth; ++u) {
           const int tile = tile0 + u * kWaves;
           const f32x16 C = sc.mfma(t[u]);
-          t[u] = sc.load(SB * ((tile + kDepth * kWaves) * 32 + l32));
+          t[u] = sc.load(sample_entry((tile + kDepth * kWaves) * 32 + l32, SB));
           float I[2];
           sc.template epilogue<TPL>(C, I);
-          const int e = SB * (tile * 32 + l32);
+          const int e = sample_entry(tile * 32 + l32, SB);
 #pragma unroll
           for (int tt = 0; tt < TPL; ++tt)
             append_private<QT>(sm, e < nvl[tt], I[tt] >= thr_a[tt], __float_as_uint(I[tt]), e, jl0 + 2 * tt, wc2[tt]);
         }
       }
-      if (l32 == 0) {
+      if (lane == 0) {
 #pragma unroll
         for (int tt = 0; tt < TPL; ++tt)
-          if (jl0 + 2 * tt < QT) sm.wcnt[wave][jl0 + 2 * tt] = wc2[tt];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            if (hf + 2 * tt < QT) sm.wcnt[wave][hf + 2 * tt] = (int)wc2[tt][hf];
       }
       __syncthreads();
       // cut of the second sample among the kept ones (regions as in the final selection)
@@ -1058,7 +1103,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
           kb[sl] = pos < cw ? okey(x) : 0u;
         }
       }
-      const int nsb = nsj > 0 ? (nv[grp_j] + SB - 1) / SB : 0;
+      const int nsb = nsj > 0 ? sample_count(nv[grp_j], SB) : 0;
       const int rb = nsb > 0 ? (int)(((int64_t)target * nsb + nv[grp_j] - 1) / nv[grp_j]) : 0;
       // too few kept (the first cut was too high): keep the first cut
       const bool act = nsj > 0 && rb >= 1 && kept >= rb;
@@ -1113,7 +1158,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
       // a token's buffer holds that token's candidates of those tiles in
       // ascending entry order.
       const int ecol = wave * 32 + l32;
-      int wcnt[2] = {0, 0};
+      uint32_t wcnt[2][2] = {{0u, 0u}, {0u, 0u}};
       BTile<FMT> t[kDepth];
   #pragma unroll
       for (int u = 0; u < kDepth; ++u) {
@@ -1133,10 +1178,12 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
             append_private<QT>(sm, e < nvl[tt], I[tt] >= thr2[tt], __float_as_uint(I[tt]), e, jl0 + 2 * tt, wcnt[tt]);
         }
       }
-      if (l32 == 0) {
+      if (lane == 0) {
   #pragma unroll
         for (int tt = 0; tt < TPL; ++tt)
-          if (jl0 + 2 * tt < QT) sm.wcnt[wave][jl0 + 2 * tt] = wcnt[tt];
+  #pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            if (hf + 2 * tt < QT) sm.wcnt[wave][hf + 2 * tt] = (int)wcnt[tt][hf];
       }
     }
   }
@@ -1299,7 +1346,8 @@ __global__ __launch_bounds__(256) void index_split_score_kernel(IndexParams p, i
   if (e0 >= e1) return;
   Scorer<FMT> sc;
   int nvl[2];
-  init_scorer<1, FMT>(sc, p, b, q, nvl);
+  const int nvq[1] = {nv};
+  init_scorer<1, FMT>(sc, p, b, q, nvq, nvl);
   const int l32 = lane & 31;
   const int ntile = (e1 - e0 + 31) / 32;
   BTile<FMT> t[kDepth];
@@ -1384,7 +1432,8 @@ __global__ __launch_bounds__(512) void index_split_cut_kernel(IndexParams p, int
   const int n = e1 - e0;
   Scorer<FMT> sc;
   int nvl[2];
-  init_scorer<1, FMT>(sc, p, b, q, nvl);
+  const int nvq[1] = {nv};
+  init_scorer<1, FMT>(sc, p, b, q, nvq, nvl);
   const int l32 = lane & 31;
   if (tid < 256) hist[tid] = 0u;
   if (tid == 0) { s_nkept = 0; s_tmin = 0xffffffffu; }
