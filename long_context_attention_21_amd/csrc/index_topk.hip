@@ -1300,9 +1300,50 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
     int32_t* o = p.idx_out + ((int64_t)b * p.n + (live ? q : 0)) * p.k;
     if constexpr (SPLIT == 0) {
       emit_canonical<QT, NS>(sm, live, ir, keep, kk, p.k, o);
+    } else if (nv[0] <= 64 * kCap) {
+      // the split path's candidates arrived in atomic order.  Rows of at
+      // most 64 kCap entries: the kept entries become a bitmap in the (free)
+      // candidate buffer, one 32-bit word per 32-entry tile, read in the
+      // canonical order: wave v takes the tiles T = 8 i + v, each lane a run
+      // of consecutive i, and writes their set bits in ascending order.
+      static_assert(kWaves == 8 && sizeof(sm.cand[0]) == 64 * kCap / 8, "one wave per canonical group, 32 entries a word");
+      uint32_t* bm = (uint32_t*)&sm.cand[0][0];
+      const int nw = (nv[0] + 31) >> 5;
+      __syncthreads();  // the selection's lists in the buffer are read
+      for (int i = tid; i < nw; i += kThreads) bm[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl)
+        if ((keep >> sl) & 1u) atomicOr(&bm[ir[sl] >> 5], 1u << (ir[sl] & 31u));
+      __syncthreads();
+      const int v = wave;
+      const int nwv = nw > v ? (nw - v + 7) >> 3 : 0;  // tiles of group v
+      const int per = (nwv + 63) >> 6;                 // per lane, at most 2 kCap / 512
+      const int i0 = lane * per;
+      uint32_t c = 0u;
+      for (int t = 0; t < per; ++t)
+        if (i0 + t < nwv) c += (uint32_t)__builtin_popcount(bm[8 * (i0 + t) + v]);
+      const uint32_t incl = wave_prefix_sum(c);
+      if (lane == 63) sm.vcnt[0][v] = incl;
+      __syncthreads();
+      uint32_t pos = incl - c;
+      for (int u = 0; u < v; ++u) pos += sm.vcnt[0][u];
+      if (live) {
+        for (int t = 0; t < per; ++t) {
+          const int i = i0 + t;
+          if (i >= nwv) break;
+          uint32_t w = bm[8 * i + v];
+          while (w) {
+            if (pos < (uint32_t)p.k) o[pos] = 32 * (8 * i + v) + __builtin_ctz(w);
+            ++pos;
+            w &= w - 1u;
+          }
+        }
+        for (int i = kk + tid; i < p.k; i += kThreads) o[i] = -1;
+      }
     } else {
-      // the split path's candidates arrived in atomic order: stage the kept
-      // entries and sort them into the canonical order
+      // longer rows: stage the kept entries and sort them into the canonical
+      // order
       int mine = 0;
 #pragma unroll
       for (int sl = 0; sl < NS; ++sl) mine += __builtin_popcountll(ballot((keep >> sl) & 1u));
