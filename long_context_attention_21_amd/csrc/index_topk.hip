@@ -971,9 +971,10 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   }
 
   // ---- A operand: rows (token, head); lane row = lane % 32, k-block = lane / 32
+  // (the split selection scores only on its exact path: set up there)
   Scorer<FMT> sc;
   int nvl[2];
-  init_scorer<QT, FMT>(sc, p, b, q0, nv, nvl);
+  if (SPLIT != 2) init_scorer<QT, FMT>(sc, p, b, q0, nv, nvl);
   const int jl0 = lane >> 5;  // this lane's tokens: jl0 + 2 tt, tt < TPL
   const int l32 = lane & 31;
   const int grp_j = wave % QT, grp_h = wave / QT;  // this wave's token group and member index
@@ -1121,15 +1122,24 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   if constexpr (SPLIT == 2) {
     // ---- the candidates appended by the partitions, laid out as the regions;
     // count those at or above the row's bound (every entry left out lies
-    // below it, so with k of them the top-k are all candidates)
+    // below it, so with k of them the top-k are all candidates).  Every load
+    // is issued before the first use (one memory round trip); the slots past
+    // the count hold stale values and are not used.
+    constexpr int kPerT = kCap / kThreads;
+    uint2 v[kPerT];
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) v[u] = srow->cand[tid + u * kThreads];
     const int cnt = srow->cnt;
     const uint32_t tkey = srow->tkey;
     const int cc = cnt < kCap ? cnt : kCap;
     int ab = 0;
-    for (int i = tid; i < cc; i += kThreads) {
-      const uint2 v = srow->cand[i];
-      sm.cand[0][i] = v;
-      ab += okey(v.x) >= tkey ? 1 : 0;
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) {
+      const int i = tid + u * kThreads;
+      if (i < cc) {
+        sm.cand[0][i] = v[u];
+        ab += okey(v[u].x) >= tkey ? 1 : 0;
+      }
     }
     for (int off = 32; off >= 1; off >>= 1) ab += __shfl_xor(ab, off);
     if (lane == 0 && ab) atomicAdd(&sm.above, ab);
@@ -1203,6 +1213,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
 
   if (sm.fallback) {
     // ---- exact streaming fallback for every token of this work-group
+    if (SPLIT == 2) init_scorer<QT, FMT>(sc, p, b, q0, nv, nvl);
     if (tid == 0 && p.fallback_count) atomicAdd(p.fallback_count, 1u);
     if (tid < QT) { sm.cnt[tid] = 0; sm.thr[tid] = __uint_as_float(0u); }
     __syncthreads();
@@ -1454,7 +1465,7 @@ __device__ __forceinline__ int cut_bin(float x, float lo, float inv) {
 template <int FMT>
 __global__ __launch_bounds__(512) void index_split_cut_kernel(IndexParams p, int parts, int r_keep) {
   constexpr int W = 8, T = 64 * W;
-  __shared__ float ssc[kCutPart];
+  __shared__ __attribute__((aligned(16))) float ssc[kCutPart];
   __shared__ uint2 kept[kCutKeep];
   __shared__ uint32_t hist[256];
   __shared__ float red[2][W];
@@ -1546,8 +1557,16 @@ __global__ __launch_bounds__(512) void index_split_cut_kernel(IndexParams p, int
 
   int cut = 0, sub = 0;
   float lo2 = 0.0f, inv2 = 0.0f;
+  // the passes below read 4 consecutive scores per thread (n4 of them; the
+  // scores at n .. n4-1 are never read as entries)
+  const int n4 = (n + 3) & ~3;
   if (spread) {
-    for (int i = tid; i < n; i += T) atomicAdd(&hist[cut_bin(ssc[i], lo, inv)], 1u);
+    for (int i = 4 * tid; i < n4; i += 4 * T) {
+      const f32x4 x = *(const f32x4*)&ssc[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (i + k < n) atomicAdd(&hist[cut_bin(x[k], lo, inv)], 1u);
+    }
     __syncthreads();
     if (wave == 0) {
       int above = 0;
@@ -1565,9 +1584,11 @@ __global__ __launch_bounds__(512) void index_split_cut_kernel(IndexParams p, int
       inv2 = inv * 256.0f;
       if (tid < 256) hist[tid] = 0u;
       __syncthreads();
-      for (int i = tid; i < n; i += T) {
-        const float x = ssc[i];
-        if (cut_bin(x, lo, inv) == cut) atomicAdd(&hist[cut_bin(x, lo2, inv2)], 1u);
+      for (int i = 4 * tid; i < n4; i += 4 * T) {
+        const f32x4 x = *(const f32x4*)&ssc[i];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (i + k < n && cut_bin(x[k], lo, inv) == cut) atomicAdd(&hist[cut_bin(x[k], lo2, inv2)], 1u);
       }
       __syncthreads();
       if (wave == 0) {
@@ -1581,25 +1602,35 @@ __global__ __launch_bounds__(512) void index_split_cut_kernel(IndexParams p, int
   }
   const bool drops = spread && (cut > 0 || sub > 0);
 
-  // ---- append the kept entries to LDS, then to the row with one atomic
+  // ---- append the kept entries to LDS (one LDS atomic per wave and pass),
+  // then to the row with one atomic
   uint32_t tmin = 0xffffffffu;
-  for (int i0 = 0; i0 < n; i0 += T) {
-    const int i = i0 + tid;
-    const bool in = i < n;
-    const float x = ssc[in ? i : 0];
-    bool kp = in;
-    if (spread && in) {
-      const int b1 = cut_bin(x, lo, inv);
-      kp = b1 > cut || (b1 == cut && (sub == 0 || cut_bin(x, lo2, inv2) >= sub));
+  for (int i0 = 0; i0 < n4; i0 += 4 * T) {  // every lane takes every pass (cross-lane sums below)
+    const int i = i0 + 4 * tid;
+    const f32x4 x = *(const f32x4*)&ssc[i < n4 ? i : 0];
+    uint32_t kb = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bool kp = i + k < n;
+      if (spread && kp) {
+        const int b1 = cut_bin(x[k], lo, inv);
+        kp = b1 > cut || (b1 == cut && (sub == 0 || cut_bin(x[k], lo2, inv2) >= sub));
+      }
+      kb |= (kp ? 1u : 0u) << k;
     }
-    const uint64_t bal = ballot(kp);
+    const uint32_t mine = (uint32_t)__builtin_popcount(kb);
+    if (!__builtin_amdgcn_ballot_w64(mine != 0u)) continue;  // nothing kept in this wave's 256 scores
+    const uint32_t incl = wave_prefix_sum(mine);
     int base = 0;
-    if (lane == 0 && bal) base = atomicAdd(&s_nkept, __builtin_popcountll(bal));
-    base = __builtin_amdgcn_readfirstlane(base);
-    const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-    if (kp) {
-      if (pos < kCutKeep) kept[pos] = make_uint2(__float_as_uint(x), (uint32_t)(e0 + i));
-      tmin = min(tmin, okey(__float_as_uint(x)));
+    if (lane == 63) base = atomicAdd(&s_nkept, (int)incl);
+    int pos = __builtin_amdgcn_readlane(base, 63) + (int)(incl - mine);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if ((kb >> k) & 1u) {
+        if (pos < kCutKeep) kept[pos] = make_uint2(__float_as_uint(x[k]), (uint32_t)(e0 + i + k));
+        tmin = min(tmin, okey(__float_as_uint(x[k])));
+        ++pos;
+      }
     }
   }
   for (int off = 32; off >= 1; off >>= 1) tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, off));
