@@ -907,6 +907,20 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
           for (int ht = 0; ht < NHT; ++ht)
             S[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(K[kt][ks], Q[ht][ks], S[kt][ht], 0, 0, 0);
       }
+      // V^T by transposing LDS reads, four 16-dim tiles ahead of their
+      // MFMAs: the first four are read before the exponentials, each later
+      // one right after the MFMAs of the tile whose registers it takes
+      auto vread = [&](int dt) {
+        const int vrow = 4 * g + (l16 >> 2);
+        const int piece = ((dt * 2 + ((l16 & 3) >> 1)) ^ vrow) & 15;  // (vrow + 16) & 15 == vrow & 15
+        const int boff = (piece << 4) + ((l16 & 1) << 3);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, kb + vrow * 256 + boff));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, kb + (vrow + 16) * 256 + boff));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 Vt[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) Vt[dt] = vread(dt);
       bf16x8 P[NHT];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht)
@@ -914,19 +928,14 @@ __global__ __launch_bounds__(64 * NW) void attend_ring_kernel(AttendParams p) {
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) P[ht][kt * 4 + i] = (__bf16)__builtin_amdgcn_exp2f(S[kt][ht][i]);
-      // ---- O^T += V^T P^T (V^T by transposing LDS reads); L += 1^T P^T
+      // ---- O^T += V^T P^T; L += 1^T P^T
       auto pv = [&](const bf16x8 (&Pw)[NHT]) {
-        const int vrow = 4 * g + (l16 >> 2);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const int piece = ((dt * 2 + ((l16 & 3) >> 1)) ^ vrow) & 15;  // (vrow + 16) & 15 == vrow & 15
-          const int boff = (piece << 4) + ((l16 & 1) << 3);
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, kb + vrow * 256 + boff));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, kb + (vrow + 16) * 256 + boff));
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int ht = 0; ht < NHT; ++ht)
-            O[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Pw[ht], O[dt][ht], 0, 0, 0);
+            O[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vt[dt % 4], Pw[ht], O[dt][ht], 0, 0, 0);
+          if (dt + 4 < 8) Vt[dt % 4] = vread(dt + 4);
         }
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht)
