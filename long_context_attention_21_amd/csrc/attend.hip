@@ -1092,25 +1092,46 @@ static hipError_t launch_ring(const AttendParams& p, hipStream_t stream) {
 // Split decode, second kernel: work-group (token, 8 heads), thread (head h,
 // 4 dims) merges the parts in ascending order: O = sum_p O_p 2^(m_p - M), L
 // likewise, with M the largest part reference; then normalise, inverse
-// RoPE, store bf16.
+// RoPE, store bf16.  The parts are read kCombineBatch at a time, every load
+// of a batch issued before the first use.
+constexpr int kCombineBatch = 16;
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendParams p) {
   const int64_t tok = p.tok0 + (blockIdx.x >> 3);
   const int h = (int)(blockIdx.x & 7) * 8 + (threadIdx.x >> 5), d0 = (threadIdx.x & 31) * 4;
   if (h >= p.H) return;
   const float* w0 = p.ws + (tok - p.tok0) * p.parts * kAttendPartFloats;
   float M = -__builtin_inff();
-  for (int q = 0; q < p.parts; ++q) M = fmaxf(M, w0[q * kAttendPartFloats + 64 * 128 + h]);
+  for (int q0 = 0; q0 < p.parts; q0 += kCombineBatch) {
+    float mq[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)
+      mq[u] = q0 + u < p.parts ? w0[(q0 + u) * kAttendPartFloats + 64 * 128 + h] : -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) M = fmaxf(M, mq[u]);
+  }
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float L = 0.0f;
-  for (int q = 0; q < p.parts; ++q) {
-    const float* w = w0 + q * kAttendPartFloats;
-    const float lq = w[64 * 128 + 64 + h];
-    if (!(lq > 0.0f)) continue;  // no keys and no sink in this part
-    const float sc = __builtin_amdgcn_exp2f(w[64 * 128 + h] - M);
-    L = __builtin_fmaf(lq, sc, L);
-    const f32x4 v = *(const f32x4*)(w + h * 128 + d0);
+  for (int q0 = 0; q0 < p.parts; q0 += kCombineBatch) {
+    float mq[kCombineBatch], lq[kCombineBatch];
+    f32x4 vq[kCombineBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(v[i], sc, acc[i]);
+    for (int u = 0; u < kCombineBatch; ++u) {
+      lq[u] = 0.0f;
+      if (q0 + u < p.parts) {
+        const float* w = w0 + (q0 + u) * kAttendPartFloats;
+        mq[u] = w[64 * 128 + h];
+        lq[u] = w[64 * 128 + 64 + h];
+        vq[u] = *(const f32x4*)(w + h * 128 + d0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      if (!(lq[u] > 0.0f)) continue;  // no keys and no sink in this part (or past the last)
+      const float sc = __builtin_amdgcn_exp2f(mq[u] - M);
+      L = __builtin_fmaf(lq[u], sc, L);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(vq[u][i], sc, acc[i]);
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const int64_t t = p.q_pos0 + (int)(tok % p.n);
