@@ -44,15 +44,15 @@ PEAK = {"bf16": 2500.0, "fp4": 10100.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s
 # taken on: a changed kernel reports null until it is measured again.  The
 # summaries are profiles/<workload>_hbm_counters.txt.
 TRAFFIC = {
-    ('csa_attend', 3): {"sha256": "31c20eb0ccd4bdd7bff40d38b3beb93075540dbbb51dc4aebc70dedb40a6100d", "bytes": 1.939e+10},  # csa_prefill_128k
-    ('csa_index_topk', 3): {"sha256": "b271a0477a3b8c97aa83e895db9bcad8be75f05509b2745cabd97ace7e95350a", "bytes": 1.222e+09},  # csa_prefill_128k
+    ('csa_attend', 3): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.961e+10},  # csa_prefill_128k
+    ('csa_index_topk', 3): {"sha256": "d51cb783742e9a6fa96fca0a68e7b3f0f273539c2e36e57613ae1c9e5bb03254", "bytes": 1.222e+09},  # csa_prefill_128k
     ('csa_compress', 3): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 7.299e+07},  # csa_prefill_128k
     ('csa_rope_rows', 3): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 6.719e+07},  # csa_prefill_128k
-    ('hca_attend', 2): {"sha256": "31c20eb0ccd4bdd7bff40d38b3beb93075540dbbb51dc4aebc70dedb40a6100d", "bytes": 1.142e+09},  # hca_32k
+    ('hca_attend', 2): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.142e+09},  # hca_32k
     ('csa_compress', 2): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 8.835e+06},  # hca_32k
     ('csa_rope_rows', 2): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 1.685e+07},  # hca_32k
-    ('csa_index_topk', 4): {"sha256": "b271a0477a3b8c97aa83e895db9bcad8be75f05509b2745cabd97ace7e95350a", "bytes": 6.093e+08},  # csa_decode_1m
-    ('csa_attend', 4): {"sha256": "31c20eb0ccd4bdd7bff40d38b3beb93075540dbbb51dc4aebc70dedb40a6100d", "bytes": 1.037e+08},  # csa_decode_1m
+    ('csa_index_topk', 4): {"sha256": "d51cb783742e9a6fa96fca0a68e7b3f0f273539c2e36e57613ae1c9e5bb03254", "bytes": 6.095e+08},  # csa_decode_1m
+    ('csa_attend', 4): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.038e+08},  # csa_decode_1m
 }
 TRAFFIC[("csa_project_in", "proj")] = {  # the GEMM (1.085e9) + the indexer-query kernel (9.7e6)
     "sha256": "59d66afdeef9ae5420b43f5642fb7e92fad86f487007ac22a01617daafc9a5f5", "bytes": 1.095e9}
