@@ -896,18 +896,27 @@ __device__ __forceinline__ void init_scorer(Scorer<FMT>& sc, const IndexParams& 
 // kMinAbove samples lie above a cut leaving `target` entries of the row
 // above it (k + 850, at most kCap - 1024), with at most kCap samples.
 constexpr int kRun = 8;
-__device__ __forceinline__ int sample_entry(int i, int S) { return (i / kRun) * (kRun * S) + (i % kRun); }
+__device__ __forceinline__ int sample_entry(int i, int S) {
+  return (int)(((uint32_t)i / kRun) * (uint32_t)(kRun * S) + ((uint32_t)i % kRun));
+}
 // samples of a row of nv entries: those with sample_entry(i) < nv, a prefix
 __device__ __forceinline__ int sample_count(int nv, int S) {
   const int full = nv / (kRun * S), rest = nv - full * (kRun * S);
   return full * kRun + (rest < kRun ? rest : kRun);
 }
+// (The sizes here are work-group uniform, but integer division runs on the
+// vector unit, a 64-bit one as about 100 instructions: every division below
+// is 32-bit.)
 __device__ __forceinline__ int sample_stride(int maxnv, int k, int& target) {
   target = k + 850;
   if (target > kCap - 1024) target = kCap - 1024;
-  int64_t want = ((int64_t)kMinAbove * maxnv + target - 1) / target;
-  if (want > kCap) want = kCap;
-  return (int)((maxnv + want - 1) / want);
+  // want = min(ceil(kMinAbove * maxnv / target), kCap); below the cap the
+  // product is under 2^24
+  const bool capped = (uint32_t)maxnv * (uint32_t)kMinAbove >= (uint32_t)(kCap - 1) * (uint32_t)target + 1u ||
+                      maxnv >= (1 << 23);
+  const uint32_t want =
+      capped ? (uint32_t)kCap : ((uint32_t)kMinAbove * (uint32_t)maxnv + (uint32_t)target - 1u) / (uint32_t)target;
+  return (int)(((uint32_t)maxnv + want - 1u) / want);
 }
 
 // Workspace row of the split path (few query rows over long entry lists):
@@ -939,8 +948,15 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   int nv[QT];
   int maxnv = 0;
   bool all_small = true;
-  int64_t cq = (p.q_pos0 + q0 + 1) / p.m;
-  int rq = (int)(p.q_pos0 + q0 + 1 - cq * p.m);
+  // (a shift for a power-of-two m)
+  const int64_t xq = p.q_pos0 + q0 + 1;
+  int64_t cq;
+  if ((p.m & (p.m - 1)) == 0) {
+    cq = xq >> __builtin_ctz((uint32_t)p.m);
+  } else {
+    cq = xq / p.m;
+  }
+  int rq = (int)(xq - cq * p.m);
 #pragma unroll
   for (int j = 0; j < QT; ++j) {
     const int q = q0 + j;
@@ -1035,7 +1051,8 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
       const int i = (m * G + grp_h) * 64 + lane;
       kr[m] = i < nsj ? okey(sm.cand[grp_j][i].x) : 0u;
     }
-    int r = nsj > 0 ? (int)(((int64_t)target_a * nsj + nv[grp_j] - 1) / nv[grp_j]) : 0;
+    // target_a * nsj < 2^26: a 32-bit division
+    int r = nsj > 0 ? (int)(((uint32_t)target_a * (uint32_t)nsj + (uint32_t)nv[grp_j] - 1u) / (uint32_t)nv[grp_j]) : 0;
     r = r < 1 ? 1 : (r > nsj ? nsj : r);
     // the cut need not be exact (a bin of up to r/16 samples is close enough);
     // never above the r-th sample; at least the order key of -inf
@@ -1105,7 +1122,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
         }
       }
       const int nsb = nsj > 0 ? sample_count(nv[grp_j], SB) : 0;
-      const int rb = nsb > 0 ? (int)(((int64_t)target * nsb + nv[grp_j] - 1) / nv[grp_j]) : 0;
+      const int rb = nsb > 0 ? (int)(((uint32_t)target * (uint32_t)nsb + (uint32_t)nv[grp_j] - 1u) / (uint32_t)nv[grp_j]) : 0;
       // too few kept (the first cut was too high): keep the first cut
       const bool act = nsj > 0 && rb >= 1 && kept >= rb;
       const RadixOut rob = group_radix<QT, NS>(sm, kb, smb, (uint32_t)(rb < 1 ? 1 : rb), (uint32_t)kept, act,
