@@ -580,9 +580,9 @@ __device__ void wg_bitonic_sort(TopkSmem<QT>& sm, int j, int cnt) {
 // the split decode path, the exact streaming path) writes the same row, and
 // attention, whose sums follow the row's order, sees the same keys in the
 // same order.  Wave w of the scoring pass scores the tiles T with
-// T % kWaves == w in ascending order, so its region of a token's buffer
-// holds whole groups (w and, with 4 waves, w + 4), each in ascending order:
-// the row is written straight from the regions.
+// T % kWaves == w in ascending order, so with 8 waves its region of a
+// token's buffer holds exactly group w, in ascending order: the row is
+// written straight from the regions.
 
 // Entries 0 .. nv-1 (all kept), in the canonical order: position i.
 __device__ __forceinline__ int32_t canon_all(int i, int nv) {
@@ -621,7 +621,9 @@ __device__ __forceinline__ void emit_canonical(TopkSmem<QT>& sm, bool live, cons
 #pragma unroll
       for (int m = 0; m < kPer; ++m) {
         const int sl = rr * kPer + m;
-        c += (uint32_t)__builtin_popcountll(ballot(((keep >> sl) & 1u) && ((ir[sl] >> 5) & 7u) == (uint32_t)(w + sv * W)));
+        // with one group per region (8 waves) every entry of region w is in group w
+        const bool ing = VPW == 1 || ((ir[sl] >> 5) & 7u) == (uint32_t)(w + sv * W);
+        c += (uint32_t)__builtin_popcountll(ballot(((keep >> sl) & 1u) && ing));
       }
       if (lane == 0) sm.vcnt[j][w + sv * W] = c;
     }
@@ -645,7 +647,7 @@ __device__ __forceinline__ void emit_canonical(TopkSmem<QT>& sm, bool live, cons
 #pragma unroll
       for (int m = 0; m < kPer; ++m) {
         const int sl = rr * kPer + m;
-        const bool in = ((keep >> sl) & 1u) && ((ir[sl] >> 5) & 7u) == (uint32_t)v;
+        const bool in = ((keep >> sl) & 1u) && (VPW == 1 || ((ir[sl] >> 5) & 7u) == (uint32_t)v);
         const uint64_t bal = ballot(in);
         const uint32_t pos = run + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
         if (in && pos < (uint32_t)k) o[pos] = (int32_t)ir[sl];
