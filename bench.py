@@ -44,14 +44,14 @@ PEAK = {"bf16": 2500.0, "fp4": 10100.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s
 # taken on: a changed kernel reports null until it is measured again.  The
 # summaries are profiles/<workload>_hbm_counters.txt.
 TRAFFIC = {
-    ('csa_attend', 3): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.961e+10},  # csa_prefill_128k
-    ('csa_index_topk', 3): {"sha256": "d51cb783742e9a6fa96fca0a68e7b3f0f273539c2e36e57613ae1c9e5bb03254", "bytes": 1.222e+09},  # csa_prefill_128k
+    ('csa_attend', 3): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.957e+10},  # csa_prefill_128k
+    ('csa_index_topk', 3): {"sha256": "4e80d340b5080f91386cc694c83c719c7972a9e2b8be506dd527dbd9ec05811c", "bytes": 1.222e+09},  # csa_prefill_128k
     ('csa_compress', 3): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 7.299e+07},  # csa_prefill_128k
     ('csa_rope_rows', 3): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 6.719e+07},  # csa_prefill_128k
     ('hca_attend', 2): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.142e+09},  # hca_32k
     ('csa_compress', 2): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 8.835e+06},  # hca_32k
     ('csa_rope_rows', 2): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 1.685e+07},  # hca_32k
-    ('csa_index_topk', 4): {"sha256": "d51cb783742e9a6fa96fca0a68e7b3f0f273539c2e36e57613ae1c9e5bb03254", "bytes": 6.095e+08},  # csa_decode_1m
+    ('csa_index_topk', 4): {"sha256": "4e80d340b5080f91386cc694c83c719c7972a9e2b8be506dd527dbd9ec05811c", "bytes": 6.095e+08},  # csa_decode_1m
     ('csa_attend', 4): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.038e+08},  # csa_decode_1m
 }
 TRAFFIC[("csa_project_in", "proj")] = {  # the GEMM (1.085e9) + the indexer-query kernel (9.7e6)
