@@ -4,8 +4,11 @@ Default workload (the 128K-context configuration): one CSA layer prefill,
 batch 1, 131072 query tokens, 64 heads of dim 128 with RoPE on the last 64
 dims, m = 4 overlapped compression (32768 entries), MXFP4 Lightning Indexer
 (8 heads x 64, q quantised in-kernel), top-k 2048, 128-token window, per-head
-sink.  One step = csa_compress -> csa_index_topk -> csa_attend over the whole
-sequence, inputs resident in HBM.
+sink.  One step = csa_compress -> csa_rope_rows (the window rotated once) ->
+csa_index_attend over the whole sequence, inputs resident in HBM:
+csa_index_topk and csa_attend pipelined over 16 token chunks, the indexer of
+chunk c + 1 on a second stream beside the attention of chunk c (--chunks 1:
+the calls in turn).
 
 The default run also times, with the same steps, the two HBM-bound
 workloads and reports each under "workloads" with its own roofline and
@@ -16,7 +19,8 @@ prefill of a CSA + HCA layer pair).
 
 Prints one JSON line: throughput (query tokens/s), the roofline of the
 dominant kernel (per-kernel durations from HIP events recorded on the launch
-stream over the timed region), per-kernel figures, and the CPU oracle timed
+stream over the timed region; for a pipelined step, over a second pass of
+the same steps with the calls in turn), per-kernel figures, and the CPU oracle timed
 on a bounded sample of the same workload with all host cores and with one
 thread (N = 1 only); a rate scaled up from a row sample says
 "extrapolated".
@@ -89,6 +93,12 @@ def parse():
                     help="time this workload alone (default: config 3, with configs 2 and 4 beside it "
                          "under 'workloads')")
     ap.add_argument("--no-extra", action="store_true", help="default run: leave out configs 2 and 4")
+    ap.add_argument("--chunks", type=int, default=16,
+                    help="configs 1 and 3: token chunks of csa_index_attend (the indexer of a chunk runs on a "
+                         "second stream beside the attention of the chunk before); 1 = the two calls in turn")
+    ap.add_argument("--trace-summary", default=None, metavar="CSV",
+                    help="only summarise a rocprofv3 kernel_trace.csv: dispatches, total and average "
+                         "duration per kernel and grid size")
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="query rows (config 4: sequences) of the oracle sample (default per config)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -348,14 +358,27 @@ class CsaLayer:
             "csa_attend": ("bf16", 4.0 * self.H * 128 * keys),
         }
         self.pairs, self.keys = pairs, keys
+        self.calls = 0
 
-    def step(self, ev=None):
+    chunks = 16  # csa_index_attend's token chunks in the timed step (1: the calls in turn)
+
+    def step(self, ev=None, serial=False):
+        """One layer step.  With per-kernel events (or serial) the four calls
+        run in turn on the current stream; otherwise the indexer and the
+        attention run as csa_index_attend over self.chunks token chunks."""
         L = self.L
+        self.calls += 1
         if ev: ev[0].record()
         L.csa_compress(self.kv, self.beta, self.m, 1, ik=self.ik, kidx_fmt=self.fmt, out=self.bufs)
         if ev: ev[1].record()
         L.csa_rope_rows(self.kv, out=self.kv_rot)
         if ev: ev[2].record()
+        if ev is None and not serial and self.chunks > 1:
+            L.csa_index_attend(self.qI, self.w, self.bufs["kidx"], self.k, self.m, self.q, self.bufs["entries"],
+                               fmt=self.fmt, kidx_scale=self.bufs.get("kidx_scale"), idx_out=self.idx,
+                               fallback_count=self.fallbacks, win_kv=self.kv_rot, win_roped=True, sink=self.sink,
+                               out=self.out, n_chunks=self.chunks)
+            return
         L.csa_index_topk(self.qI, self.w, self.bufs["kidx"], self.k, self.m, fmt=self.fmt,
                          kidx_scale=self.bufs.get("kidx_scale"), idx_out=self.idx, fallback_count=self.fallbacks)
         if ev: ev[3].record()
@@ -828,13 +851,27 @@ def measure(cfg_id, args, cpu_sample=None):
         wl.step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    # a pipelined step (csa_index_attend) overlaps the indexer and the
+    # attention: it is timed as a whole, and the per-kernel figures come from
+    # a second pass of the same steps with the calls in turn
+    piped = getattr(wl, "chunks", 1) > 1
     log("config %d: timing %d steps" % (cfg_id, args.steps))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        wl.step(evs[s])
+        wl.step(None if piped else evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    serial_ms = None
+    if piped:
+        log("config %d: per-kernel pass, %d steps with the calls in turn" % (cfg_id, args.steps))
+        wl.step(serial=True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for s in range(args.steps):
+            wl.step(evs[s])
+        torch.cuda.synchronize()
+        serial_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     per_k = np.zeros(nk)
     for s in range(args.steps):
         for i in range(nk):
@@ -879,17 +916,50 @@ def measure(cfg_id, args, cpu_sample=None):
     res = {"value": round(wl.n / (ms_step / 1e3), 1), "unit": "query-tokens/s", "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "dtype": dname, "config": cfg,
            "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu}
+    if piped:
+        res["schedule"] = {
+            "step": "csa_compress, csa_rope_rows, then csa_index_attend: %d token chunks, the indexer of chunk "
+                    "c + 1 on a second stream beside the attention of chunk c" % wl.chunks,
+            "kernels_and_roofline": "per-launch durations from a second pass of %d steps with the four calls in "
+                                    "turn on one stream" % args.steps,
+            "serial_ms_per_step": round(serial_ms, 4)}
     if hasattr(wl, "fallbacks"):  # top-k work-groups that took the exact streaming path, per call
-        res["topk_fallbacks_per_call"] = round(int(wl.fallbacks.item()) / (args.warmup + args.steps), 2)
+        ncalls = getattr(wl, "calls", args.warmup + args.steps)
+        res["topk_fallbacks_per_call"] = round(int(wl.fallbacks.item()) / ncalls, 2)
     del wl
     torch.cuda.empty_cache()
     return res
+
+
+def trace_summary(path):
+    """Dispatches, total and average duration (us) per (kernel, grid size)
+    of a rocprofv3 --kernel-trace CSV: the pipelined step's chunked launches
+    and the per-kernel pass's whole-layer launches of one kernel have
+    different grids."""
+    import csv
+    groups = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            grid = "x".join(row[c] for c in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z") if c in row)
+            if not grid:
+                grid = row.get("Grid_Size", "?")
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            g = groups.setdefault((row["Kernel_Name"], grid), [0, 0.0])
+            g[0] += 1
+            g[1] += dur
+    total = sum(v[1] for v in groups.values())
+    print("%-66s %14s %6s %12s %11s %6s" % ("kernel", "grid", "calls", "total_us", "average_us", "pct"))
+    for (name, grid), (cnt, us) in sorted(groups.items(), key=lambda kv: -kv[1][1]):
+        print("%-66s %14s %6d %12.1f %11.1f %6.2f" % (name[:66], grid, cnt, us, us / cnt, 100 * us / total))
 
 
 def main():
     args = parse()
     if args.print_sha:
         print(json.dumps({k: source_sha(k) for k in KERNEL_SOURCE}))
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -911,6 +981,7 @@ def main():
         if args.config != 4:
             sys.exit("--entry-fmt applies to config 4 only")
         DecodeLayer.entry_fmt = args.entry_fmt
+    CsaLayer.chunks = max(1, args.chunks)
     cfg_id = args.config or 3
     res = measure(cfg_id, args, args.cpu_sample)
     line = {
@@ -920,8 +991,9 @@ def main():
         "dtype": res["dtype"], "data": "synthetic (seeded, numpy default_rng)", "config": res["config"],
         "roofline": res["roofline"], "kernels": res["kernels"], "cpu_baseline": res["cpu_baseline"],
     }
-    if "topk_fallbacks_per_call" in res:
-        line["topk_fallbacks_per_call"] = res["topk_fallbacks_per_call"]
+    for key in ("schedule", "topk_fallbacks_per_call"):
+        if key in res:
+            line[key] = res[key]
     if args.config is None and not args.no_extra:
         line["workloads"] = {name: measure(c, args) for name, c in EXTRA}
     print(json.dumps(line), flush=True)

@@ -296,6 +296,50 @@ int csa_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D,
                const float* win_scale, const float* sink, int rope_dims, float rope_base,
                void* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * csa_index_attend -- csa_index_topk followed by csa_attend for one layer's
+ * query rows, pipelined over chunks of query tokens on two streams.  The
+ * top-k set and the attention of a query token depend on that token's row
+ * and the shared caches only ("deepseek V4 技术论文" 1.1: each query token
+ * selects and attends to its own top-k entries), so the rows can be taken in
+ * any grouping; the results are the bytes the two calls write.  The indexer
+ * is bound by vector-ALU work and attention by the matrix cores, so the
+ * indexer of chunk c + 1 (on aux_stream) runs beside the attention of chunk
+ * c (on stream) and the two share the compute units.
+ *
+ *  arguments    as in csa_index_topk (qidx .. fallback_count, kidx_fmt =
+ *               its fmt) and csa_attend (q .. out); B, n, q_pos0, N and m
+ *               are common to both.  The indices are written to idx_out and
+ *               read back by the attention.  No workspace: a call that
+ *               would need one in either function (few query rows over
+ *               long entry lists, FP8 or NVFP4 entries with k + n_win >=
+ *               512) returns CSA_WORKSPACE_TOO_SMALL; use the two calls.
+ *  n_chunks     requested chunk count.  With B = 1 the call uses
+ *               min(n_chunks, n / 512) chunks (at least one) of n / chunks
+ *               consecutive tokens; with B > 1 one chunk.
+ *  stream       the caller's stream.  Everything already enqueued on it is
+ *               complete before any chunk starts, and every chunk's work is
+ *               complete before later work on stream starts: to the caller
+ *               the call is ordered on stream like the two calls.
+ *  aux_stream   a second stream of the same device (not stream, default
+ *               priority), used when the call takes more than one chunk;
+ *               nothing else enqueued on it is ordered with this call.
+ *  events       three hipEvent_t of the device (any creation flags), owned
+ *               by the caller, recorded and waited on by the call; needed
+ *               when the call takes more than one chunk.  Calls that share
+ *               events or aux_stream must be issued from one host thread.
+ *  Errors: every argument is checked before anything is enqueued; a HIP
+ *  error during the enqueue returns CSA_HIP_ERROR with the chunks before it
+ *  enqueued.  Nothing is allocated or synchronised.
+ */
+int csa_index_attend(const void* qidx, const uint8_t* qidx_scale, const float* widx, const void* kidx,
+                     const uint8_t* kidx_scale, int kidx_fmt, int H_I, int d_idx, int k, int32_t* idx_out,
+                     uint32_t* fallback_count, const void* q, int H, int D, const void* entries,
+                     const void* entries_rope, const float* entry_scale, int entry_fmt, const void* win_kv,
+                     int64_t win_pos0, int win_len, int n_win, int win_fmt, const float* win_scale,
+                     const float* sink, int rope_dims, float rope_base, void* out, int B, int n, int64_t q_pos0,
+                     int N, int m, int n_chunks, void* stream, void* aux_stream, void* const* events);
+
 size_t csa_attend_workspace_bytes(int B, int n, int k, int n_win, int entry_fmt);
 
 /*

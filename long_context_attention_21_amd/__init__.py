@@ -7,17 +7,20 @@ stream; every step of the computation runs in the HIP kernels of
 caller does not pass them.
 
 Names follow the C ABI: csa_compress, csa_cache_append, csa_index_topk,
-csa_attend, hca_attend, and the projections around the path
+csa_attend, csa_index_attend (the two pipelined over token chunks), hca_attend, and the projections around the path
 (csa_project_in, csa_project_qidx, csa_project_out).
 """
 from __future__ import annotations
+
+import ctypes
 
 import torch
 
 from ._lib import (FMT_BF16, FMT_BF16_ROPED, FMT_FP8, FMT_FP8_ROPE_BF16, FMT_MXFP4, FMT_NVFP4, CsaError, check,
                    lib)
 
-__all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_noalloc", "csa_attend", "hca_attend",
+__all__ = ["csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_noalloc", "csa_attend",
+           "csa_index_attend", "hca_attend",
            "csa_project_in", "csa_project_qidx", "csa_project_out", "csa_rope_rows", "version",
            "CsaError",
            "FMT_BF16", "FMT_MXFP4", "FMT_FP8_ROPE_BF16", "FMT_NVFP4", "FMT_FP8"]
@@ -183,6 +186,59 @@ def csa_attend(q, entries, idx, q_pos0=0, m=4, win_kv=None, win_pos0=0, n_win=12
         float(rope_base), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
     return out
+
+
+_pipes = {}
+
+
+def _pipe(device):
+    """The aux stream and three events csa_index_attend runs its chunks
+    with, one set per device, created on first use (each event recorded
+    once so that its HIP handle exists)."""
+    key = torch.device(device).index
+    if key not in _pipes:
+        aux = torch.cuda.Stream(device=device)
+        evs = [torch.cuda.Event() for _ in range(3)]
+        for e in evs:
+            e.record(aux)
+        _pipes[key] = (aux, evs, (ctypes.c_void_p * 3)(*[e.cuda_event for e in evs]))
+    return _pipes[key]
+
+
+def csa_index_attend(qidx, widx, kidx, k, m, q, entries, q_pos0=0, fmt="mxfp4", qidx_scale=None,
+                     kidx_scale=None, N=None, idx_out=None, fallback_count=None, win_kv=None, win_pos0=0,
+                     n_win=128, sink=None, entries_rope=None, entry_scale=None, rope_dims=64, rope_base=10000.0,
+                     out=None, win_scale=None, win_roped=False, n_chunks=16, aux_stream=None, stream=None):
+    """csa_index_topk then csa_attend (arguments as there), pipelined over
+    n_chunks chunks of query tokens: the indexer of a chunk runs on an aux
+    stream beside the attention of the one before, on ``stream``.  Returns
+    (idx_out, out); both are the bytes the two separate calls write."""
+    B, n, H, D = q.shape
+    H_I = qidx.shape[2]
+    if N is None:
+        N = entries.shape[1]
+    if entries_rope is not None:
+        ef = FMT_FP8_ROPE_BF16
+    elif entry_scale is not None:
+        ef = FMT_NVFP4
+    else:
+        ef = FMT_BF16
+    if idx_out is None:
+        idx_out = torch.empty((B, n, k), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q, dtype=torch.bfloat16)
+    aux, _, evs = _pipe(q.device)
+    if aux_stream is not None:
+        aux = aux_stream
+    win_len = 0 if win_kv is None else win_kv.shape[1]
+    nw = int(n_win) if win_kv is not None else 0
+    wf = FMT_FP8 if win_scale is not None else (FMT_BF16_ROPED if win_roped else FMT_BF16)
+    check(lib().csa_index_attend(
+        _ptr(qidx), _ptr(qidx_scale), _ptr(widx), _ptr(kidx), _ptr(kidx_scale), _fmt(fmt), H_I, 64, k,
+        _ptr(idx_out), _ptr(fallback_count), _ptr(q), H, D, _ptr(entries), _ptr(entries_rope), _ptr(entry_scale),
+        ef, _ptr(win_kv), int(win_pos0), win_len, nw, wf, _ptr(win_scale), _ptr(sink), rope_dims, float(rope_base),
+        _ptr(out), B, n, int(q_pos0), N, m, int(n_chunks), _stream(stream), aux.cuda_stream, evs))
+    return idx_out, out
 
 
 def hca_attend(q, entries, q_pos0=0, m=128, win_kv=None, win_pos0=0, n_win=128, sink=None,

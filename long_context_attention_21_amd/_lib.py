@@ -25,7 +25,7 @@ FMT_BF16_ROPED = 5
 
 EXPORTS = ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_workspace_bytes",
            "csa_index_topk_noalloc",
-           "csa_attend", "csa_attend_workspace_bytes", "hca_attend", "csa_project_in",
+           "csa_attend", "csa_attend_workspace_bytes", "csa_index_attend", "hca_attend", "csa_project_in",
            "csa_project_qidx", "csa_project_out", "csa_rope_rows", "csa_last_error", "csa_version")
 
 
@@ -58,6 +58,9 @@ def lib():
     L.csa_index_topk_workspace_bytes.restype = sz
     L.csa_attend.argtypes = [P, i32, i32, i64, i32, i32, P, P, P, i32, i32, i32, P, i32, P, i64, i32,
                              i32, i32, P, P, i32, f32, P, P, sz, P]
+    L.csa_index_attend.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P, P,
+                                   P, i32, i32, P, P, P, i32, P, i64, i32, i32, i32, P, P, i32, f32, P,
+                                   i32, i32, i64, i32, i32, i32, P, P, P]
     L.csa_attend_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.csa_attend_workspace_bytes.restype = sz
     L.hca_attend.argtypes = [P, i32, i32, i64, i32, i32, P, i32, i32, P, i64, i32, i32, i32, P, i32, f32,
@@ -67,6 +70,7 @@ def lib():
     L.csa_project_qidx.argtypes = [P, i32, i32, P, i32, P, P, P, P]
     L.csa_project_out.argtypes = [P, i32, i32, i32, i32, P, i32, P, P]
     for f in ("csa_compress", "csa_cache_append", "csa_index_topk", "csa_index_topk_noalloc", "csa_attend",
+              "csa_index_attend",
               "hca_attend", "csa_project_in", "csa_project_qidx", "csa_project_out", "csa_rope_rows",
               "csa_version"):
         getattr(L, f).restype = i32

@@ -210,7 +210,7 @@ size_t csa_index_topk_workspace_bytes(int B, int n, int64_t q_pos0, int N, int m
 static int index_common(const void* qidx, const uint8_t* qidx_scale, const float* widx, const void* kidx,
                         const uint8_t* kidx_scale, int fmt, int B, int n, int64_t q_pos0, int H_I, int d_idx, int N,
                         int m, int k, int32_t* idx_out, void* ws, size_t ws_bytes, bool static_ws,
-                        uint32_t* fallback_count, void* stream, const char* name) {
+                        uint32_t* fallback_count, void* stream, const char* name, bool launch = true) {
   REQUIRE(B >= 0 && n >= 0 && N >= 0, "%s: B=%d n=%d N=%d must be >= 0", name, B, n, N);
   REQUIRE(fmt == CSA_FMT_BF16 || fmt == CSA_FMT_MXFP4, "%s: fmt=%d unsupported", name, fmt);
   REQUIRE(d_idx == 64, "%s: d_idx=%d unsupported (must be 64)", name, d_idx);
@@ -242,6 +242,7 @@ static int index_common(const void* qidx, const uint8_t* qidx_scale, const float
       return fail(CSA_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes < %zu needed", name, ws_bytes, need);
     REQUIRE(need == 0 || (ws != nullptr && aligned16(ws)), "%s: ws must be non-NULL and 16-byte aligned", name);
   }
+  if (!launch) return ok();
   csa::IndexParams p{};
   p.q = qidx;
   p.q_scale = (fmt == CSA_FMT_MXFP4) ? qidx_scale : nullptr;
@@ -285,7 +286,7 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
                          int64_t win_pos0, int win_len, int n_win, int win_fmt, const float* win_scale,
                          const float* sink,
                          int rope_dims, float rope_base, void* out, void* ws, size_t ws_bytes,
-                         void* stream, const char* name) {
+                         void* stream, const char* name, bool launch = true) {
   REQUIRE(B >= 0 && n >= 0 && N >= 0 && k >= 0, "%s: B, n, N and k must be >= 0", name);
   REQUIRE(D == 128, "%s: D=%d unsupported (head dim must be 128)", name, D);
   REQUIRE(H >= 1 && H <= 64, "%s: H=%d must be in [1, 64]", name, H);
@@ -331,6 +332,7 @@ static int attend_common(int mode, const void* q, int B, int n, int64_t q_pos0, 
   if (ws_bytes < need)
     return fail(CSA_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes < %zu needed", name, ws_bytes, need);
   REQUIRE(need == 0 || (ws != nullptr && aligned16(ws)), "%s: ws must be non-NULL and 16-byte aligned", name);
+  if (!launch) return ok();
   csa::AttendParams p{};
   p.q = (const uint16_t*)q;
   p.B = B;
@@ -377,6 +379,76 @@ size_t csa_attend_workspace_bytes(int B, int n, int k, int n_win, int entry_fmt)
   if (B < 0 || n < 0 || k < 0 || n_win < 0) return 0;
   return csa::attend_workspace(entry_fmt == CSA_FMT_FP8_ROPE_BF16 ? 1 : entry_fmt == CSA_FMT_NVFP4 ? 3 : 0, B, n,
                                k, n_win);
+}
+
+int csa_index_attend(const void* qidx, const uint8_t* qidx_scale, const float* widx, const void* kidx,
+                     const uint8_t* kidx_scale, int kidx_fmt, int H_I, int d_idx, int k, int32_t* idx_out,
+                     uint32_t* fallback_count, const void* q, int H, int D, const void* entries,
+                     const void* entries_rope, const float* entry_scale, int entry_fmt, const void* win_kv,
+                     int64_t win_pos0, int win_len, int n_win, int win_fmt, const float* win_scale,
+                     const float* sink, int rope_dims, float rope_base, void* out, int B, int n, int64_t q_pos0,
+                     int N, int m, int n_chunks, void* stream, void* aux_stream, void* const* events) {
+  static const char* name = "csa_index_attend";
+  REQUIRE(entry_fmt == CSA_FMT_BF16 || entry_fmt == CSA_FMT_FP8_ROPE_BF16 || entry_fmt == CSA_FMT_NVFP4,
+          "%s: entry_fmt=%d unsupported", name, entry_fmt);
+  REQUIRE(n_chunks >= 1, "%s: n_chunks=%d must be >= 1", name, n_chunks);
+  const int mode = entry_fmt == CSA_FMT_BF16 ? 0 : entry_fmt == CSA_FMT_FP8_ROPE_BF16 ? 1 : 3;
+  // chunks of at least kMinChunk tokens of the one batch row
+  constexpr int kMinChunk = 512;
+  int C = n_chunks;
+  if (B != 1 || (int64_t)C * kMinChunk > n) C = B == 1 ? (n / kMinChunk > 1 ? n / kMinChunk : 1) : 1;
+  if (C > 1) {
+    REQUIRE(aux_stream != nullptr && aux_stream != stream, "%s: n_chunks > 1 needs an aux_stream other than stream",
+            name);
+    REQUIRE(events && events[0] && events[1] && events[2], "%s: n_chunks > 1 needs three events", name);
+  }
+  // the whole call is checked before anything is enqueued (no workspace:
+  // the formats and sizes that need one are refused here)
+  int st = index_common(qidx, qidx_scale, widx, kidx, kidx_scale, kidx_fmt, B, n, q_pos0, H_I, d_idx, N, m, k,
+                        idx_out, nullptr, 0, false, fallback_count, stream, name, false);
+  if (st != CSA_OK) return st;
+  st = attend_common(mode, q, B, n, q_pos0, H, D, entries, entries_rope, entry_scale, N, m, idx_out, k, win_kv,
+                     win_pos0, win_len, n_win, win_fmt, win_scale, sink, rope_dims, rope_base, out, nullptr, 0,
+                     stream, name, false);
+  if (st != CSA_OK) return st;
+  if ((int64_t)B * n == 0) return ok();
+  // per-token byte strides of the token-major arrays (B = 1 when chunked)
+  const bool qcodes = kidx_fmt == CSA_FMT_MXFP4 && qidx_scale != nullptr;
+  const int64_t s_qidx = (int64_t)H_I * (qcodes ? 32 : 128), s_qsc = (int64_t)H_I * 2;
+  const int64_t s_w = H_I, s_idx = k, s_q = (int64_t)H * 256;
+  auto index_chunk = [&](int64_t a, int nc, void* strm) {
+    return index_common((const uint8_t*)qidx + a * s_qidx, qidx_scale ? qidx_scale + a * s_qsc : nullptr,
+                        widx + a * s_w, kidx, kidx_scale, kidx_fmt, B, nc, q_pos0 + a, H_I, d_idx, N, m, k,
+                        idx_out + a * s_idx, nullptr, 0, false, fallback_count, strm, name);
+  };
+  auto attend_chunk = [&](int64_t a, int nc) {
+    return attend_common(mode, (const uint8_t*)q + a * s_q, B, nc, q_pos0 + a, H, D, entries, entries_rope,
+                         entry_scale, N, m, idx_out + a * s_idx, k, win_kv, win_pos0, win_len, n_win, win_fmt,
+                         win_scale, sink, rope_dims, rope_base, (uint8_t*)out + a * s_q, nullptr, 0, stream, name);
+  };
+  if (C == 1) {
+    st = index_chunk(0, n, stream);
+    return st != CSA_OK ? st : attend_chunk(0, n);
+  }
+  hipStream_t sm = (hipStream_t)stream, sx = (hipStream_t)aux_stream;
+  hipEvent_t ev0 = (hipEvent_t)events[0], ring[2] = {(hipEvent_t)events[1], (hipEvent_t)events[2]};
+  // the aux stream starts after everything already enqueued on stream
+  st = hip_status(hipEventRecord(ev0, sm), "csa_index_attend: event record");
+  if (st == CSA_OK) st = hip_status(hipStreamWaitEvent(sx, ev0, 0), "csa_index_attend: stream wait");
+  auto lo = [&](int c) { return (int64_t)n * c / C; };
+  for (int c = 0; c <= C && st == CSA_OK; ++c) {
+    if (c < C) {  // top-k of chunk c on the aux stream
+      st = index_chunk(lo(c), (int)(lo(c + 1) - lo(c)), sx);
+      if (st == CSA_OK) st = hip_status(hipEventRecord(ring[c & 1], sx), "csa_index_attend: event record");
+    }
+    if (c >= 1 && st == CSA_OK) {  // attention of chunk c - 1 once its top-k is written
+      // (ring[(c-1) & 1] was last recorded for chunk c - 1: a wait takes the
+      // event's latest record at the time of the call)
+      st = hip_status(hipStreamWaitEvent(sm, ring[(c - 1) & 1], 0), "csa_index_attend: stream wait");
+      if (st == CSA_OK) st = attend_chunk(lo(c - 1), (int)(lo(c) - lo(c - 1)));
+    }
+  }
+  return st;
 }
 
 int hca_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D, const void* entries,

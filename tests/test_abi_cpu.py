@@ -271,6 +271,46 @@ def test_attend_rejects_small_workspace(L):
     assert "ws must be" in _msg(L)
 
 
+_EVS = (C.c_void_p * 3)(FAKE, FAKE, FAKE)  # never recorded: every call below fails validation first
+
+
+def _index_attend(L, **kw):
+    a = dict(qidx=FAKE, qidx_scale=None, widx=FAKE, kidx=FAKE, kidx_scale=FAKE, kidx_fmt=1, H_I=8, d_idx=64,
+             k=64, idx_out=FAKE2, fallback_count=None, q=FAKE, H=64, D=128, entries=FAKE, entries_rope=None,
+             entry_scale=None, entry_fmt=0, win_kv=FAKE, win_pos0=0, win_len=4096, n_win=128, win_fmt=5,
+             win_scale=None, sink=None, rope_dims=64, rope_base=10000.0, out=FAKE2, B=1, n=4096, q_pos0=0,
+             N=1024, m=4, n_chunks=4, stream=None, aux_stream=FAKE, events=_EVS)
+    a.update(kw)
+    return L.csa_index_attend(*a.values())
+
+
+@pytest.mark.parametrize("kw,needle,status", [
+    (dict(n_chunks=0), "n_chunks=0", _lib.CSA_INVALID_ARG),
+    (dict(entry_fmt=7), "entry_fmt=7", _lib.CSA_INVALID_ARG),
+    (dict(aux_stream=None), "aux_stream", _lib.CSA_INVALID_ARG),
+    (dict(events=None), "three events", _lib.CSA_INVALID_ARG),
+    (dict(events=(C.c_void_p * 3)(FAKE, None, FAKE)), "three events", _lib.CSA_INVALID_ARG),
+    # the indexer's and the attention's own checks, before anything is enqueued
+    (dict(k=0), "k=0", _lib.CSA_INVALID_ARG),
+    (dict(H_I=9), "H_I=9", _lib.CSA_INVALID_ARG),
+    (dict(n_win=129), "n_win=129", _lib.CSA_INVALID_ARG),
+    (dict(win_len=100), "window source", _lib.CSA_INVALID_ARG),
+    (dict(q=MIS), "aligned", _lib.CSA_INVALID_ARG),
+    # B > 1 or fewer than 1024 tokens run as one chunk: no aux stream or
+    # events are asked for, the later checks still apply
+    (dict(B=2, aux_stream=None, events=None, k=0), "k=0", _lib.CSA_INVALID_ARG),
+    (dict(n=1000, aux_stream=None, events=None, k=0), "k=0", _lib.CSA_INVALID_ARG),
+    # calls that would need a workspace are refused (decode shapes)
+    (dict(n=4, q_pos0=4 * 65536, N=65536, win_pos0=4 * 65536 - 127, win_len=131), "workspace",
+     _lib.CSA_WORKSPACE_TOO_SMALL),
+    (dict(n=1, q_pos0=8000, N=2000, k=2048, entry_fmt=2, entries_rope=FAKE, entry_scale=FAKE, win_fmt=0,
+          win_pos0=7873, win_len=128), "workspace", _lib.CSA_WORKSPACE_TOO_SMALL),
+])
+def test_index_attend_rejects(L, kw, needle, status):
+    assert _index_attend(L, **kw) == status
+    assert needle in _msg(L), _msg(L)
+
+
 def _proj_in(L, **kw):
     a = dict(x=FAKE, M=5, d=256, w_in=FAKE2, n_q=512, n_kv=128, n_ik=64, n_lat=32, n_w=8, n_z=2, w_up=FAKE,
              n_qidx=512, q_out=FAKE, kv_out=FAKE, ik_out=FAKE, lat_out=FAKE, w_out=FAKE, z_out=FAKE, qidx_out=FAKE,

@@ -267,3 +267,55 @@ def test_index_split_path_independent_of_batch_size(orc):
         one = _index_call(q, w, kc, ks, [b], 0, 1, P, k, "mxfp4")
         for i in np.nonzero(sel == b)[0][:5]:
             assert np.array_equal(one[0], big[i]), (b, i)
+
+
+@pytest.mark.parametrize("fmt,n,k,q_pos0,chunks", [
+    ("mxfp4", 6144, 512, 0, (1, 3, 8, 12)),
+    ("bf16", 4096, 256, 0, (2, 5)),
+    ("mxfp4", 2600, 512, 1000, (4,)),   # a prefill chunk after 1000 tokens, uneven chunks
+])
+def test_index_attend_pipeline_equals_the_two_calls(orc, fmt, n, k, q_pos0, chunks):
+    """csa_index_attend (indexer of chunk c + 1 on an aux stream beside the
+    attention of chunk c) writes the same top-k rows and output bits as
+    csa_index_topk followed by csa_attend, for any chunk count; sampled rows
+    against the oracle."""
+    H, H_I = 64, 8
+    c = synth.csa_prefill(n, H, H_I, 32, k, seed=131, indexer=fmt)
+    P = q_pos0
+    kv = dev(c["kv"])
+    comp = L.csa_compress(kv, dev(c["beta"]), 4, 1, ik=dev(c["ik"]), kidx_fmt=fmt)
+    # the window: rows at positions 0 .. P + n - 1 (the first P rows stand in
+    # for the earlier chunk), rotated once
+    win = torch.cat([kv[:, :P], kv], dim=1) if P else kv
+    kv_rot = L.csa_rope_rows(win.contiguous())
+    qI, w, q, sink = dev(c["q_I"]), dev(c["w_I"]), dev(c["q"]), dev(c["sink"])
+    # entries of the first P positions: reuse the chunk's own (any key cache works)
+    ents = comp["entries"]
+    N = ents.shape[1]
+    kcache, kscale = comp["kidx"], comp.get("kidx_scale")
+    ref_idx = L.csa_index_topk(qI, w, kcache, k, 4, q_pos0=P, fmt=fmt, kidx_scale=kscale, N=N)
+    ref_out = L.csa_attend(q, ents, ref_idx, q_pos0=P, m=4, win_kv=kv_rot, win_roped=True, sink=sink, N=N)
+    torch.cuda.synchronize()
+    ri, ro = host(ref_idx), host_bits(ref_out)
+    for C in chunks:
+        print("index_attend fmt %s n %d chunks %d" % (fmt, n, C), flush=True)
+        fc = torch.zeros(1, dtype=torch.int32, device="cuda")
+        gi, go = L.csa_index_attend(qI, w, kcache, k, 4, q, ents, q_pos0=P, fmt=fmt, kidx_scale=kscale, N=N,
+                                    win_kv=kv_rot, win_roped=True, sink=sink, n_chunks=C, fallback_count=fc)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(gi), ri), "top-k rows differ with %d chunks" % C
+        assert np.array_equal(host_bits(go), ro), "attention output differs with %d chunks" % C
+    # the pipelined result against the oracle on rows of several chunks
+    rows = np.array([0, 1, n // 3, n // 2 + 7, n - 2, n - 1], np.int32)
+    ent, kid = orc.compress(c["kv"][0], c["beta"], 4, 1, ik=c["ik"][0])
+    e_bits = orc.bf16_from_f32(ent)
+    if fmt == "mxfp4":
+        kc, ks = orc.mxfp4_encode(kid)
+        qc, qs = orc.mxfp4_encode(orc.bf16_to_f64(c["q_I"][0]).astype(np.float32))
+        oidx = orc.index_topk_rows(orc.mxfp4_decode(qc, qs), c["w_I"][0], orc.mxfp4_decode(kc, ks), 4, P, rows, k)
+        assert np.array_equal(canonical_rows(host(gi)[0][rows]), canonical_rows(oidx))
+    else:
+        oidx = host(gi)[0][rows]  # bf16 sets: tie bands are checked in the indexer's own parity tests
+    wf = np.concatenate([c["kv"][0][:P], c["kv"][0]]) if P else c["kv"][0]
+    ref = orc.attend_rows(c["q"][0], P, orc.bf16_to_f64(e_bits), 4, rows, "csa", idx=oidx, win=wf, sink=c["sink"])
+    assert_close(host_bits(go)[0][rows], ref, "csa_index_attend")

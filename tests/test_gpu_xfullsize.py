@@ -91,6 +91,16 @@ def test_config3_csa_full(orc):
     ref = orc.attend_rows(c["q"][0], 0, orc.bf16_to_f64(e_bits), 4, rows, "csa", idx=ref_idx, win=c["kv"][0],
                           sink=c["sink"])
     assert_close(_bits(wl.out)[0][rows], ref, "config 3 csa_attend")
+    # the step pipelines the indexer and the attention over token chunks on
+    # two streams (csa_index_attend): the calls in turn give the same bytes
+    assert wl.chunks > 1
+    piped_idx, piped_out = wl.idx.cpu().numpy().copy(), _bits(wl.out).copy()
+    wl.idx.zero_()
+    wl.out.zero_()
+    wl.step(serial=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(wl.idx.cpu().numpy(), piped_idx), "pipelined top-k differs from the calls in turn"
+    assert np.array_equal(_bits(wl.out), piped_out), "pipelined attention differs from the calls in turn"
 
 
 @pytest.mark.timeout(1100)
