@@ -93,9 +93,10 @@ def parse():
                     help="time this workload alone (default: config 3, with configs 2 and 4 beside it "
                          "under 'workloads')")
     ap.add_argument("--no-extra", action="store_true", help="default run: leave out configs 2 and 4")
-    ap.add_argument("--chunks", type=int, default=16,
-                    help="configs 1 and 3: token chunks of csa_index_attend (the indexer of a chunk runs on a "
-                         "second stream beside the attention of the chunk before); 1 = the two calls in turn")
+    ap.add_argument("--chunks", type=int, default=None,
+                    help="configs 1, 3 and 5: token chunks of csa_index_attend (the indexer of a chunk runs on a "
+                         "second stream beside the attention of the chunk before; default 16, config 5: 1); "
+                         "1 = the two calls in turn")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="only summarise a rocprofv3 kernel_trace.csv: dispatches, total and average "
                          "duration per kernel and grid size")
@@ -699,6 +700,7 @@ class PairLayer:
         self.fallbacks = torch.zeros(1, dtype=torch.int32, device=cu)  # exact-path work-groups
         self.c_out = torch.empty((1, n, H, 128), dtype=torch.bfloat16, device=cu)
         self.h_out = torch.empty((1, n, H, 128), dtype=torch.bfloat16, device=cu)
+        self.calls = 0
         log("pair inputs generated in %.1f s" % (time.time() - t0))
         self.kernels = ["csa_compress", "csa_rope_rows", "csa_index_topk", "csa_attend", "hca_compress",
                         "hca_rope_rows", "hca_attend"]
@@ -719,8 +721,19 @@ class PairLayer:
             "hca_attend": ("bf16", 4.0 * H * 128 * keys_h),
         }
 
-    def step(self, ev=None):
+    # csa_index_attend's token chunks for the CSA layer.  1 (the calls in
+    # turn): a chunk of this layer's rows, which see up to 262144 entries
+    # each, has too few long indexer work-groups to fill the GPU, so chunks
+    # add their tails (measured 6.0-6.2 ms/step in turn, 6.2 / 7.9 / 9.0 ms
+    # with 2 / 4 / 8 chunks)
+    chunks = 1
+
+    def step(self, ev=None, serial=False):
+        """One step of the pair.  With per-kernel events (or serial) every
+        call runs in turn; otherwise the CSA layer's indexer and attention
+        run as csa_index_attend over self.chunks token chunks."""
         L, P, n = self.L, self.P, self.n
+        self.calls += 1
         if ev: ev[0].record()
         L.csa_compress(self.c_win[:, 128:], self.c_beta, 4, 1, pos0=P, ik=self.c_ik[:, 4:],
                        prev_kv=self.c_win[:, 124:128], prev_ik=self.c_ik[:, :4], kidx_fmt="mxfp4",
@@ -729,11 +742,17 @@ class PairLayer:
         if ev: ev[1].record()
         L.csa_rope_rows(self.c_win, pos0=P - 128, out=self.c_rot)
         if ev: ev[2].record()
-        L.csa_index_topk(self.c_qI, self.c_w, self.c_kc, self.k, 4, q_pos0=P, fmt="mxfp4",
-                         kidx_scale=self.c_ks, idx_out=self.idx, fallback_count=self.fallbacks)
-        if ev: ev[3].record()
-        L.csa_attend(self.c_q, self.c_ent, self.idx, q_pos0=P, m=4, win_kv=self.c_rot, win_pos0=P - 128,
-                     win_roped=True, sink=self.c_sink, out=self.c_out)
+        if ev is None and not serial and self.chunks > 1:
+            L.csa_index_attend(self.c_qI, self.c_w, self.c_kc, self.k, 4, self.c_q, self.c_ent, q_pos0=P,
+                               fmt="mxfp4", kidx_scale=self.c_ks, idx_out=self.idx, fallback_count=self.fallbacks,
+                               win_kv=self.c_rot, win_pos0=P - 128, win_roped=True, sink=self.c_sink,
+                               out=self.c_out, n_chunks=self.chunks)
+        else:
+            L.csa_index_topk(self.c_qI, self.c_w, self.c_kc, self.k, 4, q_pos0=P, fmt="mxfp4",
+                             kidx_scale=self.c_ks, idx_out=self.idx, fallback_count=self.fallbacks)
+            if ev: ev[3].record()
+            L.csa_attend(self.c_q, self.c_ent, self.idx, q_pos0=P, m=4, win_kv=self.c_rot, win_pos0=P - 128,
+                         win_roped=True, sink=self.c_sink, out=self.c_out)
         if ev: ev[4].record()
         L.csa_compress(self.h_win[:, 128:], self.h_beta, 128, 0, pos0=P, out={"entries": self.h_ent[:, self.Nh0:]})
         if ev: ev[5].record()
@@ -981,7 +1000,8 @@ def main():
         if args.config != 4:
             sys.exit("--entry-fmt applies to config 4 only")
         DecodeLayer.entry_fmt = args.entry_fmt
-    CsaLayer.chunks = max(1, args.chunks)
+    if args.chunks is not None:
+        CsaLayer.chunks = PairLayer.chunks = max(1, args.chunks)
     cfg_id = args.config or 3
     res = measure(cfg_id, args, args.cpu_sample)
     line = {
