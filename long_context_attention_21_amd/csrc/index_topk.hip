@@ -780,6 +780,27 @@ __device__ __forceinline__ void append_private(TopkSmem<QT>& sm, bool vis, bool 
   wc[1] += nhi;
 }
 
+// append_private for a tile every entry of which is visible to both of the
+// lane's tokens and which cannot overflow a region (the caller checks both
+// on the scalar unit): no per-lane visibility or bound test.  Token j0 (lanes
+// 0..31) and j0 + 1 (lanes 32..63) have adjacent buffers, so one position
+// serves both halves: the upper lanes add the buffer length plus their
+// half's count less everything mbcnt_lo counted below them.
+template <int QT>
+__device__ __forceinline__ void append_full(TopkSmem<QT>& sm, bool ge, uint32_t val, int e, int j0, int wave,
+                                            uint32_t upper, uint32_t (&wc)[2]) {
+  constexpr int kReg = Shape<QT>::Reg;
+  const uint64_t bal = ballot(ge);
+  const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+  const uint32_t nlo = (uint32_t)__builtin_popcount(lo), nhi = (uint32_t)__builtin_popcount(hi);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readfirstlane((int)(kCap + wc[1] - wc[0] - nlo));
+  const uint32_t pos = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, upper & d));
+  const uint32_t s0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(j0 * kCap + wave * kReg) + wc[0]));
+  if (ge) (&sm.cand[0][0])[pos + s0] = make_uint2(val, (uint32_t)e);
+  wc[0] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(wc[0] + nlo));
+  wc[1] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(wc[1] + nhi));
+}
+
 // Scorer of a work-group's QT query tokens q0 .. q0+QT-1 of batch row b:
 // the MFMA A operand (rows = (token, head); MXFP4 quantised in-kernel from
 // bf16 q when no scales are given), the head weights, and the entry-key
@@ -940,7 +961,8 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   constexpr int kWaves = Shape<QT>::W, kThreads = Shape<QT>::T, kTile = Shape<QT>::Tile, kReg = Shape<QT>::Reg;
   constexpr int TPL = Shape<QT>::TPL;
   __shared__ TopkSmem<QT> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: region offsets stay scalar
   const int nblk = (p.n + QT - 1) / QT;
   const int b = blockIdx.x / nblk;
   const int q0 = (nblk - 1 - (int)(blockIdx.x % nblk)) * QT;  // heavy (late) blocks first
@@ -1194,7 +1216,36 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
         t[u] = sc.load(u * kTile + ecol);
         __builtin_amdgcn_sched_barrier(0);  // issue order = consumption order (tight waits)
       }
-      for (int base = 0; base < maxnv; base += kDepth * kTile) {
+      int base = 0;
+      // Groups every entry of which every token sees, while no region can
+      // fill within a group (both tested on the scalar unit): append_full.
+      // Work-groups with a slot past QT or past the last row (QT = 1, the
+      // batch row's end) take the checked loop only.
+      int nvmin = nv[0];
+  #pragma unroll
+      for (int j = 1; j < QT; ++j) nvmin = nv[j] < nvmin ? nv[j] : nvmin;
+      if (QT < 2 || q0 + QT > p.n) nvmin = 0;
+      const int nfull = __builtin_amdgcn_readfirstlane(nvmin / (kDepth * kTile));
+      uint32_t upper = lane >= 32 ? 0xffffffffu : 0u;
+      asm volatile("" : "+v"(upper));  // an opaque mask: one v_and per tile, not a move and a select
+      for (int g = 0; g < nfull; ++g, base += kDepth * kTile) {
+        uint32_t wmax = 0;
+  #pragma unroll
+        for (int tt = 0; tt < TPL; ++tt) wmax = max(wmax, max(wcnt[tt][0], wcnt[tt][1]));
+        if (__builtin_amdgcn_readfirstlane((int)wmax) > kReg - kDepth * 32) break;
+  #pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+          const f32x16 C = sc.mfma(t[u]);
+          t[u] = sc.load(base + (u + kDepth) * kTile + ecol);
+          const int e = base + u * kTile + ecol;
+          float I[2];
+          sc.template epilogue<TPL>(C, I);
+  #pragma unroll
+          for (int tt = 0; tt < TPL; ++tt)
+            append_full<QT>(sm, I[tt] >= thr2[tt], __float_as_uint(I[tt]), e, 2 * tt, wave, upper, wcnt[tt]);
+        }
+      }
+      for (; base < maxnv; base += kDepth * kTile) {
   #pragma unroll
         for (int u = 0; u < kDepth; ++u) {  // unconditional: tiles past the end never pass
           const f32x16 C = sc.mfma(t[u]);
