@@ -1036,10 +1036,13 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
   if (SPLIT != 2 && sampling) {
     // sample tiles wave, wave + kWaves, ...; kDepth tiles in flight per wave
     const int ntile = (sample_count(maxnv, S) + 31) / 32;
+    // sample_entry(tile * 32 + l32, S) = tile * 32 S + sample_entry(l32, S):
+    // a uniform tile offset plus a lane constant (no per-tile division)
+    const int soff = sample_entry(l32, S), tstride = __builtin_amdgcn_readfirstlane(32 * S);
     BTile<FMT> t[kDepth];
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
-      t[u] = sc.load(sample_entry((wave + u * kWaves) * 32 + l32, S));
+      t[u] = sc.load((wave + u * kWaves) * tstride + soff);
       __builtin_amdgcn_sched_barrier(0);  // issue order = consumption order (tight waits)
     }
     for (int tile0 = wave; tile0 < ntile; tile0 += kDepth * kWaves) {
@@ -1048,7 +1051,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
         // unconditional: tiles past the end store nothing (e >= nvl)
         const int tile = tile0 + u * kWaves;
         const f32x16 C = sc.mfma(t[u]);
-        t[u] = sc.load(sample_entry((tile + kDepth * kWaves) * 32 + l32, S));
+        t[u] = sc.load((tile + kDepth * kWaves) * tstride + soff);
         float I[2];
         sc.template epilogue<TPL>(C, I);
         // The MFMA takes operands from all 64 lanes.  Its result must be used
@@ -1057,7 +1060,7 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
         // lanes would feed stale registers.
         asm volatile("" : "+v"(I[0]), "+v"(I[1]));
         const int i = tile * 32 + l32;
-        const int e = sample_entry(i, S);
+        const int e = tile * tstride + soff;  // sample_entry(i, S)
 #pragma unroll
         for (int tt = 0; tt < TPL; ++tt) {
           const int j = jl0 + 2 * tt;
@@ -1096,11 +1099,12 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
       // wave-private regions of the token buffers
       const int SB = S / 4;
       const int ntile_b = (sample_count(maxnv, SB) + 31) / 32;
+      const int soffb = sample_entry(l32, SB), tstrideb = __builtin_amdgcn_readfirstlane(32 * SB);
       uint32_t wc2[2][2] = {{0u, 0u}, {0u, 0u}};
       BTile<FMT> t[kDepth];
 #pragma unroll
       for (int u = 0; u < kDepth; ++u) {
-        t[u] = sc.load(sample_entry((wave + u * kWaves) * 32 + l32, SB));
+        t[u] = sc.load((wave + u * kWaves) * tstrideb + soffb);
         __builtin_amdgcn_sched_barrier(0);
       }
       for (int tile0 = wave; tile0 < ntile_b; tile0 += kDepth * kWaves) {
@@ -1108,10 +1112,10 @@ __global__ __launch_bounds__(Shape<QT>::T) void index_topk_kernel(IndexParams p)
         for (int u = 0; u < kDepth; ++u) {
           const int tile = tile0 + u * kWaves;
           const f32x16 C = sc.mfma(t[u]);
-          t[u] = sc.load(sample_entry((tile + kDepth * kWaves) * 32 + l32, SB));
+          t[u] = sc.load((tile + kDepth * kWaves) * tstrideb + soffb);
           float I[2];
           sc.template epilogue<TPL>(C, I);
-          const int e = sample_entry(tile * 32 + l32, SB);
+          const int e = tile * tstrideb + soffb;  // sample_entry(tile * 32 + l32, SB)
 #pragma unroll
           for (int tt = 0; tt < TPL; ++tt)
             append_private<QT>(sm, e < nvl[tt], I[tt] >= thr_a[tt], __float_as_uint(I[tt]), e, jl0 + 2 * tt, wc2[tt]);
