@@ -48,14 +48,14 @@ PEAK = {"bf16": 2500.0, "fp4": 10100.0, "hbm": 8000.0}  # TFLOP/s, TFLOP/s, GB/s
 # taken on: a changed kernel reports null until it is measured again.  The
 # summaries are profiles/<workload>_hbm_counters.txt.
 TRAFFIC = {
-    ('csa_attend', 3): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.957e+10},  # csa_prefill_128k
-    ('csa_index_topk', 3): {"sha256": "4e80d340b5080f91386cc694c83c719c7972a9e2b8be506dd527dbd9ec05811c", "bytes": 1.222e+09},  # csa_prefill_128k
+    ('csa_attend', 3): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.941e+10},  # csa_prefill_128k
+    ('csa_index_topk', 3): {"sha256": "1ebf0f2e46b7587dddc74f1ad9e5325151889e29d886181e441c7940a1bdd024", "bytes": 1.222e+09},  # csa_prefill_128k
     ('csa_compress', 3): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 7.299e+07},  # csa_prefill_128k
     ('csa_rope_rows', 3): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 6.719e+07},  # csa_prefill_128k
     ('hca_attend', 2): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.142e+09},  # hca_32k
     ('csa_compress', 2): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 8.835e+06},  # hca_32k
     ('csa_rope_rows', 2): {"sha256": "9def0ef3ce63aa439bf0cab9ffe57b6148e0da778a945889a248fd9cdfded242", "bytes": 1.685e+07},  # hca_32k
-    ('csa_index_topk', 4): {"sha256": "4e80d340b5080f91386cc694c83c719c7972a9e2b8be506dd527dbd9ec05811c", "bytes": 6.095e+08},  # csa_decode_1m
+    ('csa_index_topk', 4): {"sha256": "1ebf0f2e46b7587dddc74f1ad9e5325151889e29d886181e441c7940a1bdd024", "bytes": 6.095e+08},  # csa_decode_1m
     ('csa_attend', 4): {"sha256": "71df24787571677521eb64a0726bef4b05a552d4332d9a05f3b449d45ed08d4b", "bytes": 1.038e+08},  # csa_decode_1m
 }
 TRAFFIC[("csa_project_in", "proj")] = {  # the GEMM (1.085e9) + the indexer-query kernel (9.7e6)
@@ -98,8 +98,8 @@ def parse():
                          "second stream beside the attention of the chunk before; default 16, config 5: 1); "
                          "1 = the two calls in turn")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
-                    help="only summarise a rocprofv3 kernel_trace.csv: dispatches, total and average "
-                         "duration per kernel and grid size")
+                    help="only summarise a rocprofv3 kernel_trace.csv (dispatches, total and average duration "
+                         "per kernel and grid size) or counter_collection.csv (mean counter values per dispatch)")
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="query rows (config 4: sequences) of the oracle sample (default per config)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -950,18 +950,35 @@ def measure(cfg_id, args, cpu_sample=None):
     return res
 
 
+def _grid(row):
+    grid = "x".join(row[c] for c in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z") if c in row)
+    return grid or row.get("Grid_Size", "?")
+
+
 def trace_summary(path):
     """Dispatches, total and average duration (us) per (kernel, grid size)
-    of a rocprofv3 --kernel-trace CSV: the pipelined step's chunked launches
-    and the per-kernel pass's whole-layer launches of one kernel have
-    different grids."""
+    of a rocprofv3 --kernel-trace CSV (or, for a --pmc counter_collection
+    CSV, each counter's mean value per dispatch): the pipelined step's
+    chunked launches and the per-kernel pass's whole-layer launches of one
+    kernel have different grids."""
     import csv
-    groups = {}
     with open(path, newline="") as f:
-        for row in csv.DictReader(f):
-            grid = "x".join(row[c] for c in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z") if c in row)
-            if not grid:
-                grid = row.get("Grid_Size", "?")
+        rows = list(csv.DictReader(f))
+    if rows and "Counter_Name" in rows[0]:
+        per = {}  # (kernel, grid) -> counter -> dispatch -> value
+        for row in rows:
+            d = per.setdefault((row["Kernel_Name"], _grid(row)), {}).setdefault(row["Counter_Name"], {})
+            d[row["Dispatch_Id"]] = d.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+        print("%-66s %14s %6s %-28s %16s" % ("kernel", "grid", "n", "counter", "mean_per_dispatch"))
+        for (name, grid), cs in sorted(per.items()):
+            for cname, disp in sorted(cs.items()):
+                print("%-66s %14s %6d %-28s %16.6g" % (name[:66], grid, len(disp), cname,
+                                                       sum(disp.values()) / len(disp)))
+        return
+    groups = {}
+    if True:
+        for row in rows:
+            grid = _grid(row)
             dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
             g = groups.setdefault((row["Kernel_Name"], grid), [0, 0.0])
             g[0] += 1
