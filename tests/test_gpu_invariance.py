@@ -319,3 +319,30 @@ def test_index_attend_pipeline_equals_the_two_calls(orc, fmt, n, k, q_pos0, chun
     wf = np.concatenate([c["kv"][0][:P], c["kv"][0]]) if P else c["kv"][0]
     ref = orc.attend_rows(c["q"][0], P, orc.bf16_to_f64(e_bits), 4, rows, "csa", idx=oidx, win=wf, sink=c["sink"])
     assert_close(host_bits(go)[0][rows], ref, "csa_index_attend")
+
+
+@pytest.mark.parametrize("efmt,B,n,k,chunks", [
+    ("fp8", 1, 3072, 256, 5),     # the FP8 decode-format kernel, unsplit (k + n_win < 512)
+    ("nvfp4", 1, 3072, 256, 4),
+    ("bf16", 2, 2048, 512, 8),    # B > 1: one chunk, no aux stream needed
+])
+def test_index_attend_pipeline_entry_formats(orc, efmt, B, n, k, chunks):
+    """csa_index_attend with the decode cache formats whose attention needs
+    no workspace, and with B > 1, against the two calls: same bytes."""
+    H, H_I = 64, 8
+    c = synth.csa_prefill(n, H, H_I, 32, k, seed=141, B=B, indexer="mxfp4")
+    kv = dev(c["kv"])
+    comp = L.csa_compress(kv, dev(c["beta"]), 4, 1, ik=dev(c["ik"]), kidx_fmt="mxfp4", entry_fmt=efmt)
+    kv_rot = L.csa_rope_rows(kv)
+    qI, w, q, sink = dev(c["q_I"]), dev(c["w_I"]), dev(c["q"]), dev(c["sink"])
+    ekw = {k_: comp[k_] for k_ in ("entries_rope", "entry_scale") if comp.get(k_) is not None}
+    ref_idx = L.csa_index_topk(qI, w, comp["kidx"], k, 4, fmt="mxfp4", kidx_scale=comp["kidx_scale"])
+    ref_out = L.csa_attend(q, comp["entries"], ref_idx, m=4, win_kv=kv_rot, win_roped=True, sink=sink, **ekw)
+    torch.cuda.synchronize()
+    print("index_attend entry format %s B %d chunks %d" % (efmt, B, chunks), flush=True)
+    gi, go = L.csa_index_attend(qI, w, comp["kidx"], k, 4, q, comp["entries"], fmt="mxfp4",
+                                kidx_scale=comp["kidx_scale"], win_kv=kv_rot, win_roped=True, sink=sink,
+                                n_chunks=chunks, **ekw)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(gi), host(ref_idx))
+    assert np.array_equal(host_bits(go), host_bits(ref_out))
