@@ -870,27 +870,28 @@ def measure(cfg_id, args, cpu_sample=None):
         wl.step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
-    # a pipelined step (csa_index_attend) overlaps the indexer and the
-    # attention: it is timed as a whole, and the per-kernel figures come from
-    # a second pass of the same steps with the calls in turn
+    # The steps are timed as a whole with nothing but the launches in the
+    # timed region; the per-kernel figures come from a second pass of the
+    # same number of steps with a HIP event between the calls.  A pipelined
+    # step (csa_index_attend) overlaps the indexer and the attention, so its
+    # second pass runs the calls in turn.
     piped = getattr(wl, "chunks", 1) > 1
     log("config %d: timing %d steps" % (cfg_id, args.steps))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        wl.step(None if piped else evs[s])
+        wl.step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    serial_ms = None
+    log("config %d: per-kernel pass, %d steps%s" % (cfg_id, args.steps, " with the calls in turn" if piped else ""))
     if piped:
-        log("config %d: per-kernel pass, %d steps with the calls in turn" % (cfg_id, args.steps))
         wl.step(serial=True)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for s in range(args.steps):
-            wl.step(evs[s])
-        torch.cuda.synchronize()
-        serial_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(args.steps):
+        wl.step(evs[s])
+    torch.cuda.synchronize()
+    pass_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     per_k = np.zeros(nk)
     for s in range(args.steps):
         for i in range(nk):
@@ -940,10 +941,15 @@ def measure(cfg_id, args, cpu_sample=None):
             "step": "csa_compress, csa_rope_rows, then csa_index_attend: %d token chunks, the indexer of chunk "
                     "c + 1 on a second stream beside the attention of chunk c" % wl.chunks,
             "kernels_and_roofline": "per-launch durations from a second pass of %d steps with the four calls in "
-                                    "turn on one stream" % args.steps,
-            "serial_ms_per_step": round(serial_ms, 4)}
+                                    "turn on one stream, HIP events between them" % args.steps,
+            "serial_ms_per_step": round(pass_ms, 4)}
+    else:
+        res["schedule"] = {
+            "kernels_and_roofline": "per-launch durations from a second pass of %d steps with HIP events between "
+                                    "the calls" % args.steps,
+            "events_ms_per_step": round(pass_ms, 4)}
     if hasattr(wl, "fallbacks"):  # top-k work-groups that took the exact streaming path, per call
-        ncalls = getattr(wl, "calls", args.warmup + args.steps)
+        ncalls = getattr(wl, "calls", args.warmup + 2 * args.steps)  # the timed steps and the per-kernel pass
         res["topk_fallbacks_per_call"] = round(int(wl.fallbacks.item()) / ncalls, 2)
     del wl
     torch.cuda.empty_cache()
