@@ -316,6 +316,20 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def beside(side, first, second):
+    """Run first() on a side stream beside second() on the current stream,
+    then make the current stream wait for both: the two are independent
+    calls of one layer step (the window rotation and the compression both
+    only read the layer's KV rows)."""
+    import torch
+    cur = torch.cuda.current_stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        first()
+    second()
+    cur.wait_stream(side)
+
+
 class CsaLayer:
     """Config 1 / 3: csa_compress -> csa_index_topk -> csa_attend."""
 
@@ -360,26 +374,32 @@ class CsaLayer:
         }
         self.pairs, self.keys = pairs, keys
         self.calls = 0
+        self.side = torch.cuda.Stream()
 
     chunks = 16  # csa_index_attend's token chunks in the timed step (1: the calls in turn)
 
     def step(self, ev=None, serial=False):
         """One layer step.  With per-kernel events (or serial) the four calls
-        run in turn on the current stream; otherwise the indexer and the
+        run in turn on the current stream; otherwise the window rotation runs
+        on a side stream beside the compression, and the indexer and the
         attention run as csa_index_attend over self.chunks token chunks."""
         L = self.L
         self.calls += 1
-        if ev: ev[0].record()
-        L.csa_compress(self.kv, self.beta, self.m, 1, ik=self.ik, kidx_fmt=self.fmt, out=self.bufs)
-        if ev: ev[1].record()
-        L.csa_rope_rows(self.kv, out=self.kv_rot)
-        if ev: ev[2].record()
+        compress = lambda: L.csa_compress(self.kv, self.beta, self.m, 1, ik=self.ik, kidx_fmt=self.fmt,
+                                          out=self.bufs)
+        rope = lambda: L.csa_rope_rows(self.kv, out=self.kv_rot)
         if ev is None and not serial and self.chunks > 1:
+            beside(self.side, rope, compress)
             L.csa_index_attend(self.qI, self.w, self.bufs["kidx"], self.k, self.m, self.q, self.bufs["entries"],
                                fmt=self.fmt, kidx_scale=self.bufs.get("kidx_scale"), idx_out=self.idx,
                                fallback_count=self.fallbacks, win_kv=self.kv_rot, win_roped=True, sink=self.sink,
                                out=self.out, n_chunks=self.chunks)
             return
+        if ev: ev[0].record()
+        compress()
+        if ev: ev[1].record()
+        rope()
+        if ev: ev[2].record()
         L.csa_index_topk(self.qI, self.w, self.bufs["kidx"], self.k, self.m, fmt=self.fmt,
                          kidx_scale=self.bufs.get("kidx_scale"), idx_out=self.idx, fallback_count=self.fallbacks)
         if ev: ev[3].record()
@@ -456,6 +476,7 @@ class HcaLayer:
         self.out = torch.empty((1, self.n, self.H, 128), dtype=torch.bfloat16, device="cuda")
         self.kernels = ["csa_compress", "csa_rope_rows", "hca_attend"]
         self.kv_rot = torch.empty_like(self.kv)
+        self.side = torch.cuda.Stream()
         t = np.arange(self.n, dtype=np.int64)
         keys = int((np.minimum(N, (t + 1) // self.m) + np.minimum(t + 1, 128)).sum())
         self.keys = keys
@@ -472,12 +493,19 @@ class HcaLayer:
         self.work_alt = {"hca_attend": ("bf16", 4.0 * self.H * 128 * keys)}
 
     def step(self, ev=None):
+        """One layer step; without per-kernel events the window rotation runs
+        on a side stream beside the compression."""
         L = self.L
-        if ev: ev[0].record()
-        L.csa_compress(self.kv, self.beta, self.m, 0, out=self.bufs)
-        if ev: ev[1].record()
-        L.csa_rope_rows(self.kv, out=self.kv_rot)
-        if ev: ev[2].record()
+        compress = lambda: L.csa_compress(self.kv, self.beta, self.m, 0, out=self.bufs)
+        rope = lambda: L.csa_rope_rows(self.kv, out=self.kv_rot)
+        if ev is None:
+            beside(self.side, rope, compress)
+        else:
+            ev[0].record()
+            compress()
+            ev[1].record()
+            rope()
+            ev[2].record()
         L.hca_attend(self.q, self.bufs["entries"], m=self.m, win_kv=self.kv_rot, win_roped=True, sink=self.sink,
                      out=self.out)
         if ev: ev[3].record()
@@ -859,15 +887,23 @@ def cpu_leg(wl, cfg_id, sample):
     return cpu
 
 
-def measure(cfg_id, args, cpu_sample=None):
+def measure(cfg_id, args, cpu_sample=None, min_warm_s=0.0):
     """Warm up, time args.steps steps of workload `cfg_id` (per-kernel HIP
-    events on the launch stream), then the oracle baseline."""
+    events on the launch stream), then the oracle baseline.  min_warm_s:
+    after the args.warmup steps, keep warming up until that much wall time
+    has passed (short steps: a few of them do not bring the GPU clock up);
+    the count actually run is reported as `warmup`."""
     import torch
     wl = {1: CsaLayer, 2: HcaLayer, 3: CsaLayer, 4: DecodeLayer, 5: PairLayer}[cfg_id](cfg_id)
     nk = len(wl.kernels)
     log("config %d: warmup %d steps" % (cfg_id, args.warmup))
-    for _ in range(args.warmup):
+    tw = time.perf_counter()
+    warm = 0
+    while warm < args.warmup or time.perf_counter() - tw < min_warm_s:
         wl.step()
+        warm += 1
+        if warm >= args.warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
     # The steps are timed as a whole with nothing but the launches in the
@@ -934,7 +970,7 @@ def measure(cfg_id, args, cpu_sample=None):
     cfg = {"workload": wname, "global_batch": getattr(wl, "B", 1), "seq_len": wl.n,
            "heads": wl.H, "head_dim": 128}
     res = {"value": round(wl.n / (ms_step / 1e3), 1), "unit": "query-tokens/s", "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "dtype": dname, "config": cfg,
+           "warmup": warm, "ms_per_step": round(ms_step, 4), "dtype": dname, "config": cfg,
            "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu}
     if piped:
         res["schedule"] = {
@@ -949,7 +985,7 @@ def measure(cfg_id, args, cpu_sample=None):
                                     "the calls" % args.steps,
             "events_ms_per_step": round(pass_ms, 4)}
     if hasattr(wl, "fallbacks"):  # top-k work-groups that took the exact streaming path, per call
-        ncalls = getattr(wl, "calls", args.warmup + 2 * args.steps)  # the timed steps and the per-kernel pass
+        ncalls = getattr(wl, "calls", warm + 2 * args.steps)  # warmup, the timed steps and the per-kernel pass
         res["topk_fallbacks_per_call"] = round(int(wl.fallbacks.item()) / ncalls, 2)
     del wl
     torch.cuda.empty_cache()
@@ -1038,7 +1074,8 @@ def main():
         if key in res:
             line[key] = res[key]
     if args.config is None and not args.no_extra:
-        line["workloads"] = {name: measure(c, args) for name, c in EXTRA}
+        # the extra workloads' steps last 0.2-0.6 ms: at least 0.5 s of warmup each
+        line["workloads"] = {name: measure(c, args, min_warm_s=0.5) for name, c in EXTRA}
     print(json.dumps(line), flush=True)
 
 
