@@ -887,13 +887,19 @@ def cpu_leg(wl, cfg_id, sample):
     return cpu
 
 
-def measure(cfg_id, args, cpu_sample=None, min_warm_s=0.0):
+# wall time of warmup at least, per workload: the HCA and decode steps last
+# 0.2-0.6 ms, and a few of them do not bring the GPU clock up
+MIN_WARM_S = {2: 0.5, 4: 0.5}
+
+
+def measure(cfg_id, args, cpu_sample=None):
     """Warm up, time args.steps steps of workload `cfg_id` (per-kernel HIP
-    events on the launch stream), then the oracle baseline.  min_warm_s:
-    after the args.warmup steps, keep warming up until that much wall time
-    has passed (short steps: a few of them do not bring the GPU clock up);
-    the count actually run is reported as `warmup`."""
+    events on the launch stream), then the oracle baseline.  After the
+    args.warmup steps, short-step workloads keep warming up until
+    MIN_WARM_S of wall time has passed;
+    the count actually run is reported as `warmup` (MIN_WARM_S)."""
     import torch
+    min_warm_s = MIN_WARM_S.get(cfg_id, 0.0)
     wl = {1: CsaLayer, 2: HcaLayer, 3: CsaLayer, 4: DecodeLayer, 5: PairLayer}[cfg_id](cfg_id)
     nk = len(wl.kernels)
     log("config %d: warmup %d steps" % (cfg_id, args.warmup))
@@ -1065,7 +1071,7 @@ def main():
     res = measure(cfg_id, args, args.cpu_sample)
     line = {
         "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "steps": args.steps, "warmup": res["warmup"], "ms_per_step": res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": res["dtype"], "data": "synthetic (seeded, numpy default_rng)", "config": res["config"],
         "roofline": res["roofline"], "kernels": res["kernels"], "cpu_baseline": res["cpu_baseline"],
@@ -1074,8 +1080,7 @@ def main():
         if key in res:
             line[key] = res[key]
     if args.config is None and not args.no_extra:
-        # the extra workloads' steps last 0.2-0.6 ms: at least 0.5 s of warmup each
-        line["workloads"] = {name: measure(c, args, min_warm_s=0.5) for name, c in EXTRA}
+        line["workloads"] = {name: measure(c, args) for name, c in EXTRA}
     print(json.dumps(line), flush=True)
 
 
