@@ -324,13 +324,15 @@ int csa_attend(const void* q, int B, int n, int64_t q_pos0, int H, int D,
  *  aux_stream   a second stream of the same device (not stream, default
  *               priority), used when the call takes more than one chunk;
  *               nothing else enqueued on it is ordered with this call.
- *  events       three hipEvent_t of the device (any creation flags), owned
- *               by the caller, recorded and waited on by the call; needed
- *               when the call takes more than one chunk.  Calls that share
- *               events or aux_stream must be issued from one host thread.
+ *  events       three distinct hipEvent_t of the device (any creation
+ *               flags), owned by the caller, recorded and waited on by the
+ *               call; needed when the call takes more than one chunk.  Calls
+ *               that share events or aux_stream must be issued from one host
+ *               thread.
  *  Errors: every argument is checked before anything is enqueued; a HIP
  *  error during the enqueue returns CSA_HIP_ERROR with the chunks before it
- *  enqueued.  Nothing is allocated or synchronised.
+ *  enqueued (the call then still tries to order the aux stream's work
+ *  before later work on stream).  Nothing is allocated or synchronised.
  */
 int csa_index_attend(const void* qidx, const uint8_t* qidx_scale, const float* widx, const void* kidx,
                      const uint8_t* kidx_scale, int kidx_fmt, int H_I, int d_idx, int k, int32_t* idx_out,

@@ -401,6 +401,8 @@ int csa_index_attend(const void* qidx, const uint8_t* qidx_scale, const float* w
     REQUIRE(aux_stream != nullptr && aux_stream != stream, "%s: n_chunks > 1 needs an aux_stream other than stream",
             name);
     REQUIRE(events && events[0] && events[1] && events[2], "%s: n_chunks > 1 needs three events", name);
+    REQUIRE(events[0] != events[1] && events[0] != events[2] && events[1] != events[2],
+            "%s: the three events must be distinct", name);
   }
   // the whole call is checked before anything is enqueued (no workspace:
   // the formats and sizes that need one are refused here)
@@ -436,8 +438,10 @@ int csa_index_attend(const void* qidx, const uint8_t* qidx_scale, const float* w
   st = hip_status(hipEventRecord(ev0, sm), "csa_index_attend: event record");
   if (st == CSA_OK) st = hip_status(hipStreamWaitEvent(sx, ev0, 0), "csa_index_attend: stream wait");
   auto lo = [&](int c) { return (int64_t)n * c / C; };
+  bool aux_used = false;
   for (int c = 0; c <= C && st == CSA_OK; ++c) {
     if (c < C) {  // top-k of chunk c on the aux stream
+      aux_used = true;
       st = index_chunk(lo(c), (int)(lo(c + 1) - lo(c)), sx);
       if (st == CSA_OK) st = hip_status(hipEventRecord(ring[c & 1], sx), "csa_index_attend: event record");
     }
@@ -447,6 +451,11 @@ int csa_index_attend(const void* qidx, const uint8_t* qidx_scale, const float* w
       st = hip_status(hipStreamWaitEvent(sm, ring[(c - 1) & 1], 0), "csa_index_attend: stream wait");
       if (st == CSA_OK) st = attend_chunk(lo(c - 1), (int)(lo(c) - lo(c - 1)));
     }
+  }
+  if (st != CSA_OK && aux_used) {
+    // best effort: order what the aux stream already holds before later work
+    // on the caller's stream (the error message is the first failure's)
+    if (hipEventRecord(ev0, sx) == hipSuccess) (void)hipStreamWaitEvent(sm, ev0, 0);
   }
   return st;
 }

@@ -271,7 +271,7 @@ def test_attend_rejects_small_workspace(L):
     assert "ws must be" in _msg(L)
 
 
-_EVS = (C.c_void_p * 3)(FAKE, FAKE, FAKE)  # never recorded: every call below fails validation first
+_EVS = (C.c_void_p * 3)(FAKE, FAKE2, MIS)  # never recorded: every call below fails validation first
 
 
 def _index_attend(L, **kw):
@@ -290,6 +290,7 @@ def _index_attend(L, **kw):
     (dict(aux_stream=None), "aux_stream", _lib.CSA_INVALID_ARG),
     (dict(events=None), "three events", _lib.CSA_INVALID_ARG),
     (dict(events=(C.c_void_p * 3)(FAKE, None, FAKE)), "three events", _lib.CSA_INVALID_ARG),
+    (dict(events=(C.c_void_p * 3)(FAKE, FAKE2, FAKE)), "distinct", _lib.CSA_INVALID_ARG),
     # the indexer's and the attention's own checks, before anything is enqueued
     (dict(k=0), "k=0", _lib.CSA_INVALID_ARG),
     (dict(H_I=9), "H_I=9", _lib.CSA_INVALID_ARG),
