@@ -95,7 +95,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="default run: leave out configs 2 and 4")
     ap.add_argument("--chunks", type=int, default=None,
                     help="configs 1, 3 and 5: token chunks of csa_index_attend (the indexer of a chunk runs on a "
-                         "second stream beside the attention of the chunk before; default 16, config 5: 1); "
+                         "second stream beside the attention of the chunk before; default min(16, tokens / 8192), config 5: 1); "
                          "1 = the two calls in turn")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="only summarise a rocprofv3 kernel_trace.csv (dispatches, total and average duration "
@@ -375,8 +375,14 @@ class CsaLayer:
         self.pairs, self.keys = pairs, keys
         self.calls = 0
         self.side = torch.cuda.Stream()
+        if self.chunks is None:
+            self.chunks = max(1, min(16, n // 8192))
 
-    chunks = 16  # csa_index_attend's token chunks in the timed step (1: the calls in turn)
+    # csa_index_attend's token chunks in the timed step (1: the calls in
+    # turn); None: 16, or fewer so that a chunk holds at least 8192 tokens
+    # (small layers gain nothing from the second stream: config 1, 1024
+    # tokens, took 0.186 ms/step in 2 chunks against 0.069 ms in turn)
+    chunks = None
 
     def step(self, ev=None, serial=False):
         """One layer step.  With per-kernel events (or serial) the four calls
@@ -980,8 +986,9 @@ def measure(cfg_id, args, cpu_sample=None):
            "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu}
     if piped:
         res["schedule"] = {
-            "step": "csa_compress, csa_rope_rows, then csa_index_attend: %d token chunks, the indexer of chunk "
-                    "c + 1 on a second stream beside the attention of chunk c" % wl.chunks,
+            "step": "csa_compress with csa_rope_rows beside it on a side stream, then csa_index_attend: %d token "
+                    "chunks, the indexer of chunk c + 1 on a second stream beside the attention of chunk c"
+                    % wl.chunks,
             "kernels_and_roofline": "per-launch durations from a second pass of %d steps with the four calls in "
                                     "turn on one stream, HIP events between them" % args.steps,
             "serial_ms_per_step": round(pass_ms, 4)}
